@@ -1,0 +1,234 @@
+"""Plain float64 definition of exact attention and its gradient (oracle).
+
+TEST INFRASTRUCTURE ONLY -- see ``oracle/__init__.py``.  Nothing in the
+product path may import this module.
+
+What is computed (per batch index b and head h, with N queries = N keys):
+
+  S = scale * Q K^T                       [lynx] "El algoritmo naive de
+                                          attention" (step 1; scale 1/sqrt(d)
+                                          as in [mm] "O algoritmo de atencao do
+                                          Flash"); [tonho] "como funciona"
+                                          writes the same factor as tau.
+  S_ij = -inf where key j is not visible  [mm] "O mascaramento causal ..."
+         to query i                       (causal: keys in the future of the
+                                          query are excluded); [agi] block-sparse
+                                          paragraph (whole blocks dropped).
+  LSE_i = log sum_j exp(S_ij)             natural log; the pages keep the row
+                                          max m and row sum l, and
+                                          LSE = m + log(l) carries both.
+  P = exp(S - LSE)                        [lynx] "El algoritmo naive" step 2
+  O = P V                                 [lynx] "El algoritmo naive" step 3
+
+Backward (the pages give no gradient formulas except the D identity; this is
+the analytic gradient of the definition above, pinned by finite differences
+in the tests):
+
+  dV = P^T dO
+  dP = dO V^T
+  D_i = sum_j P_ij dP_ij                  [tonho] "como funciona" states that
+                                          this equals the d-length dot
+                                          dO_i . O_i; both are returned.
+  dS = P o (dP - D)
+  dQ = scale * dS K
+  dK = scale * dS^T Q
+
+Visibility of key j to query i (mask_block = side of a mask block):
+  [not causal or j <= i] and [block_mask is None or
+                              block_mask[i // mask_block, j // mask_block] != 0]
+
+Fully masked rows (possible only with a general block mask): O_i = 0,
+LSE_i = -inf, and the row contributes nothing to any gradient.
+
+Memory: rows are processed in chunks, and each chunk only touches the key
+columns that can be visible to some row of the chunk (a causal prefix, or the
+kept key blocks of the chunk's query blocks).  Columns left out are exactly
+those whose probability is 0 for every row of the chunk, so the result is the
+same as the dense masked evaluation; a test checks this on small shapes.
+Each row's softmax is always evaluated over all of its candidate columns at
+once -- no online recurrence is used here.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "visibility",
+    "attention_probs",
+    "attention_forward",
+    "attention_backward",
+]
+
+_CHUNK_ELEMS = 1 << 22  # rows * candidate columns per chunk (32 MiB of f64)
+
+
+def visibility(rows, cols, causal=False, block_mask=None, mask_block=128):
+    """Boolean matrix vis[r, c]: is key ``cols[c]`` visible to query ``rows[r]``."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    vis = np.ones((rows.size, cols.size), dtype=bool)
+    if causal:
+        vis &= cols[None, :] <= rows[:, None]
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        vis &= bm[(rows // mask_block)[:, None], (cols // mask_block)[None, :]]
+    return vis
+
+
+def _candidate_columns(r0, r1, n, causal, block_mask, mask_block):
+    """Key columns that may be visible to some query row in [r0, r1)."""
+    cols = np.arange(n, dtype=np.int64)
+    if causal:
+        cols = cols[cols < r1]
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        qblocks = np.unique(np.arange(r0, r1) // mask_block)
+        kept_kblocks = bm[qblocks].any(axis=0)
+        cols = cols[kept_kblocks[cols // mask_block]]
+    return cols
+
+
+def _row_chunks(n, causal, block_mask, mask_block, row_chunk):
+    if row_chunk is None:
+        if block_mask is not None:
+            row_chunk = mask_block
+        else:
+            row_chunk = max(1, min(n, _CHUNK_ELEMS // max(n, 1)))
+    r0 = 0
+    while r0 < n:
+        r1 = min(n, r0 + row_chunk)
+        yield r0, r1
+        r0 = r1
+
+
+def _softmax_rows(s):
+    """Natural-log LSE and probabilities of each row of s (entries may be -inf).
+
+    A row whose entries are all -inf gets LSE = -inf and probabilities 0.
+    """
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    live = np.isfinite(m)
+    m_safe = np.where(live, m, 0.0)
+    e = np.exp(s - m_safe[:, None])
+    l = e.sum(axis=1)
+    with np.errstate(divide="ignore"):
+        lse = np.where(live, m_safe + np.log(np.where(live, l, 1.0)), -np.inf)
+    p = np.where(live[:, None], e / np.where(live, l, 1.0)[:, None], 0.0)
+    return lse, p
+
+
+def attention_probs(q, k, scale, causal=False, block_mask=None, mask_block=128):
+    """Dense P (N x N) and LSE (N) for ONE head; small shapes only."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    n = q.shape[0]
+    s = scale * (q @ k.T)
+    vis = visibility(np.arange(n), np.arange(k.shape[0]), causal, block_mask, mask_block)
+    s = np.where(vis, s, -np.inf)
+    lse, p = _softmax_rows(s)
+    return p, lse
+
+
+def _forward_head(q, k, v, scale, causal, block_mask, mask_block, row_chunk):
+    n, d = q.shape
+    o = np.zeros((n, v.shape[1]), dtype=np.float64)
+    lse = np.full(n, -np.inf, dtype=np.float64)
+    for r0, r1 in _row_chunks(n, causal, block_mask, mask_block, row_chunk):
+        cols = _candidate_columns(r0, r1, k.shape[0], causal, block_mask, mask_block)
+        rows = np.arange(r0, r1)
+        if cols.size == 0:
+            continue
+        s = scale * (q[r0:r1] @ k[cols].T)
+        s = np.where(visibility(rows, cols, causal, block_mask, mask_block), s, -np.inf)
+        lse_c, p = _softmax_rows(s)
+        lse[r0:r1] = lse_c
+        o[r0:r1] = p @ v[cols]
+    return o, lse
+
+
+def _backward_head(q, k, v, do, scale, causal, block_mask, mask_block, row_chunk):
+    n, d = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    d_vec = np.zeros(n)
+    d_dot = np.zeros(n)
+    for r0, r1 in _row_chunks(n, causal, block_mask, mask_block, row_chunk):
+        cols = _candidate_columns(r0, r1, k.shape[0], causal, block_mask, mask_block)
+        rows = np.arange(r0, r1)
+        if cols.size == 0:
+            continue
+        s = scale * (q[r0:r1] @ k[cols].T)
+        s = np.where(visibility(rows, cols, causal, block_mask, mask_block), s, -np.inf)
+        _, p = _softmax_rows(s)
+        o_c = p @ v[cols]
+        dv[cols] += p.T @ do[r0:r1]
+        dp = do[r0:r1] @ v[cols].T
+        dd = (p * dp).sum(axis=1)
+        ds = p * (dp - dd[:, None])
+        dq[r0:r1] = scale * (ds @ k[cols])
+        dk[cols] += scale * (ds.T @ q[r0:r1])
+        d_vec[r0:r1] = dd
+        d_dot[r0:r1] = (do[r0:r1] * o_c).sum(axis=1)
+    return dq, dk, dv, d_vec, d_dot
+
+
+def _as_bhnd(x):
+    x = np.asarray(x)
+    if x.ndim == 2:
+        x = x[None, None]
+    if x.ndim != 4:
+        raise ValueError("expected (B, H, N, d) or (N, d)")
+    return x.astype(np.float64)
+
+
+def _select(x, heads):
+    if heads is None:
+        return [(b, h) for b in range(x.shape[0]) for h in range(x.shape[1])]
+    return [tuple(bh) for bh in heads]
+
+
+def attention_forward(q, k, v, scale, causal=False, block_mask=None, mask_block=128,
+                      heads=None, row_chunk=None):
+    """O (float64) and natural-log LSE (float64) of the definition above.
+
+    q, k, v: (B, H, N, d) or (N, d) arrays of any float dtype (upcast exactly).
+    heads: optional list of (b, h); then the results are stacked in that order
+           with shapes (len(heads), N, d) and (len(heads), N).
+    """
+    q, k, v = _as_bhnd(q), _as_bhnd(k), _as_bhnd(v)
+    sel = _select(q, heads)
+    outs, lses = [], []
+    for b, h in sel:
+        o, lse = _forward_head(q[b, h], k[b, h], v[b, h], scale, causal, block_mask,
+                               mask_block, row_chunk)
+        outs.append(o)
+        lses.append(lse)
+    o = np.stack(outs)
+    lse = np.stack(lses)
+    if heads is None:
+        o = o.reshape(q.shape[0], q.shape[1], *o.shape[1:])
+        lse = lse.reshape(q.shape[0], q.shape[1], -1)
+    return o, lse
+
+
+def attention_backward(q, k, v, do, scale, causal=False, block_mask=None, mask_block=128,
+                       heads=None, row_chunk=None, return_d=False):
+    """dQ, dK, dV (float64) of f = <O(Q, K, V), dO>; P is rebuilt from Q and K.
+
+    With return_d=True also returns (D, D_dot): D_i = sum_j P_ij dP_ij and the
+    d-length dot dO_i . O_i, which the pages state are equal.
+    """
+    q, k, v, do = _as_bhnd(q), _as_bhnd(k), _as_bhnd(v), _as_bhnd(do)
+    sel = _select(q, heads)
+    res = [_backward_head(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, block_mask,
+                          mask_block, row_chunk) for b, h in sel]
+    dq, dk, dv, dd, ddot = (np.stack([r[i] for r in res]) for i in range(5))
+    if heads is None:
+        shp = (q.shape[0], q.shape[1])
+        dq, dk, dv = (x.reshape(*shp, *x.shape[1:]) for x in (dq, dk, dv))
+        dd, ddot = (x.reshape(*shp, -1) for x in (dd, ddot))
+    if return_d:
+        return dq, dk, dv, dd, ddot
+    return dq, dk, dv
