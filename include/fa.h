@@ -1,0 +1,125 @@
+/*
+ * fa.h -- C ABI of libfa_mi355x: tiled exact attention (forward and backward)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every batch index b and head h, with N queries and N
+ * keys of head dimension d:
+ *
+ *   S = scale * Q K^T, with S_ij = -inf where key j is not visible to query i,
+ *   LSE_i = log sum_j exp(S_ij)              (natural logarithm),
+ *   O = exp(S - LSE) V.
+ *
+ * This is the attention of "02 -- FlashAttention como una optimizacion de
+ * roofline" (lynx-cortex), section "El algoritmo naive de attention", computed
+ * block by block with the running row maximum and row sum of the online
+ * softmax ("El algoritmo Flash (forward)" there; "como funciona" in the
+ * tonho.wtf digest) so that no N x N matrix is written to memory.  The
+ * backward recomputes the probabilities from Q, K and the saved LSE instead of
+ * storing them ("Passo para tras: recalcular em vez de armazenar", the
+ * marketmaker.cc article) and uses D_i = dO_i . O_i for the softmax gradient
+ * ("como funciona", tonho.wtf digest).
+ *
+ * Visibility of key j to query i:
+ *   [causal == 0 or j <= i]   (future keys excluded -- the causal-mask section
+ *                              of the marketmaker.cc article)
+ *   and [block_mask == NULL or block_mask[i / mask_block][j / mask_block] != 0]
+ *                             (block-sparse attention -- block-sparse paragraph
+ *                              of the agihunt.info summary of the paper).
+ * A query row with no visible key gets O = 0, LSE = -inf and contributes
+ * nothing to the gradients.
+ *
+ * Layouts.  Q, K, V, O, dO, dQ, dK, dV are contiguous row-major tensors of
+ * shape (B, H, N, d) in the problem's dtype; element (b, h, n, c) sits at
+ * ((b * H + h) * N + n) * d + c.  LSE is float32 (B, H, N).  block_mask is
+ * uint8 [N / mask_block][N / mask_block], row = query block, shared by all
+ * (b, h).  Every tensor pointer is a DEVICE pointer (hipMalloc'd or equivalent)
+ * unless stated otherwise; device pointers must be 16-byte aligned.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = default stream).
+ * All work is enqueued asynchronously on it; no call synchronises the host.
+ *
+ * Ownership.  The caller allocates and owns every buffer, including the
+ * workspace, and keeps them alive until the enqueued work has completed.  The
+ * library allocates nothing, keeps no state between calls and is thread-safe.
+ *
+ * Errors.  Every entry point returns FA_OK (0) on success or a negative status
+ * before anything is enqueued.  There is never a silent fallback to another
+ * implementation: an unsupported problem is an error.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_dtype {
+  FA_F32 = 0,  /* float32 in, float32 arithmetic (vector ALU path)          */
+  FA_F16 = 1,  /* float16 in/out, float32 accumulation on matrix cores       */
+  FA_BF16 = 2  /* bfloat16 in/out, float32 accumulation on matrix cores      */
+};
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_ARG = -1,          /* null pointer, non-positive size, non-finite scale,
+                               misaligned pointer                              */
+  FA_ERR_UNSUPPORTED = -2,  /* d not in {64, 128}; unknown dtype; a block mask
+                               whose block is not a positive multiple of 128 or
+                               does not divide N                               */
+  FA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required     */
+  FA_ERR_LAUNCH = -4        /* the HIP runtime rejected a kernel launch       */
+};
+
+typedef struct fa_problem {
+  int32_t B, H, N, d;         /* batch, heads, sequence length, head dim       */
+  int32_t dtype;              /* enum fa_dtype                                 */
+  int32_t causal;             /* 0 or 1                                        */
+  float scale;                /* multiplies Q K^T, e.g. 1/sqrt(d); finite      */
+  const uint8_t* block_mask;  /* device pointer or NULL (dense)                */
+  int32_t mask_block;         /* side of one mask block; used iff block_mask   */
+} fa_problem;
+
+/* Bytes of device workspace that fa_fwd (pass 0) or fa_bwd (pass 1) needs for
+ * problem p; 0 if none.  Host-only arithmetic, no GPU call.  Returns 0 for an
+ * invalid problem (the entry point itself then reports the error). */
+size_t fa_workspace_size(const fa_problem* p, int pass);
+
+/* Forward.  Reads q, k, v; overwrites o (B,H,N,d, dtype) and lse (B,H,N,
+ * float32, natural log).  workspace: device buffer of at least
+ * fa_workspace_size(p, 0) bytes (may be NULL when that is 0). */
+int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, void* o,
+           float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* Backward of f = <O, dO>.  Reads q, k, v, o, dout and lse, which must be the
+ * O and LSE that fa_fwd produced for the same q, k, v and problem.  Overwrites
+ * (does not accumulate into) dq, dk, dv.  workspace: at least
+ * fa_workspace_size(p, 1) bytes; it receives D_i = dO_i . O_i (float32, B*H*N)
+ * and, with a block mask, the compiled block lists. */
+int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t ws_bytes, void* stream);
+
+/* Block-mask compilation (the step both passes run first when a block mask is
+ * given).  mask: device uint8 [nb][nb]; writes, all int32 device arrays:
+ *   row_ptr[nb + 1], col_idx[nnz]: for query block r, the kept key blocks
+ *     col_idx[row_ptr[r] .. row_ptr[r+1]) in increasing order;
+ *   col_ptr[nb + 1], row_idx[nnz]: for key block c, the query blocks that keep
+ *     it, row_idx[col_ptr[c] .. col_ptr[c+1]) in increasing order.
+ * col_idx and row_idx must hold nb*nb entries (the worst case). */
+int fa_mask_compile(const uint8_t* mask, int32_t nb, int32_t* row_ptr, int32_t* col_idx,
+                    int32_t* col_ptr, int32_t* row_idx, void* stream);
+
+/* Static string for a status code. */
+const char* fa_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

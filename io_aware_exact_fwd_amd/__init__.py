@@ -1,5 +1,44 @@
 """MI355X-native tiled exact attention (FlashAttention forward and backward).
 
-The compute path is the HIP library ``libfa_mi355x.so`` built from ``csrc/``;
-this package only marshals arguments to its C ABI.
+The compute path is the HIP library ``libfa_mi355x.so`` built from ``csrc/``
+(``python -m io_aware_exact_fwd_amd.build``); this package only marshals
+arguments to its C ABI (``include/fa.h``) and never computes on the CPU.
+
+    o, lse = fa_fwd(q, k, v, causal=True, scale=0.125)
+    dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=True, scale=0.125)
+    o = attention(q, k, v, causal=True)        # differentiable wrapper
 """
+
+from .binding import (  # noqa: F401
+    FA_BF16,
+    FA_F16,
+    FA_F32,
+    FaError,
+    fa_bwd,
+    fa_fwd,
+    fa_mask_compile,
+    fa_status_string,
+    fa_version,
+    fa_workspace_size,
+    make_problem,
+)
+
+
+def attention(q, k, v, causal=False, scale=None, block_mask=None, mask_block=128):
+    """softmax(scale * Q K^T, masked) V with a backward through ``fa_bwd``."""
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q_, k_, v_):
+            o, lse = fa_fwd(q_, k_, v_, causal, scale, block_mask, mask_block)
+            ctx.save_for_backward(q_, k_, v_, o, lse)
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q_, k_, v_, o, lse = ctx.saved_tensors
+            return fa_bwd(q_, k_, v_, o, do.contiguous(), lse, causal, scale, block_mask,
+                          mask_block)
+
+    return _Attention.apply(q, k, v)

@@ -1,0 +1,203 @@
+"""ctypes binding of libfa_mi355x (include/fa.h).  Argument marshalling only.
+
+Every step of the computation runs in the HIP library; PyTorch provides the
+device memory (outputs and workspace) and the current stream.  If the library
+is missing, or a tensor is not a contiguous GPU tensor of a supported type,
+the call raises -- there is no CPU or PyTorch fallback.
+
+Names follow the C ABI: ``fa_fwd``, ``fa_bwd``, ``fa_mask_compile``,
+``fa_workspace_size``, ``fa_status_string``, ``fa_version``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK, FA_ERR_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = 0, -1, -2, -3, -4
+
+EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_bwd", "fa_mask_compile", "fa_status_string",
+           "fa_version")
+
+
+class FaProblem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("N", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("block_mask", ctypes.c_void_p),
+        ("mask_block", ctypes.c_int32),
+    ]
+
+
+class FaError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {fa_status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa_mi355x.so (built in-tree); raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m io_aware_exact_fwd_amd.build` "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    pp = ctypes.POINTER(FaProblem)
+    L.fa_workspace_size.argtypes = [pp, ctypes.c_int]
+    L.fa_workspace_size.restype = sz
+    L.fa_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.fa_fwd.restype = ctypes.c_int
+    L.fa_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.fa_bwd.restype = ctypes.c_int
+    L.fa_mask_compile.argtypes = [vp, i32, vp, vp, vp, vp, vp]
+    L.fa_mask_compile.restype = ctypes.c_int
+    L.fa_status_string.argtypes = [ctypes.c_int]
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_version.argtypes = []
+    L.fa_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def fa_version() -> int:
+    return int(lib().fa_version())
+
+
+def _dtype_code(t):
+    import torch
+
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def make_problem(q, causal=False, scale=None, block_mask=None, mask_block=128) -> FaProblem:
+    """Problem descriptor for (B, H, N, d) tensor q; scale defaults to 1/sqrt(d)."""
+    if q.dim() != 4:
+        raise ValueError("expected (B, H, N, d) tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    p = FaProblem()
+    p.B, p.H, p.N, p.d = B, H, N, d
+    p.dtype = _dtype_code(q)
+    p.causal = 1 if causal else 0
+    p.scale = float(scale)
+    p.block_mask = block_mask.data_ptr() if block_mask is not None else None
+    p.mask_block = int(mask_block) if block_mask is not None else 0
+    return p
+
+
+def fa_workspace_size(p: FaProblem, pass_: int) -> int:
+    return int(lib().fa_workspace_size(ctypes.byref(p), int(pass_)))
+
+
+def _check_tensors(ref, *ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous (B, H, N, d)")
+        if t.dtype != ref.dtype or t.shape != ref.shape:
+            raise ValueError("q, k, v (and o, dO) must share dtype and shape")
+
+
+def _mask_arg(block_mask, ref):
+    import torch
+
+    if block_mask is None:
+        return None
+    if not isinstance(block_mask, torch.Tensor):
+        block_mask = torch.as_tensor(block_mask)
+    return block_mask.to(device=ref.device, dtype=torch.uint8).contiguous()
+
+
+def _stream(t):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def fa_fwd(q, k, v, causal=False, scale=None, block_mask=None, mask_block=128, out=None,
+           lse=None):
+    """Forward: returns (O, LSE); O like q, LSE float32 (B, H, N), natural log."""
+    import torch
+
+    _check_tensors(q, k, v)
+    bm = _mask_arg(block_mask, q)
+    p = make_problem(q, causal, scale, bm, mask_block)
+    B, H, N, d = q.shape
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensors(q, o)
+    ws_n = fa_workspace_size(p, 0)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    st = lib().fa_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                      lse_t.data_ptr(), ws.data_ptr(), ws_n, _stream(q))
+    if st != FA_OK:
+        raise FaError("fa_fwd", st)
+    return o, lse_t
+
+
+def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, block_mask=None, mask_block=128):
+    """Backward of <O, dO>: returns (dQ, dK, dV) like q."""
+    import torch
+
+    _check_tensors(q, k, v, o, dout)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 GPU tensor")
+    bm = _mask_arg(block_mask, q)
+    p = make_problem(q, causal, scale, bm, mask_block)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_n = fa_workspace_size(p, 1)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    st = lib().fa_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                      dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                      dv.data_ptr(), ws.data_ptr(), ws_n, _stream(q))
+    if st != FA_OK:
+        raise FaError("fa_bwd", st)
+    return dq, dk, dv
+
+
+def fa_mask_compile(block_mask):
+    """Compile a uint8 [nb, nb] GPU block mask; returns (row_ptr, col_idx,
+    col_ptr, row_idx) int32 GPU tensors, index lists trimmed to nnz."""
+    import torch
+
+    bm = block_mask.to(torch.uint8).contiguous()
+    if not bm.is_cuda or bm.dim() != 2 or bm.shape[0] != bm.shape[1]:
+        raise ValueError("block mask must be a square uint8 GPU tensor")
+    nb = bm.shape[0]
+    dev = bm.device
+    row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    col_ptr = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(nb * nb, dtype=torch.int32, device=dev)
+    row_idx = torch.empty(nb * nb, dtype=torch.int32, device=dev)
+    st = lib().fa_mask_compile(bm.data_ptr(), nb, row_ptr.data_ptr(), col_idx.data_ptr(),
+                               col_ptr.data_ptr(), row_idx.data_ptr(), _stream(bm))
+    if st != FA_OK:
+        raise FaError("fa_mask_compile", st)
+    nnz = int(row_ptr[-1].item())
+    return row_ptr, col_idx[:nnz], col_ptr, row_idx[:nnz]

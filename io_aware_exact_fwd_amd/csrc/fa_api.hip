@@ -1,0 +1,244 @@
+// fa_api.hip -- the C ABI of libfa_mi355x (declared in include/fa.h):
+// argument checking, workspace layout, and dispatch to the kernels on the
+// caller's stream.  No allocation, no synchronisation, no state.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_common.hpp"
+#include "fa_kernels.hpp"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+bool uses_lists(const fa_problem* p) { return p->block_mask != nullptr && p->dtype != FA_F32; }
+
+int check_problem(const fa_problem* p) {
+  if (!p) return FA_ERR_ARG;
+  if (p->B <= 0 || p->H <= 0 || p->N <= 0 || p->d <= 0) return FA_ERR_ARG;
+  if (!isfinite(p->scale)) return FA_ERR_ARG;
+  if (p->causal != 0 && p->causal != 1) return FA_ERR_ARG;
+  if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (p->d != 64 && p->d != 128) return FA_ERR_UNSUPPORTED;
+  // one head must be addressable with 32-bit byte offsets
+  if ((int64_t)p->N * p->d * elem_bytes(p->dtype) > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
+  const int64_t heads = (int64_t)p->B * p->H;
+  if (heads * ((p->N + 63) / 64) > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (p->block_mask) {
+    if (p->mask_block <= 0 || p->mask_block % 128 != 0) return FA_ERR_UNSUPPORTED;
+    if (p->N % p->mask_block != 0) return FA_ERR_UNSUPPORTED;
+  }
+  return FA_OK;
+}
+
+size_t lists_bytes(const fa_problem* p) {
+  if (!uses_lists(p)) return 0;
+  const size_t nb = (size_t)(p->N / p->mask_block);
+  return align_up((nb + 1) * 4) * 2 + align_up(nb * nb * 4) * 2;
+}
+
+size_t dvec_bytes(const fa_problem* p) {
+  return align_up((size_t)p->B * p->H * p->N * sizeof(float));
+}
+
+struct Lists {
+  int32_t *row_ptr, *col_idx, *col_ptr, *row_idx;
+};
+
+Lists carve_lists(const fa_problem* p, char* base) {
+  const size_t nb = (size_t)(p->N / p->mask_block);
+  Lists l;
+  l.row_ptr = (int32_t*)base;
+  base += align_up((nb + 1) * 4);
+  l.col_ptr = (int32_t*)base;
+  base += align_up((nb + 1) * 4);
+  l.col_idx = (int32_t*)base;
+  base += align_up(nb * nb * 4);
+  l.row_idx = (int32_t*)base;
+  return l;
+}
+
+fa::MaskLists mask_lists(const fa_problem* p, const Lists& l) {
+  fa::MaskLists m;
+  m.row_ptr = l.row_ptr;
+  m.col_idx = l.col_idx;
+  m.col_ptr = l.col_ptr;
+  m.row_idx = l.row_idx;
+  m.mask_block = p->mask_block;
+  return m;
+}
+
+fa::MaskLists no_lists() {
+  fa::MaskLists m;
+  m.row_ptr = m.col_idx = m.col_ptr = m.row_idx = nullptr;
+  m.mask_block = 0;
+  return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_workspace_size(const fa_problem* p, int pass) {
+  if (check_problem(p) != FA_OK) return 0;
+  if (pass == 0) return lists_bytes(p);
+  return dvec_bytes(p) + lists_bytes(p);
+}
+
+int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, void* o, float* lse,
+           void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_problem(p);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
+    return FA_ERR_ARG;
+  const size_t need = fa_workspace_size(p, 0);
+  if (need > 0 && (!workspace || ws_bytes < need)) return FA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const float c = p->scale * fa::kLog2e;
+  const int nheads = p->B * p->H;
+
+  if (p->dtype == FA_F32) {
+    fa::F32Params f = {};
+    f.q = (const float*)q;
+    f.k = (const float*)k;
+    f.v = (const float*)v;
+    f.out_o = (float*)o;
+    f.lse = lse;
+    f.block_mask = p->block_mask;
+    f.mask_block = p->mask_block;
+    f.N = p->N;
+    f.nheads = nheads;
+    f.d = p->d;
+    f.causal = p->causal;
+    f.c = c;
+    f.scale = p->scale;
+    return fa::launch_f32_fwd(f, s) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  }
+
+  fa::FwdParams f;
+  f.q = q;
+  f.k = k;
+  f.v = v;
+  f.o = o;
+  f.lse = lse;
+  f.N = p->N;
+  f.nheads = nheads;
+  f.nqt = (p->N + fa::kFwdRows - 1) / fa::kFwdRows;
+  f.c = c;
+  f.m = no_lists();
+  const bool masked = p->block_mask != nullptr;
+  if (masked) {
+    Lists l = carve_lists(p, (char*)workspace);
+    if (fa::launch_mask_compile(p->block_mask, p->N / p->mask_block, l.row_ptr, l.col_idx,
+                                l.col_ptr, l.row_idx, s) != hipSuccess)
+      return FA_ERR_LAUNCH;
+    f.m = mask_lists(p, l);
+  }
+  return fa::launch_fwd(f, p->dtype, p->d, p->causal != 0, masked, s) == hipSuccess ? FA_OK
+                                                                                    : FA_ERR_LAUNCH;
+}
+
+int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t ws_bytes, void* stream) {
+  int st = check_problem(p);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
+    return FA_ERR_ARG;
+  const size_t need = fa_workspace_size(p, 1);
+  if (!workspace || ws_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const float c = p->scale * fa::kLog2e;
+  const int nheads = p->B * p->H;
+  float* dvec = (float*)workspace;
+
+  if (p->dtype == FA_F32) {
+    fa::F32Params f = {};
+    f.q = (const float*)q;
+    f.k = (const float*)k;
+    f.v = (const float*)v;
+    f.o = (const float*)o;
+    f.dout = (const float*)dout;
+    f.lse = (float*)lse;
+    f.dq = (float*)dq;
+    f.dk = (float*)dk;
+    f.dv = (float*)dv;
+    f.dvec = dvec;
+    f.block_mask = p->block_mask;
+    f.mask_block = p->mask_block;
+    f.N = p->N;
+    f.nheads = nheads;
+    f.d = p->d;
+    f.causal = p->causal;
+    f.c = c;
+    f.scale = p->scale;
+    return fa::launch_f32_bwd(f, s) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  }
+
+  fa::BwdParams b;
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.o = o;
+  b.dout = dout;
+  b.lse = lse;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.dvec = dvec;
+  b.N = p->N;
+  b.nheads = nheads;
+  b.c = c;
+  b.scale = p->scale;
+  b.m = no_lists();
+  const bool masked = p->block_mask != nullptr;
+  if (masked) {
+    Lists l = carve_lists(p, (char*)workspace + dvec_bytes(p));
+    if (fa::launch_mask_compile(p->block_mask, p->N / p->mask_block, l.row_ptr, l.col_idx,
+                                l.col_ptr, l.row_idx, s) != hipSuccess)
+      return FA_ERR_LAUNCH;
+    b.m = mask_lists(p, l);
+  }
+  const bool causal = p->causal != 0;
+  b.ntiles = (p->N + fa::kFwdRows - 1) / fa::kFwdRows;
+  if (fa::launch_bwd_dq(b, p->dtype, p->d, causal, masked, s) != hipSuccess) return FA_ERR_LAUNCH;
+  b.ntiles = (p->N + fa::kBwdKeys - 1) / fa::kBwdKeys;
+  if (fa::launch_bwd_dkdv(b, p->dtype, p->d, causal, masked, s) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+int fa_mask_compile(const uint8_t* mask, int32_t nb, int32_t* row_ptr, int32_t* col_idx,
+                    int32_t* col_ptr, int32_t* row_idx, void* stream) {
+  if (!mask || nb <= 0 || !row_ptr || !col_idx || !col_ptr || !row_idx) return FA_ERR_ARG;
+  return fa::launch_mask_compile(mask, nb, row_ptr, col_idx, col_ptr, row_idx,
+                                 (hipStream_t)stream) == hipSuccess
+             ? FA_OK
+             : FA_ERR_LAUNCH;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported problem";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,443 @@
+// fa_bwd.hip -- backward pass of tiled exact attention on gfx950 matrix cores.
+//
+// The probabilities are never stored: both kernels rebuild each tile
+// P = exp(scale * Q K^T - LSE) from Q, K and the LSE saved by the forward
+// ("Passo para tras: recalcular em vez de armazenar", marketmaker.cc article;
+// "como funciona", tonho.wtf digest).  With dP = dO V^T and
+// D_i = dO_i . O_i (the d-length dot that replaces the N-length reduction
+// sum_j P_ij dP_ij, "como funciona", tonho.wtf digest):
+//     dS = P o (dP - D),   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+//
+// Two kernels, so that every output is reduced inside one workgroup and
+// written once (no atomics, no float32 dQ accumulator in memory, bitwise
+// repeatable):
+//   bwd_dq_kernel    query-outer (128 query rows per workgroup, 64-key steps):
+//                    computes D for its rows first, then S^T, dP^T, dS^T and
+//                    dQ^T += K^T dS^T.  It writes D for the second kernel.
+//   bwd_dkdv_kernel  key-outer (128 keys per workgroup, 4 waves x 32 keys;
+//                    64-query steps): S, dP, dS with one key per lane, then
+//                    dV += P^T dO and dK += dS^T Q.
+// The price is computing S and dP in both kernels: 14 d multiply-add FLOPs
+// per visible pair instead of 10 d.
+#include "fa_common.hpp"
+#include "fa_kernels.hpp"
+#include "fa_tiles.hpp"
+
+namespace fa {
+
+// ============================================================================
+// dQ kernel
+// ============================================================================
+template <int D>
+struct DqGeom {
+  static constexpr int KT = kKeyTile;
+  static constexpr int KP = D * 2 + 32;   // K tile: read by rows and by transpose
+  static constexpr int VP = D * 2 + 16;   // V tile: read by rows
+  static constexpr int KBYTES = KT * KP;
+  static constexpr int VBYTES = KT * VP;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int CPR = D / 8;
+  static constexpr int CPT = KT * CPR / kThreads;
+  static constexpr int NDB = D / 32;
+  static constexpr int NKS = D / 16;
+};
+
+template <typename T, int D, bool CAUSAL, bool MASKED>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p) {
+  using G = DqGeom<D>;
+  using V8 = typename Vec8<T>::type;
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int head = logical / p.ntiles;
+  int qt = logical % p.ntiles;
+  if (CAUSAL) qt = p.ntiles - 1 - qt;
+  const int N = p.N;
+  const int q0 = qt * kFwdRows;
+  const int qw0 = q0 + wave * 32;
+  const int q = qw0 + l32;
+  const int q_hi = min(q0 + kFwdRows, N) - 1;
+
+  const size_t head_off = (size_t)head * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * sizeof(T);
+  const Buf bq = make_buf((const T*)p.q + head_off, head_bytes);
+  const Buf bk = make_buf((const T*)p.k + head_off, head_bytes);
+  const Buf bv = make_buf((const T*)p.v + head_off, head_bytes);
+  const Buf bo = make_buf((const T*)p.o + head_off, head_bytes);
+  const Buf bdo = make_buf((const T*)p.dout + head_off, head_bytes);
+
+  KeyTileList<G::KT, CAUSAL, MASKED> tiles;
+  tiles.init(p.m, N, q0, q_hi);
+
+  // Q and dO fragments (B operands, k = head dim); D_i = dO_i . O_i
+  V8 qf[G::NKS], dof[G::NKS];
+  float dpart = 0.f;
+#pragma unroll
+  for (int t = 0; t < G::NKS; ++t) {
+    const uint32_t off = (uint32_t)(q * D + t * 16 + g * 8) * sizeof(T);
+    qf[t] = __builtin_bit_cast(V8, buf_load16(bq, off));
+    dof[t] = __builtin_bit_cast(V8, buf_load16(bdo, off));
+    const V8 of = __builtin_bit_cast(V8, buf_load16(bo, off));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dpart += to_f32(dof[t][i]) * to_f32(of[i]);
+  }
+  const float dq_d = dpart + __shfl_xor(dpart, 32, 64);
+  float lse2 = __builtin_huge_valf();  // rows past the end or with no visible key: P = 0
+  if (q < N) {
+    const float lse = p.lse[(size_t)head * N + q];
+    if (lse != kNegInf) lse2 = lse * kLog2e;
+    if (g == 0) p.dvec[(size_t)head * N + q] = dq_d;
+  }
+
+  f32x16 acc[G::NDB];
+#pragma unroll
+  for (int i = 0; i < G::NDB; ++i) acc[i] = f32x16{0};
+
+  u32x4 pk[G::CPT], pv[G::CPT];
+  auto gload = [&](int it) {
+    const int k0 = tiles.key0(it);
+#pragma unroll
+    for (int i = 0; i < G::CPT; ++i) {
+      const int ci = tid + i * kThreads;
+      const int row = ci / G::CPR, cc = ci % G::CPR;
+      const uint32_t off = (uint32_t)((k0 + row) * D * sizeof(T) + cc * 16);
+      pk[i] = buf_load16(bk, off);
+      pv[i] = buf_load16(bv, off);
+    }
+  };
+  auto lstore = [&](int stage) {
+    char* ks = smem + stage * G::STAGE;
+    char* vs = ks + G::KBYTES;
+#pragma unroll
+    for (int i = 0; i < G::CPT; ++i) {
+      const int ci = tid + i * kThreads;
+      const int row = ci / G::CPR, cc = ci % G::CPR;
+      *(u32x4*)(ks + row * G::KP + cc * 16) = pk[i];
+      *(u32x4*)(vs + row * G::VP + cc * 16) = pv[i];
+    }
+  };
+
+  const int ntiles = tiles.count;
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const bool more = it + 1 < ntiles;
+    if (more) gload(it + 1);
+
+    const int k0 = tiles.key0(it);
+    const char* ks = smem + cur * G::STAGE;
+    const char* vs = ks + G::KBYTES;
+    const bool active = !CAUSAL || k0 <= qw0 + 31;
+    if (active) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{0};
+        dp[kb] = f32x16{0};
+#pragma unroll
+        for (int t = 0; t < G::NKS; ++t) {
+          const V8 a = lds_read8<T>(ks + (kb * 32 + l32) * G::KP + t * 32 + g * 16);
+          s[kb] = mfma32(a, qf[t], s[kb]);
+          const V8 b = lds_read8<T>(vs + (kb * 32 + l32) * G::VP + t * 32 + g * 16);
+          dp[kb] = mfma32(b, dof[t], dp[kb]);
+        }
+      }
+      const bool need_mask = (CAUSAL && k0 + G::KT - 1 > qw0) || (k0 + G::KT > N);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[kb][r];
+          if (need_mask) {
+            const int key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+            if ((CAUSAL && key > q) || key >= N) x = kNegInf;
+          }
+          const float pr = fast_exp2(__builtin_fmaf(x, p.c, -lse2));
+          s[kb][r] = pr * (dp[kb][r] - dq_d) * p.scale;  // dS^T (scaled)
+        }
+      // dQ^T += K^T dS^T : A = K^T via transpose reads of the K tile
+      V8 bs[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kb = t >> 1, r0 = (t & 1) * 8;
+        bs[t] = pack8<T>(s[kb][r0 + 0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3],
+                         s[kb][r0 + 4], s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
+      }
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const char* p0 = ks + (t * 16 + g * 4 + tr_row) * G::KP + (db * 32 + tr_col) * 2;
+          const V8 a = lds_tr_operand<T>(p0, p0 + 8 * G::KP);
+          acc[db] = mfma32(a, bs[t], acc[db]);
+        }
+    }
+    if (more) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (q < N) {
+    T* row = (T*)p.dq + head_off + (size_t)q * D;
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        u32x2 w;
+        w[0] = pack2<T>(acc[db][rr * 4 + 0], acc[db][rr * 4 + 1]);
+        w[1] = pack2<T>(acc[db][rr * 4 + 2], acc[db][rr * 4 + 3]);
+        *(u32x2*)(row + db * 32 + rr * 8 + g * 4) = w;
+      }
+  }
+}
+
+// ============================================================================
+// dK / dV kernel
+// ============================================================================
+template <int D>
+struct DkvGeom {
+  static constexpr int QT = 64;             // queries per step
+  static constexpr int P = D * 2 + 32;      // Q / dO tile pitch: rows and transpose
+  static constexpr int TBYTES = QT * P;
+  static constexpr int STAGE = 2 * TBYTES + 2 * QT * 4;  // Q, dO, lse2, D
+  static constexpr int CPR = D / 8;
+  static constexpr int CPT = QT * CPR / kThreads;
+  static constexpr int NDB = D / 32;
+  static constexpr int NKS = D / 16;
+  static constexpr int NQB = QT / 32;       // 32-query blocks per step
+  static constexpr int WPE = D == 64 ? 2 : 1;  // waves per SIMD the registers allow
+};
+
+template <typename T, int D, bool CAUSAL, bool MASKED>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(DkvGeom<D>::WPE, DkvGeom<D>::WPE)))
+void bwd_dkdv_kernel(BwdParams p) {
+  using G = DkvGeom<D>;
+  using V8 = typename Vec8<T>::type;
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int head = logical / p.ntiles;
+  const int kt = logical % p.ntiles;  // ascending: under causal, longest first
+  const int N = p.N;
+  const int k0 = kt * kBwdKeys;
+  const int kw0 = k0 + wave * 32;
+  const int key = kw0 + l32;          // this lane's key
+
+  const size_t head_off = (size_t)head * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * sizeof(T);
+  const Buf bq = make_buf((const T*)p.q + head_off, head_bytes);
+  const Buf bk = make_buf((const T*)p.k + head_off, head_bytes);
+  const Buf bv = make_buf((const T*)p.v + head_off, head_bytes);
+  const Buf bdo = make_buf((const T*)p.dout + head_off, head_bytes);
+  const float* lse_h = p.lse + (size_t)head * N;
+  const float* dvec_h = p.dvec + (size_t)head * N;
+
+  QueryTileList<G::QT, CAUSAL, MASKED> tiles;
+  tiles.init(p.m, N, k0);
+
+  // K and V fragments: B operands of S = Q K^T and dP = dO V^T (k = head dim)
+  V8 kf[G::NKS], vf[G::NKS];
+#pragma unroll
+  for (int t = 0; t < G::NKS; ++t) {
+    const uint32_t off = (uint32_t)(key * D + t * 16 + g * 8) * sizeof(T);
+    kf[t] = __builtin_bit_cast(V8, buf_load16(bk, off));
+    vf[t] = __builtin_bit_cast(V8, buf_load16(bv, off));
+  }
+
+  f32x16 dka[G::NDB], dva[G::NDB];
+#pragma unroll
+  for (int i = 0; i < G::NDB; ++i) {
+    dka[i] = f32x16{0};
+    dva[i] = f32x16{0};
+  }
+
+  u32x4 pq[G::CPT], pd[G::CPT];
+  float plse = 0.f, pdv = 0.f;
+  auto gload = [&](int it) {
+    const int qs = tiles.query0(it);
+#pragma unroll
+    for (int i = 0; i < G::CPT; ++i) {
+      const int ci = tid + i * kThreads;
+      const int row = ci / G::CPR, cc = ci % G::CPR;
+      const uint32_t off = (uint32_t)((qs + row) * D * sizeof(T) + cc * 16);
+      pq[i] = buf_load16(bq, off);
+      pd[i] = buf_load16(bdo, off);
+    }
+    if (tid < G::QT) {
+      const int qq = qs + tid;
+      plse = __builtin_huge_valf();
+      pdv = 0.f;
+      if (qq < N) {
+        const float l = lse_h[qq];
+        if (l != kNegInf) plse = l * kLog2e;
+        pdv = dvec_h[qq];
+      }
+    }
+  };
+  auto lstore = [&](int stage) {
+    char* qs = smem + stage * G::STAGE;
+    char* ds = qs + G::TBYTES;
+    float* ls = (float*)(ds + G::TBYTES);
+#pragma unroll
+    for (int i = 0; i < G::CPT; ++i) {
+      const int ci = tid + i * kThreads;
+      const int row = ci / G::CPR, cc = ci % G::CPR;
+      *(u32x4*)(qs + row * G::P + cc * 16) = pq[i];
+      *(u32x4*)(ds + row * G::P + cc * 16) = pd[i];
+    }
+    if (tid < G::QT) {
+      ls[tid] = plse;
+      ls[G::QT + tid] = pdv;
+    }
+  };
+
+  const int ntiles = tiles.count;
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const bool more = it + 1 < ntiles;
+    if (more) gload(it + 1);
+
+    const int qs0 = tiles.query0(it);
+    const char* qsm = smem + cur * G::STAGE;
+    const char* dsm = qsm + G::TBYTES;
+    const float* lsm = (const float*)(dsm + G::TBYTES);
+    const bool active = !CAUSAL || qs0 + G::QT - 1 >= kw0;
+    if (active) {
+      f32x16 s[G::NQB], dp[G::NQB];
+#pragma unroll
+      for (int qb = 0; qb < G::NQB; ++qb) {
+        s[qb] = f32x16{0};
+        dp[qb] = f32x16{0};
+#pragma unroll
+        for (int t = 0; t < G::NKS; ++t) {
+          const V8 a = lds_read8<T>(qsm + (qb * 32 + l32) * G::P + t * 32 + g * 16);
+          s[qb] = mfma32(a, kf[t], s[qb]);
+          const V8 b = lds_read8<T>(dsm + (qb * 32 + l32) * G::P + t * 32 + g * 16);
+          dp[qb] = mfma32(b, vf[t], dp[qb]);
+        }
+      }
+      const bool need_mask = CAUSAL && qs0 < kw0 + 31;
+#pragma unroll
+      for (int qb = 0; qb < G::NQB; ++qb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const f32x4 l4 = *(const f32x4*)(lsm + qb * 32 + rr * 8 + g * 4);
+          const f32x4 d4 = *(const f32x4*)(lsm + G::QT + qb * 32 + rr * 8 + g * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = rr * 4 + e;
+            float x = s[qb][r];
+            if (need_mask) {
+              const int qq = qs0 + qb * 32 + rr * 8 + g * 4 + e;
+              if (key > qq) x = kNegInf;
+            }
+            const float pr = fast_exp2(__builtin_fmaf(x, p.c, -l4[e]));
+            s[qb][r] = pr;                                   // P
+            dp[qb][r] = pr * (dp[qb][r] - d4[e]) * p.scale;  // dS (scaled)
+          }
+        }
+      // dV += P^T dO,  dK += dS^T Q ; k-step t covers queries 16t .. 16t+15
+#pragma unroll
+      for (int t = 0; t < G::QT / 16; ++t) {
+        const int qb = t >> 1, r0 = (t & 1) * 8;
+        const V8 ap = pack8<T>(s[qb][r0 + 0], s[qb][r0 + 1], s[qb][r0 + 2], s[qb][r0 + 3],
+                               s[qb][r0 + 4], s[qb][r0 + 5], s[qb][r0 + 6], s[qb][r0 + 7]);
+        const V8 ad = pack8<T>(dp[qb][r0 + 0], dp[qb][r0 + 1], dp[qb][r0 + 2], dp[qb][r0 + 3],
+                               dp[qb][r0 + 4], dp[qb][r0 + 5], dp[qb][r0 + 6], dp[qb][r0 + 7]);
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+          const int off = (t * 16 + g * 4 + tr_row) * G::P + (db * 32 + tr_col) * 2;
+          const V8 bdo_ = lds_tr_operand<T>(dsm + off, dsm + off + 8 * G::P);
+          dva[db] = mfma32(ap, bdo_, dva[db]);
+          const V8 bq_ = lds_tr_operand<T>(qsm + off, qsm + off + 8 * G::P);
+          dka[db] = mfma32(ad, bq_, dka[db]);
+        }
+      }
+    }
+    if (more) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // C layout: lane -> head-dim column, register -> key row
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = kw0 + (r >> 2) * 8 + g * 4 + (r & 3);
+      if (kr < N) {
+        const size_t idx = head_off + (size_t)kr * D + db * 32 + l32;
+        ((T*)p.dk)[idx] = (T)dka[db][r];
+        ((T*)p.dv)[idx] = (T)dva[db][r];
+      }
+    }
+}
+
+template <typename T, int D>
+static hipError_t launch_dq_t(const BwdParams& p, bool causal, bool masked, hipStream_t s) {
+  dim3 grid(p.nheads * p.ntiles), block(kThreads);
+  if (causal && masked) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, true>), grid, block, 0, s, p);
+  else if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, false>), grid, block, 0, s, p);
+  else if (masked) hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_dkdv_t(const BwdParams& p, bool causal, bool masked, hipStream_t s) {
+  dim3 grid(p.nheads * p.ntiles), block(kThreads);
+  if (causal && masked) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, true>), grid, block, 0, s, p);
+  else if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, false>), grid, block, 0, s, p);
+  else if (masked) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                         hipStream_t s) {
+  if (dtype == 1)
+    return d == 64 ? launch_dq_t<_Float16, 64>(p, causal, masked, s)
+                   : launch_dq_t<_Float16, 128>(p, causal, masked, s);
+  return d == 64 ? launch_dq_t<__bf16, 64>(p, causal, masked, s)
+                 : launch_dq_t<__bf16, 128>(p, causal, masked, s);
+}
+
+hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                           hipStream_t s) {
+  if (dtype == 1)
+    return d == 64 ? launch_dkdv_t<_Float16, 64>(p, causal, masked, s)
+                   : launch_dkdv_t<_Float16, 128>(p, causal, masked, s);
+  return d == 64 ? launch_dkdv_t<__bf16, 64>(p, causal, masked, s)
+                 : launch_dkdv_t<__bf16, 128>(p, causal, masked, s);
+}
+
+}  // namespace fa

@@ -1,0 +1,136 @@
+// fa_common.hpp -- gfx950 building blocks shared by the attention kernels:
+// matrix-core (MFMA) wrappers, LDS transpose reads, buffer loads with hardware
+// range checking, conversions, and the workgroup -> tile mapping.
+//
+// Register layouts of v_mfma_f32_32x32x16_{f16,bf16} (wave64), confirmed by an
+// on-device layout check before any kernel was built on them:
+//   A (32 x 16):  lane l holds A[l % 32][8 * (l / 32) + i],  i = 0..7
+//   B (16 x 32):  lane l holds B[8 * (l / 32) + i][l % 32],  i = 0..7
+//   C (32 x 32):  lane l, register r holds
+//                 C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32],  r = 0..15
+// Only the pairing of A and B along k matters for the product, so any k
+// permutation applied to both operands gives the same C.
+//
+// ds_read_b64_tr_b16 (LDS transpose read), per group of 16 lanes: lane
+// j = 4a + b supplies the address of X[r0 + a][c0 + 4b .. 4b + 3] (row-major
+// 16-bit storage); lane i of the group then receives X[r0 + a][c0 + i] for
+// a = 0..3.  This turns a row-major tile into an MFMA operand whose k index
+// runs along the rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <typename T> struct Vec8;
+template <> struct Vec8<_Float16> { typedef f16x8 type; };
+template <> struct Vec8<__bf16> { typedef bf16x8 type; };
+
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even conversion of two floats into one packed 32-bit word
+// (low half = a).
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float a, float b) {
+  _Float16 x = (_Float16)a, y = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+template <> __device__ __forceinline__ uint32_t pack2<__bf16>(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+
+// Eight floats -> one MFMA operand of T.
+template <typename T>
+__device__ __forceinline__ typename Vec8<T>::type pack8(float x0, float x1, float x2, float x3,
+                                                       float x4, float x5, float x6, float x7) {
+  u32x4 w;
+  w[0] = pack2<T>(x0, x1);
+  w[1] = pack2<T>(x2, x3);
+  w[2] = pack2<T>(x4, x5);
+  w[3] = pack2<T>(x6, x7);
+  return __builtin_bit_cast(typename Vec8<T>::type, w);
+}
+
+// ---- LDS access -----------------------------------------------------------
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* lds_byte_ptr) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_byte_ptr));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// A/B operand of 8 x 16-bit gathered by two transpose reads (rows r0..r0+3
+// and r0+8..r0+11 of a row-major tile, pitch in bytes), see header comment.
+template <typename T>
+__device__ __forceinline__ typename Vec8<T>::type lds_tr_operand(const char* p0, const char* p1) {
+  u32x2 lo = lds_read_tr16(p0);
+  u32x2 hi = lds_read_tr16(p1);
+  u32x4 w;
+  w[0] = lo[0];
+  w[1] = lo[1];
+  w[2] = hi[0];
+  w[3] = hi[1];
+  return __builtin_bit_cast(typename Vec8<T>::type, w);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Vec8<T>::type lds_read8(const char* p) {
+  return __builtin_bit_cast(typename Vec8<T>::type, *(const u32x4*)p);
+}
+
+// ---- global memory through buffer resources -------------------------------
+// Loads at byte offsets >= num_bytes return zeros (hardware range check), which
+// is how ragged sequence tails are padded without branches.
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ Buf make_buf(const void* base, uint32_t num_bytes) {
+  Buf b;
+  b.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)num_bytes, 0x00020000);
+  return b;
+}
+__device__ __forceinline__ u32x4 buf_load16(const Buf& b, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b.r, byte_off, 0, 0));
+}
+
+// ---- workgroup -> work-item mapping -----------------------------------------
+// Workgroups are handed to the 8 XCDs round-robin by linear id.  Remap so that
+// each XCD receives one contiguous range of the logical order (head-major):
+// all tiles of a head then share one L2.  A bijection for any grid size.
+__device__ __forceinline__ int xcd_remap(int linear, int total) {
+  const int nx = 8;
+  int x = linear % nx, slot = linear / nx;
+  int per = total / nx, rem = total % nx;
+  return x * per + (x < rem ? x : rem) + slot;
+}
+
+__device__ __forceinline__ float wave_max_pair(float v) {
+  // lanes l and l ^ 32 hold the two halves of one query's row
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace fa

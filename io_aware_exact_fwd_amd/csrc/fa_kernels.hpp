@@ -1,0 +1,92 @@
+// fa_kernels.hpp -- parameter blocks and launchers of the attention kernels
+// (host-visible declarations; the kernels live in fa_fwd.hip, fa_bwd.hip,
+// fa_f32.hip and fa_mask.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Tile geometry of the matrix-core kernels.
+constexpr int kFwdRows = 128;   // query rows per forward / dQ workgroup (4 waves x 32)
+constexpr int kKeyTile = 64;    // keys per inner step of the forward / dQ loop
+constexpr int kBwdKeys = 128;   // keys per dK/dV workgroup (4 waves x 32)
+constexpr int kThreads = 256;
+
+// Block-sparse lists compiled from the dense block mask (see fa_mask_compile).
+struct MaskLists {
+  const int32_t* row_ptr;  // [nb + 1]
+  const int32_t* col_idx;  // kept key blocks per query block
+  const int32_t* col_ptr;  // [nb + 1]
+  const int32_t* row_idx;  // query blocks per key block
+  int32_t mask_block;      // multiple of 128
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int N;
+  int nheads;     // B * H
+  int nqt;        // query tiles per head
+  float c;        // scale * log2(e)
+  MaskLists m;
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;    // D_i = dO_i . O_i, float32 [B*H*N]
+  int N;
+  int nheads;
+  int ntiles;     // query tiles (dQ kernel) or key tiles (dK/dV kernel) per head
+  float c;        // scale * log2(e)
+  float scale;
+  MaskLists m;
+};
+
+struct F32Params {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* o;
+  const float* dout;
+  float* out_o;
+  float* lse;       // forward output / backward input
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dvec;
+  const uint8_t* block_mask;
+  int mask_block;
+  int N;
+  int nheads;
+  int d;
+  int causal;
+  float c;
+  float scale;
+};
+
+// Each launcher returns hipSuccess or the launch error.
+hipError_t launch_fwd(const FwdParams& p, int dtype, int d, bool causal, bool masked,
+                      hipStream_t s);
+hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                         hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                           hipStream_t s);
+hipError_t launch_f32_fwd(const F32Params& p, hipStream_t s);
+hipError_t launch_f32_bwd(const F32Params& p, hipStream_t s);
+hipError_t launch_mask_compile(const uint8_t* mask, int nb, int32_t* row_ptr, int32_t* col_idx,
+                               int32_t* col_ptr, int32_t* row_idx, hipStream_t s);
+
+}  // namespace fa

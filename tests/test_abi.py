@@ -1,0 +1,118 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+that include/fa.h declares, and rejects invalid problems before any launch."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from io_aware_exact_fwd_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libfa_mi355x.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared_functions() == sorted(B.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    L = ctypes.CDLL(B.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert B.fa_version() == 10000
+    assert B.fa_status_string(0) == "ok"
+    assert "workspace" in B.fa_status_string(B.FA_ERR_WORKSPACE)
+    assert B.fa_status_string(12345) == "unknown status"
+
+
+def _problem(**kw):
+    p = B.FaProblem()
+    p.B, p.H, p.N, p.d = kw.get("B", 2), kw.get("H", 3), kw.get("N", 256), kw.get("d", 64)
+    p.dtype = kw.get("dtype", B.FA_F16)
+    p.causal = kw.get("causal", 0)
+    p.scale = kw.get("scale", 0.125)
+    p.block_mask = kw.get("block_mask", None)
+    p.mask_block = kw.get("mask_block", 0)
+    return p
+
+
+def test_workspace_sizes():
+    p = _problem()
+    assert B.fa_workspace_size(p, 0) == 0
+    dvec = 2 * 3 * 256 * 4
+    assert B.fa_workspace_size(p, 1) == (dvec + 255) // 256 * 256
+    pm = _problem(N=512, block_mask=0x1000, mask_block=128)
+    nb = 4
+    lists = 2 * 256 + 2 * ((nb * nb * 4 + 255) // 256 * 256)
+    assert B.fa_workspace_size(pm, 0) == lists
+    assert B.fa_workspace_size(pm, 1) == (2 * 3 * 512 * 4 + 255) // 256 * 256 + lists
+    # float32 reads the dense mask directly: no lists
+    assert B.fa_workspace_size(_problem(N=512, dtype=B.FA_F32, block_mask=0x1000,
+                                        mask_block=128), 0) == 0
+    assert B.fa_workspace_size(_problem(d=96), 1) == 0  # invalid problem
+
+
+FAKE = 0x10000  # an aligned non-null address; never dereferenced (errors come first)
+
+
+def _fwd(p, ws=None, ws_n=0, ptrs=(FAKE,) * 5):
+    L = B.lib()
+    return L.fa_fwd(ctypes.byref(p), *ptrs, ws, ws_n, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"d": 96}, B.FA_ERR_UNSUPPORTED),
+    ({"d": 32}, B.FA_ERR_UNSUPPORTED),
+    ({"dtype": 7}, B.FA_ERR_UNSUPPORTED),
+    ({"N": 0}, B.FA_ERR_ARG),
+    ({"B": -1}, B.FA_ERR_ARG),
+    ({"scale": math.inf}, B.FA_ERR_ARG),
+    ({"scale": math.nan}, B.FA_ERR_ARG),
+    ({"causal": 2}, B.FA_ERR_ARG),
+    ({"block_mask": FAKE, "mask_block": 64}, B.FA_ERR_UNSUPPORTED),
+    ({"block_mask": FAKE, "mask_block": 128, "N": 200}, B.FA_ERR_UNSUPPORTED),
+    ({"N": 1 << 24, "d": 128}, B.FA_ERR_UNSUPPORTED),
+])
+def test_invalid_problems_rejected(kw, status):
+    assert _fwd(_problem(**kw)) == status
+
+
+def test_null_and_misaligned_pointers_rejected():
+    p = _problem()
+    assert _fwd(p, ptrs=(FAKE, FAKE, None, FAKE, FAKE)) == B.FA_ERR_ARG
+    assert _fwd(p, ptrs=(FAKE, FAKE + 2, FAKE, FAKE, FAKE)) == B.FA_ERR_ARG
+    assert B.lib().fa_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.FA_ERR_ARG
+
+
+def test_workspace_checked_before_launch():
+    pm = _problem(N=512, block_mask=FAKE, mask_block=128)
+    need = B.fa_workspace_size(pm, 0)
+    assert _fwd(pm, ws=None, ws_n=0) == B.FA_ERR_WORKSPACE
+    assert _fwd(pm, ws=FAKE, ws_n=need - 1) == B.FA_ERR_WORKSPACE
+    p = _problem()
+    L = B.lib()
+    args = [FAKE] * 9
+    assert L.fa_bwd(ctypes.byref(p), *args, None, 0, None) == B.FA_ERR_WORKSPACE
+    assert L.fa_bwd(ctypes.byref(p), *args, FAKE, B.fa_workspace_size(p, 1) - 4,
+                    None) == B.FA_ERR_WORKSPACE
+
+
+def test_mask_compile_argument_checks():
+    L = B.lib()
+    assert L.fa_mask_compile(None, 4, FAKE, FAKE, FAKE, FAKE, None) == B.FA_ERR_ARG
+    assert L.fa_mask_compile(FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == B.FA_ERR_ARG
