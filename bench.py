@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Throughput of tiled exact attention, forward + backward, on one MI355X.
+
+One step = the whole path over one batch of the workload: fa_fwd, then the two
+backward stages fa_bwd_dq and fa_bwd_dkdv, all through the C ABI.  Default
+workload: GPT-2-medium-shaped attention, B=64 H=16 N=1024 d=64, fp16, causal,
+scale 1/8 (the shape of the paper's headline measurement), synthetic seeded
+inputs already resident in HBM.
+
+Reported value: fwd+bwd TFLOP/s with matrix-core FLOPs counted over kept
+(query, key) pairs -- 4 d per pair forward and 10 d per pair backward
+(Q K^T, P V; the score recompute, dV, dP, dK, dQ).  The backward's extra
+score/dP recompute in the dQ kernel is work done but not credited.
+
+Prints ONE JSON line (plus a few human-readable lines on stderr).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s (B64·H16·N1024·d64 fp16 causal), % of MFMA peak"
+# MI355X published peaks: dense fp16/bf16 matrix 2.5 PFLOP/s (= 256 CUs x 4096
+# FLOP/clk x 2.4 GHz), HBM3E 8 TB/s.
+PEAK_MFMA_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+PEAK_HBM_GBS = 8000.0
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = os.path.join(ROOT, "io_aware_exact_fwd_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest():
+    """sha256 over the kernel sources; measured HBM traffic is only reported
+    while it matches the digest recorded with the counters."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(KERNEL_SOURCES, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    absent or taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    if rec.get("source_sha256") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(f"{kernel}/{workload}")
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def kernel_work(w):
+    """Per-launch algorithmic work of each kernel of the step (FLOPs, bytes).
+
+    Units: kept (query, key) pairs.  fwd: Q K^T and P V = 4 d FLOP/pair.
+    dq kernel: S, dP and dQ products = 6 d FLOP/pair.  dkdv kernel: S, dP, dV,
+    dK products = 8 d FLOP/pair.  Bytes: each tensor the kernel must read or
+    write, once."""
+    from io_aware_exact_fwd_amd.workloads import kept_pairs_per_head
+
+    pairs = kept_pairs_per_head(w.N, w.causal, w.block_mask(), w.mask_block) * w.B * w.H
+    x = w.B * w.H * w.N * w.d * w.elem_bytes  # one (B, H, N, d) tensor
+    n4 = w.B * w.H * w.N * 4                  # one float32 (B, H, N) vector
+    return {
+        "fwd": {"flops": 4.0 * w.d * pairs, "bytes": 4 * x + n4},            # Q K V -> O, LSE
+        "dq": {"flops": 6.0 * w.d * pairs, "bytes": 6 * x + 2 * n4},         # Q K V O dO LSE -> dQ D
+        "dkdv": {"flops": 8.0 * w.d * pairs, "bytes": 6 * x + 2 * n4},       # Q K V dO LSE D -> dK dV
+    }
+
+
+def roofline(name, work, ms):
+    """Roofline entry for one kernel: bound = the larger of its compulsory-byte
+    time at peak HBM and its FLOP time at peak matrix rate."""
+    t_hbm = work["bytes"] / (PEAK_HBM_GBS * 1e9)
+    t_mfma = work["flops"] / (PEAK_MFMA_TFLOPS * 1e12)
+    sec = ms / 1e3
+    if t_hbm > t_mfma:
+        ach = work["bytes"] / sec / 1e9
+        return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    ach = work["flops"] / sec / 1e12
+    return {"kernel": name, "bound": "mfma", "achieved": round(ach, 1),
+            "peak": round(PEAK_MFMA_TFLOPS, 1), "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_MFMA_TFLOPS, 4), "traffic": None}
+
+
+def cpu_baseline(w, inputs, seconds):
+    """Time the fp64 oracle (as it stands) on whole heads of the same workload
+    until `seconds` have passed; report its fwd+bwd rate in the metric's unit."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from io_aware_exact_fwd_amd.workloads import kept_pairs_per_head
+    from oracle import attention_backward, attention_forward
+
+    q, k, v, do = inputs
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    bm = w.block_mask()
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        qn, kn, vn, don = (t[b, h].float().numpy() for t in (q, k, v, do))
+        attention_forward(qn, kn, vn, w.scale, w.causal, bm, w.mask_block)
+        attention_backward(qn, kn, vn, don, w.scale, w.causal, bm, w.mask_block)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    flops = 14.0 * w.d * kept_pairs_per_head(w.N, w.causal, bm, w.mask_block) * done
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads of {w.name}, fwd+bwd, numpy float64, "
+                      f"{el:.1f} s on {len(os.sched_getaffinity(0))} host cores "
+                      f"({platform.processor() or platform.machine()})"}
+
+
+def _short(name):
+    for key in ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "mask_compile", "f32_"):
+        if key in name:
+            return key + name[name.find(key) + len(key):][:40]
+    return name[:60]
+
+
+def summarize_stats(path):
+    import csv
+
+    rows = list(csv.DictReader(open(path)))
+    print(f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
+    for r in rows:
+        print(f"{_short(r['Name']):60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+              f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} "
+              f"{float(r['Percentage']):6.2f}")
+
+
+def summarize_pmc(path):
+    import collections
+    import csv
+
+    agg = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for r in csv.DictReader(open(path)):
+        k = _short(r["Kernel_Name"])
+        agg[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k].add(r["Dispatch_Id"])
+    for k in agg:
+        n = len(disp[k])
+        vals = " ".join(f"{c}={v / n:.6g}" for c, v in sorted(agg[k].items()))
+        print(f"{k:60s} dispatches={n} per-dispatch: {vals}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_medium")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU budget of the oracle baseline (0 to skip)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain elementwise copy of 2 x 512 MiB (counter calibration)")
+    ap.add_argument("--summarize-stats", metavar="CSV",
+                    help="print a summary of a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--summarize-pmc", metavar="CSV",
+                    help="print per-kernel means of a rocprofv3 counter_collection.csv and exit")
+    args = ap.parse_args()
+
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(attention shards over (batch, head) with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from io_aware_exact_fwd_amd import bwd_workspace, fa_bwd_dkdv, fa_bwd_dq, fa_fwd
+    from io_aware_exact_fwd_amd.workloads import WORKLOADS, bwd_flops, fwd_flops, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.copy_probe:
+        n = 256 * 1024 * 1024  # 512 MiB of fp16 read, 512 MiB written per launch
+        x = torch.ones(n, dtype=torch.float16, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 5 launches, each reads {2 * n} B and writes {2 * n} B")
+        return
+    w = WORKLOADS[args.workload]
+    inputs = make_inputs(w.B, w.H, w.N, w.d, w.dtype)
+    q, k, v, do = (t.to(dev) for t in inputs)
+    bm = w.block_mask()
+    bmd = None if bm is None else torch.as_tensor(bm, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    p, ws, ws_n, bmt = bwd_workspace(q, w.causal, w.scale, bmd, w.mask_block)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa_fwd(q, k, v, w.causal, w.scale, bmt, w.mask_block, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        fa_bwd_dq(p, q, k, v, o, do, lse, dq, ws, ws_n)
+        if ev is not None:
+            ev[2].record()
+        fa_bwd_dkdv(p, q, k, v, do, lse, dk, dv, ws, ws_n)
+        if ev is not None:
+            ev[3].record()
+
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} "
+        f"causal={w.causal} mask={w.mask}; warmup {args.warmup}, steps {args.steps}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = {"fwd": 0.0, "dq": 0.0, "dkdv": 0.0}
+    for ev in events:
+        ms["fwd"] += ev[0].elapsed_time(ev[1])
+        ms["dq"] += ev[1].elapsed_time(ev[2])
+        ms["dkdv"] += ev[2].elapsed_time(ev[3])
+    ms = {kk: vv / args.steps for kk, vv in ms.items()}
+    ms_step = wall * 1e3 / args.steps
+    f_fwd, f_bwd = fwd_flops(w), bwd_flops(w)
+    value = (f_fwd + f_bwd) / (ms_step / 1e3) / 1e12
+    work = kernel_work(w)
+    dom = max(ms, key=ms.get)
+    roof = roofline(dom, work[dom], ms[dom])
+    roof["traffic"] = measured_traffic(dom, w.name)
+
+    for kk in ms:
+        r = roofline(kk, work[kk], ms[kk])
+        log(f"[bench] {kk:5s} {ms[kk] * 1e3:9.1f} us  {r['achieved']:8.1f} {r['unit']} "
+            f"({100 * r['frac']:.1f}% of {r['bound']} peak)")
+    log(f"[bench] step {ms_step * 1e3:.1f} us -> {value:.1f} TFLOP/s "
+        f"({100 * value / PEAK_MFMA_TFLOPS:.1f}% of {PEAK_MFMA_TFLOPS:.0f}); fwd alone "
+        f"{f_fwd / (ms['fwd'] / 1e3) / 1e12:.1f} TFLOP/s")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s ...")
+        cpu = cpu_baseline(w, inputs, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "dtype": w.dtype, "causal": w.causal, "scale": w.scale,
+                   "block_mask": w.mask},
+        "pct_of_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
+        "fwd_tflops": round(f_fwd / (ms["fwd"] / 1e3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / ((ms["dq"] + ms["dkdv"]) / 1e3) / 1e12, 2),
+        "kernel_ms": {kk: round(vv, 5) for kk, vv in ms.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -102,6 +102,20 @@ int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, con
            const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
            size_t ws_bytes, void* stream);
 
+/* The two stages of fa_bwd, for callers that schedule or time them apart.
+ * fa_bwd_dq: computes D_i = dO_i . O_i into the workspace (and, with a block
+ *   mask, the compiled block lists), then writes dq.
+ * fa_bwd_dkdv: writes dk and dv; reads D (and the lists) from the SAME
+ *   workspace, so it must be enqueued after fa_bwd_dq on the same stream with
+ *   unchanged arguments.  fa_bwd is exactly fa_bwd_dq followed by fa_bwd_dkdv.
+ * Arguments, layouts and errors are those of fa_bwd. */
+int fa_bwd_dq(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
+              const void* dout, const float* lse, void* dq, void* workspace, size_t ws_bytes,
+              void* stream);
+int fa_bwd_dkdv(const fa_problem* p, const void* q, const void* k, const void* v,
+                const void* dout, const float* lse, void* dk, void* dv, void* workspace,
+                size_t ws_bytes, void* stream);
+
 /* Block-mask compilation (the step both passes run first when a block mask is
  * given).  mask: device uint8 [nb][nb]; writes, all int32 device arrays:
  *   row_ptr[nb + 1], col_idx[nnz]: for query block r, the kept key blocks

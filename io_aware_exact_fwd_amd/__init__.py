@@ -14,7 +14,10 @@ from .binding import (  # noqa: F401
     FA_F16,
     FA_F32,
     FaError,
+    bwd_workspace,
     fa_bwd,
+    fa_bwd_dkdv,
+    fa_bwd_dq,
     fa_fwd,
     fa_mask_compile,
     fa_status_string,

@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = 0, -1, -2, -3, -4
 
-EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_bwd", "fa_mask_compile", "fa_status_string",
-           "fa_version")
+EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv",
+           "fa_mask_compile", "fa_status_string", "fa_version")
 
 
 class FaProblem(ctypes.Structure):
@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd.restype = ctypes.c_int
     L.fa_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.fa_bwd.restype = ctypes.c_int
+    L.fa_bwd_dq.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.fa_bwd_dq.restype = ctypes.c_int
+    L.fa_bwd_dkdv.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.fa_bwd_dkdv.restype = ctypes.c_int
     L.fa_mask_compile.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     L.fa_mask_compile.restype = ctypes.c_int
     L.fa_status_string.argtypes = [ctypes.c_int]
@@ -179,6 +183,35 @@ def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, block_mask=None, mas
     if st != FA_OK:
         raise FaError("fa_bwd", st)
     return dq, dk, dv
+
+
+def bwd_workspace(q, causal=False, scale=None, block_mask=None, mask_block=128):
+    """(problem, workspace tensor, workspace bytes) for the two backward stages."""
+    import torch
+
+    bm = _mask_arg(block_mask, q)
+    p = make_problem(q, causal, scale, bm, mask_block)
+    ws_n = fa_workspace_size(p, 1)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    return p, ws, ws_n, bm
+
+
+def fa_bwd_dq(p, q, k, v, o, dout, lse, dq, ws, ws_n):
+    """First backward stage (D and dQ) for a problem from ``bwd_workspace``."""
+    st = lib().fa_bwd_dq(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                         dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), ws.data_ptr(), ws_n,
+                         _stream(q))
+    if st != FA_OK:
+        raise FaError("fa_bwd_dq", st)
+
+
+def fa_bwd_dkdv(p, q, k, v, dout, lse, dk, dv, ws, ws_n):
+    """Second backward stage (dK, dV); same problem and workspace as fa_bwd_dq."""
+    st = lib().fa_bwd_dkdv(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           dout.data_ptr(), lse.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           ws.data_ptr(), ws_n, _stream(q))
+    if st != FA_OK:
+        raise FaError("fa_bwd_dkdv", st)
 
 
 def fa_mask_compile(block_mask):

@@ -40,31 +40,34 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfa_mi355x)")
 
 
-def _compile(src: str, hipcc: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc, *HIP_FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, hipcc: str, build_dir: str, defines) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [hipcc, *HIP_FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, defines=(), out: str = LIB) -> str:
+    """Compile and link; `defines` are extra preprocessor definitions (tuning
+    knobs of the kernels), `out` the library path."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    build_dir = BUILD if out == LIB else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     workers = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "8"))))
     with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(lambda s: _compile(s, hipcc), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, hipcc, build_dir, defines), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -146,77 +146,129 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
                                                                                     : FA_ERR_LAUNCH;
 }
 
-int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
-           const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
-           size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared checks and parameter block of the backward entry points.  Pointers a
+// stage does not use may be NULL; `need` lists which ones must be present.
+int bwd_setup(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
+              const void* dout, const float* lse, const void* dq, const void* dk, const void* dv,
+              void* workspace, size_t ws_bytes, bool want_dq, bool want_dkdv,
+              fa::BwdParams* b) {
   int st = check_problem(p);
   if (st != FA_OK) return st;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
-    return FA_ERR_ARG;
+  if (!q || !k || !v || !dout || !lse) return FA_ERR_ARG;
+  if (want_dq && (!o || !dq)) return FA_ERR_ARG;
+  if (want_dkdv && (!dk || !dv)) return FA_ERR_ARG;
+  const void* ptrs[] = {q, k, v, dout, want_dq ? o : q, want_dq ? dq : q, want_dkdv ? dk : q,
+                        want_dkdv ? dv : q};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_ARG;
+  if ((uintptr_t)lse & 3u) return FA_ERR_ARG;
   const size_t need = fa_workspace_size(p, 1);
   if (!workspace || ws_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ARG;
-  hipStream_t s = (hipStream_t)stream;
-  const float c = p->scale * fa::kLog2e;
-  const int nheads = p->B * p->H;
-  float* dvec = (float*)workspace;
-
-  if (p->dtype == FA_F32) {
-    fa::F32Params f = {};
-    f.q = (const float*)q;
-    f.k = (const float*)k;
-    f.v = (const float*)v;
-    f.o = (const float*)o;
-    f.dout = (const float*)dout;
-    f.lse = (float*)lse;
-    f.dq = (float*)dq;
-    f.dk = (float*)dk;
-    f.dv = (float*)dv;
-    f.dvec = dvec;
-    f.block_mask = p->block_mask;
-    f.mask_block = p->mask_block;
-    f.N = p->N;
-    f.nheads = nheads;
-    f.d = p->d;
-    f.causal = p->causal;
-    f.c = c;
-    f.scale = p->scale;
-    return fa::launch_f32_bwd(f, s) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
-  }
-
-  fa::BwdParams b;
-  b.q = q;
-  b.k = k;
-  b.v = v;
-  b.o = o;
-  b.dout = dout;
-  b.lse = lse;
-  b.dq = dq;
-  b.dk = dk;
-  b.dv = dv;
-  b.dvec = dvec;
-  b.N = p->N;
-  b.nheads = nheads;
-  b.c = c;
-  b.scale = p->scale;
-  b.m = no_lists();
-  const bool masked = p->block_mask != nullptr;
-  if (masked) {
-    Lists l = carve_lists(p, (char*)workspace + dvec_bytes(p));
-    if (fa::launch_mask_compile(p->block_mask, p->N / p->mask_block, l.row_ptr, l.col_idx,
-                                l.col_ptr, l.row_idx, s) != hipSuccess)
-      return FA_ERR_LAUNCH;
-    b.m = mask_lists(p, l);
-  }
-  const bool causal = p->causal != 0;
-  b.ntiles = (p->N + fa::kFwdRows - 1) / fa::kFwdRows;
-  if (fa::launch_bwd_dq(b, p->dtype, p->d, causal, masked, s) != hipSuccess) return FA_ERR_LAUNCH;
-  b.ntiles = (p->N + fa::kBwdKeys - 1) / fa::kBwdKeys;
-  if (fa::launch_bwd_dkdv(b, p->dtype, p->d, causal, masked, s) != hipSuccess)
-    return FA_ERR_LAUNCH;
+  b->q = q;
+  b->k = k;
+  b->v = v;
+  b->o = o;
+  b->dout = dout;
+  b->lse = lse;
+  b->dq = const_cast<void*>(dq);
+  b->dk = const_cast<void*>(dk);
+  b->dv = const_cast<void*>(dv);
+  b->dvec = (float*)workspace;
+  b->N = p->N;
+  b->nheads = p->B * p->H;
+  b->c = p->scale * fa::kLog2e;
+  b->scale = p->scale;
+  b->m = no_lists();
+  if (p->block_mask) b->m = mask_lists(p, carve_lists(p, (char*)workspace + dvec_bytes(p)));
   return FA_OK;
+}
+
+fa::F32Params f32_params(const fa_problem* p, const fa::BwdParams& b) {
+  fa::F32Params f = {};
+  f.q = (const float*)b.q;
+  f.k = (const float*)b.k;
+  f.v = (const float*)b.v;
+  f.o = (const float*)b.o;
+  f.dout = (const float*)b.dout;
+  f.lse = (float*)b.lse;
+  f.dq = (float*)b.dq;
+  f.dk = (float*)b.dk;
+  f.dv = (float*)b.dv;
+  f.dvec = b.dvec;
+  f.block_mask = p->block_mask;
+  f.mask_block = p->mask_block;
+  f.N = p->N;
+  f.nheads = b.nheads;
+  f.d = p->d;
+  f.causal = p->causal;
+  f.c = b.c;
+  f.scale = p->scale;
+  return f;
+}
+
+int run_dq(const fa_problem* p, fa::BwdParams b, hipStream_t s) {
+  if (p->dtype == FA_F32)
+    return fa::launch_f32_dq(f32_params(p, b), s) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  const bool masked = p->block_mask != nullptr;
+  if (masked && fa::launch_mask_compile(p->block_mask, p->N / p->mask_block,
+                                        (int32_t*)b.m.row_ptr, (int32_t*)b.m.col_idx,
+                                        (int32_t*)b.m.col_ptr, (int32_t*)b.m.row_idx,
+                                        s) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  b.ntiles = (p->N + fa::kFwdRows - 1) / fa::kFwdRows;
+  return fa::launch_bwd_dq(b, p->dtype, p->d, p->causal != 0, masked, s) == hipSuccess
+             ? FA_OK
+             : FA_ERR_LAUNCH;
+}
+
+int run_dkdv(const fa_problem* p, fa::BwdParams b, hipStream_t s) {
+  if (p->dtype == FA_F32)
+    return fa::launch_f32_dkdv(f32_params(p, b), s) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  b.ntiles = (p->N + fa::kBwdKeys - 1) / fa::kBwdKeys;
+  return fa::launch_bwd_dkdv(b, p->dtype, p->d, p->causal != 0, p->block_mask != nullptr, s) ==
+                 hipSuccess
+             ? FA_OK
+             : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t ws_bytes, void* stream) {
+  fa::BwdParams b;
+  int st = bwd_setup(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, true, true, &b);
+  if (st != FA_OK) return st;
+  st = run_dq(p, b, (hipStream_t)stream);
+  if (st != FA_OK) return st;
+  return run_dkdv(p, b, (hipStream_t)stream);
+}
+
+int fa_bwd_dq(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
+              const void* dout, const float* lse, void* dq, void* workspace, size_t ws_bytes,
+              void* stream) {
+  fa::BwdParams b;
+  int st = bwd_setup(p, q, k, v, o, dout, lse, dq, nullptr, nullptr, workspace, ws_bytes, true,
+                     false, &b);
+  if (st != FA_OK) return st;
+  return run_dq(p, b, (hipStream_t)stream);
+}
+
+int fa_bwd_dkdv(const fa_problem* p, const void* q, const void* k, const void* v,
+                const void* dout, const float* lse, void* dk, void* dv, void* workspace,
+                size_t ws_bytes, void* stream) {
+  fa::BwdParams b;
+  int st = bwd_setup(p, q, k, v, nullptr, dout, lse, nullptr, dk, dv, workspace, ws_bytes, false,
+                     true, &b);
+  if (st != FA_OK) return st;
+  return run_dkdv(p, b, (hipStream_t)stream);
 }
 
 int fa_mask_compile(const uint8_t* mask, int32_t nb, int32_t* row_ptr, int32_t* col_idx,

@@ -51,7 +51,7 @@ void bwd_dq_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
@@ -129,6 +129,7 @@ void bwd_dq_kernel(BwdParams p) {
     gload(0);
     lstore(0);
   }
+  wait_all_memory();
   __syncthreads();
 
   const int tr_row = (lane & 15) >> 2;
@@ -157,17 +158,24 @@ void bwd_dq_kernel(BwdParams p) {
           dp[kb] = mfma32(b, dof[t], dp[kb]);
         }
       }
+      // hide keys in the future of the query and past the end: key of register
+      // r is k0 + g*4 + C(kb, r) with C = kb*32 + (r/4)*8 + r%4; hidden iff
+      // C > bound
       const bool need_mask = (CAUSAL && k0 + G::KT - 1 > qw0) || (k0 + G::KT > N);
+      if (need_mask) {
+        int bound = N - 1 - k0 - g * 4;
+        if (CAUSAL) bound = min(bound, q - k0 - g * 4);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + (r >> 2) * 8 + (r & 3) > bound) s[kb][r] = kNegInf;
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r];
-          if (need_mask) {
-            const int key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-            if ((CAUSAL && key > q) || key >= N) x = kNegInf;
-          }
-          const float pr = fast_exp2(__builtin_fmaf(x, p.c, -lse2));
+          const float pr = fast_exp2(__builtin_fmaf(s[kb][r], p.c, -lse2));
           s[kb][r] = pr * (dp[kb][r] - dq_d) * p.scale;  // dS^T (scaled)
         }
       // dQ^T += K^T dS^T : A = K^T via transpose reads of the K tile
@@ -232,7 +240,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
@@ -317,6 +325,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     gload(0);
     lstore(0);
   }
+  wait_all_memory();
   __syncthreads();
 
   const int tr_row = (lane & 15) >> 2;
@@ -346,7 +355,18 @@ void bwd_dkdv_kernel(BwdParams p) {
           dp[qb] = mfma32(b, vf[t], dp[qb]);
         }
       }
+      // causal: hide queries before this lane's key.  Query of register r in
+      // block qb is qs0 + g*4 + C(qb, r), C = qb*32 + (r/4)*8 + r%4; hidden
+      // iff C < key - qs0 - g*4
       const bool need_mask = CAUSAL && qs0 < kw0 + 31;
+      if (need_mask) {
+        const int bound = key - qs0 - g * 4;
+#pragma unroll
+        for (int qb = 0; qb < G::NQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (qb * 32 + (r >> 2) * 8 + (r & 3) < bound) s[qb][r] = kNegInf;
+      }
 #pragma unroll
       for (int qb = 0; qb < G::NQB; ++qb)
 #pragma unroll
@@ -356,12 +376,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = rr * 4 + e;
-            float x = s[qb][r];
-            if (need_mask) {
-              const int qq = qs0 + qb * 32 + rr * 8 + g * 4 + e;
-              if (key > qq) x = kNegInf;
-            }
-            const float pr = fast_exp2(__builtin_fmaf(x, p.c, -l4[e]));
+            const float pr = fast_exp2(__builtin_fmaf(s[qb][r], p.c, -l4[e]));
             s[qb][r] = pr;                                   // P
             dp[qb][r] = pr * (dp[qb][r] - d4[e]) * p.scale;  // dS (scaled)
           }

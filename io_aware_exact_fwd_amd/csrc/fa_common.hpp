@@ -47,15 +47,25 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // Round-to-nearest-even conversion of two floats into one packed 32-bit word
-// (low half = a).
+// (low half = a); one v_cvt_pk_{f16,bf16}_f32 on gfx950.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
 template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float a, float b) {
-  _Float16 x = (_Float16)a, y = (_Float16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
 }
 template <> __device__ __forceinline__ uint32_t pack2<__bf16>(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// Sum of the two 16-bit values packed in w, added to acc (v_dot2 with (1, 1)).
+template <typename T> __device__ __forceinline__ float add_pair(uint32_t w, float acc);
+template <> __device__ __forceinline__ float add_pair<_Float16>(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), (f16x2){1, 1}, acc, false);
+}
+template <> __device__ __forceinline__ float add_pair<__bf16>(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), (bf16x2){1, 1}, acc, false);
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
@@ -125,10 +135,28 @@ __device__ __forceinline__ int xcd_remap(int linear, int total) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// IEEE maximum (NaN-propagating): v_maximum3_f32 on gfx950, no input
+// canonicalisation as fmaxf needs.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float wave_max_pair(float v) {
   // lanes l and l ^ 32 hold the two halves of one query's row
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+  return vmax(v, __shfl_xor(v, 32, 64));
 }
+
+// Marks a rarely taken uniform branch so the compiler keeps it a branch
+// instead of executing its body on every pass with selects.
+#define FA_KEEP_BRANCH() __asm__ volatile("" ::: "memory")
+
+// Wait for every outstanding memory operation of this wave.  Used once before
+// a tile loop so that the compiler's wait tracking does not carry loads issued
+// before the loop (operands kept in registers) into every iteration, where it
+// would also wait for the prefetch of the next tile.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Wave index as a wave-uniform (scalar) value, so that branches on it stay
+// scalar branches instead of being if-converted.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -203,12 +203,15 @@ hipError_t launch_f32_fwd(const F32Params& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_f32_bwd(const F32Params& p, hipStream_t s) {
+hipError_t launch_f32_dq(const F32Params& p, hipStream_t s) {
   dim3 grid(p.nheads, (p.N + kF32Threads - 1) / kF32Threads), block(kF32Threads);
   if (p.d == 64) hipLaunchKernelGGL(f32_dq_kernel<64>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(f32_dq_kernel<128>, grid, block, 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_dkdv(const F32Params& p, hipStream_t s) {
+  dim3 grid(p.nheads, (p.N + kF32Threads - 1) / kF32Threads), block(kF32Threads);
   if (p.d == 64) hipLaunchKernelGGL(f32_dkdv_kernel<64>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(f32_dkdv_kernel<128>, grid, block, 0, s, p);
   return hipGetLastError();

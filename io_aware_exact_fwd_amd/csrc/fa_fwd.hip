@@ -1,25 +1,33 @@
 // fa_fwd.hip -- forward pass of tiled exact attention on gfx950 matrix cores.
 //
-// One workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32
-// rows.  The workgroup walks the visible key tiles (64 keys each) in order;
+// One workgroup = NW waves; each wave owns QB blocks of 32 query rows of one
+// (b, h).  The workgroup walks the visible key tiles (64 keys each) in order;
 // per tile it stages K and V in LDS (double-buffered, the next tile's global
 // loads in flight while the current one is used) and every wave
-//   1. computes its score block S^T = K_j Q_i^T (64 keys x 32 queries) on the
-//      matrix cores, fp32 accumulate -- the block never leaves registers;
+//   1. computes its score blocks S^T = K_j Q_i^T (64 keys x 32 queries each)
+//      on the matrix cores, fp32 accumulate -- they never leave registers;
+//      every K fragment read from LDS feeds QB products;
 //   2. applies the causal / sequence-end mask on the tiles that need it;
-//   3. runs the online-softmax update: new row maximum, rescale factor
-//      alpha = 2^(m_old - m_new), P = 2^(S * scale * log2 e - m_new), running
-//      row sum l <- alpha * l + rowsum(P), O <- alpha * O;
+//   3. runs the online-softmax update in the base-2 domain: row maximum of
+//      the tile, P = 2^(S * scale * log2 e - m), running row sum l += rowsum P;
 //   4. accumulates O^T += V_j^T P^T on the matrix cores (P rounded to the
-//      input type, V read from LDS with transpose reads).
+//      input type, V read from LDS with transpose reads, each V fragment
+//      feeding QB products).
 // After the last tile, O is divided by l once and LSE = (m + log2 l) * ln 2 is
 // written (natural log).
 //
 // This is the query-outer order with the division deferred to the end, as in
 // "02 -- FlashAttention como una optimizacion de roofline" (lynx-cortex),
-// section "El algoritmo Flash (forward)", and the recurrence of the tonho.wtf
-// digest, section "como funciona"; the running maximum and sum are kept in the
-// base-2 exponential domain (a change of base, same result).
+// section "El algoritmo Flash (forward)", and the running max / running sum
+// recurrence of the tonho.wtf digest, section "como funciona".
+//
+// Reference maximum.  The recurrence rescales the accumulated O and l by
+// 2^(m_old - m_new) whenever the row maximum grows.  Any reference value gives
+// the same O / l and the same m + log2 l, as long as the exponentials stay in
+// range; so the reference is only moved when the tile maximum exceeds it by
+// more than kRescaleTau (P <= 2^kRescaleTau = 256, exact in fp16/bf16 range).
+// With scores of moderate spread this skips nearly every rescale.  The move is
+// decided per wave (any row over the threshold moves all rows of the wave).
 //
 // Register layout: computing S^T (keys as rows) rather than S puts one query
 // per lane (lanes l and l+32 share it), so row reductions are in-lane plus one
@@ -31,7 +39,24 @@
 
 namespace fa {
 
-template <int D>
+constexpr float kRescaleTau = 8.0f;
+
+// Tuning knobs of the dense head-dim-64 forward: waves per workgroup, 32-row
+// query blocks per wave, waves per SIMD the register budget targets.  Measured
+// on MI355X: 32 rows per wave at 4 waves per SIMD (127 VGPRs) beats 64 rows per
+// wave at 2 waves per SIMD; latency hiding across waves matters more there than
+// reusing each LDS fragment twice.
+#ifndef FA_FWD64_NW
+#define FA_FWD64_NW 4
+#endif
+#ifndef FA_FWD64_QB
+#define FA_FWD64_QB 1
+#endif
+#ifndef FA_FWD64_WPE
+#define FA_FWD64_WPE 4
+#endif
+
+template <int D, int NW>
 struct FwdGeom {
   static constexpr int KT = kKeyTile;           // keys per tile
   static constexpr int KP = D * 2 + 16;         // K tile pitch (bytes)
@@ -39,22 +64,27 @@ struct FwdGeom {
   static constexpr int KBYTES = KT * KP;
   static constexpr int VBYTES = KT * VP;
   static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int THREADS = NW * 64;
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int CPT = KT * CPR / kThreads;  // chunks per thread per tensor
+  static constexpr int CPT = KT * CPR / THREADS;  // chunks per thread per tensor
   static constexpr int NDB = D / 32;            // 32-wide blocks of the head dim
   static constexpr int NKS = D / 16;            // k-steps of the QK^T product
+  static_assert(KT * CPR % THREADS == 0, "tile must split evenly over threads");
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <typename T, int D, bool CAUSAL, bool MASKED, int NW, int QB, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(FwdParams p) {
-  using G = FwdGeom<D>;
+  using G = FwdGeom<D, NW>;
   using V8 = typename Vec8<T>::type;
+  constexpr int BR = NW * QB * 32;  // query rows per workgroup
+  constexpr int WQ = QB * 32;       // query rows per wave
   __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int g = lane >> 5;        // which half of the wave
   const int l32 = lane & 31;
 
@@ -63,10 +93,9 @@ void fwd_kernel(FwdParams p) {
   int qt = logical % p.nqt;
   if (CAUSAL) qt = p.nqt - 1 - qt;  // longest rows first
   const int N = p.N;
-  const int q0 = qt * kFwdRows;
-  const int qw0 = q0 + wave * 32;   // this wave's first query
-  const int q = qw0 + l32;          // this lane's query
-  const int q_hi = min(q0 + kFwdRows, N) - 1;
+  const int q0 = qt * BR;
+  const int qw0 = q0 + wave * WQ;   // this wave's first query
+  const int q_hi = min(q0 + BR, N) - 1;
 
   const size_t head_off = (size_t)head * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * sizeof(T);
@@ -77,23 +106,32 @@ void fwd_kernel(FwdParams p) {
   KeyTileList<G::KT, CAUSAL, MASKED> tiles;
   tiles.init(p.m, N, q0, q_hi);
 
-  // Q fragments: B operand of S^T = K Q^T (k = head dim), rows >= N read as 0.
-  V8 qf[G::NKS];
+  // Q fragments: B operands of S^T = K Q^T (k = head dim), rows >= N read as 0.
+  V8 qf[QB][G::NKS];
 #pragma unroll
-  for (int t = 0; t < G::NKS; ++t)
-    qf[t] = __builtin_bit_cast(V8, buf_load16(bq, (uint32_t)(q * D + t * 16 + g * 8) * sizeof(T)));
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int t = 0; t < G::NKS; ++t)
+      qf[qb][t] = __builtin_bit_cast(
+          V8, buf_load16(bq, (uint32_t)((qw0 + qb * 32 + l32) * D + t * 16 + g * 8) * sizeof(T)));
 
-  f32x16 o[G::NDB];
+  f32x16 o[QB][G::NDB];
+  float m_ref[QB], ref[QB], l_run[QB];
 #pragma unroll
-  for (int i = 0; i < G::NDB; ++i) o[i] = f32x16{0};
-  float m_run = kNegInf, l_run = 0.f;
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int i = 0; i < G::NDB; ++i) o[qb][i] = f32x16{0};
+    m_ref[qb] = kNegInf;
+    ref[qb] = 0.f;
+    l_run[qb] = 0.f;
+  }
 
   u32x4 pk[G::CPT], pv[G::CPT];
   auto gload = [&](int it) {
     const int k0 = tiles.key0(it);
 #pragma unroll
     for (int i = 0; i < G::CPT; ++i) {
-      const int ci = tid + i * kThreads;
+      const int ci = tid + i * G::THREADS;
       const int row = ci / G::CPR, cc = ci % G::CPR;
       const uint32_t off = (uint32_t)((k0 + row) * D * sizeof(T) + cc * 16);
       pk[i] = buf_load16(bk, off);
@@ -105,7 +143,7 @@ void fwd_kernel(FwdParams p) {
     char* vs = ks + G::KBYTES;
 #pragma unroll
     for (int i = 0; i < G::CPT; ++i) {
-      const int ci = tid + i * kThreads;
+      const int ci = tid + i * G::THREADS;
       const int row = ci / G::CPR, cc = ci % G::CPR;
       *(u32x4*)(ks + row * G::KP + cc * 16) = pk[i];
       *(u32x4*)(vs + row * G::VP + cc * 16) = pv[i];
@@ -117,7 +155,11 @@ void fwd_kernel(FwdParams p) {
     gload(0);
     lstore(0);
   }
+  wait_all_memory();
   __syncthreads();
+
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
@@ -127,71 +169,96 @@ void fwd_kernel(FwdParams p) {
     const int k0 = tiles.key0(it);
     const char* ks = smem + cur * G::STAGE;
     const char* vs = ks + G::KBYTES;
-    const bool active = !CAUSAL || k0 <= qw0 + 31;
+    const bool active = !CAUSAL || k0 <= qw0 + WQ - 1;
     if (active) {
-      // 1. S^T = K Q^T, two 32-key blocks
-      f32x16 s[2];
+      // 1. S^T = K Q^T for each (key block kb, query block qb)
+      f32x16 s[QB][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{0};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{0};
 #pragma unroll
         for (int t = 0; t < G::NKS; ++t) {
           const V8 a = lds_read8<T>(ks + (kb * 32 + l32) * G::KP + t * 32 + g * 16);
-          s[kb] = mfma32(a, qf[t], s[kb]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][t], s[qb][kb]);
         }
       }
-      // 2. mask keys in the future of the query, and keys past the end
+      // 2. mask keys in the future of the query, and keys past the end.
+      // Key of register r is k0 + g*4 + C(kb, r), C = kb*32 + (r/4)*8 + r%4;
+      // it is hidden iff C > bound with one per-lane bound for both rules.
       const bool need_mask = (CAUSAL && k0 + G::KT - 1 > qw0) || (k0 + G::KT > N);
       if (need_mask) {
+        FA_KEEP_BRANCH();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int qb = 0; qb < QB; ++qb) {
+          int bound = N - 1 - k0 - g * 4;
+          if (CAUSAL) bound = min(bound, qw0 + qb * 32 + l32 - k0 - g * 4);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-            const bool hide = (CAUSAL && key > q) || key >= N;
-            if (hide) s[kb][r] = kNegInf;
-          }
-      }
-      // 3. online softmax (base-2 domain)
-      float mx = s[0][0];
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = wave_max_pair(mx);
-      const float m_new = fmaxf(m_run, mx * p.c);
-      const float ref = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - ref);
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(__builtin_fmaf(s[kb][r], p.c, -ref));
-          s[kb][r] = e;
-          lsum += e;
+            for (int r = 0; r < 16; ++r)
+              if (kb * 32 + (r >> 2) * 8 + (r & 3) > bound) s[qb][kb][r] = kNegInf;
         }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < G::NDB; ++i) o[i] *= alpha;
-      // 4. O^T += V^T P^T; k-step t covers keys 16t .. 16t+15
-      V8 bp[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int kb = t >> 1, r0 = (t & 1) * 8;
-        bp[t] = pack8<T>(s[kb][r0 + 0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3],
-                         s[kb][r0 + 4], s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
       }
-      const int tr_row = (lane & 15) >> 2;
-      const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+      // 3. tile row maxima; move the reference only past the threshold
+      float mxs[QB];
+      bool move = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = vmax(s[qb][0][0], s[qb][1][0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = vmax(mx, vmax(s[qb][0][r], s[qb][1][r]));
+        mxs[qb] = wave_max_pair(mx) * p.c;
+        move |= mxs[qb] > m_ref[qb] + kRescaleTau;
+      }
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        FA_KEEP_BRANCH();
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float m_new = vmax(m_ref[qb], mxs[qb]);
+          const float r_new = (m_new == kNegInf) ? 0.f : m_new;
+          const float alpha = fast_exp2(m_ref[qb] - r_new);  // 0 while m_ref = -inf
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int i = 0; i < G::NDB; ++i) o[qb][i] *= alpha;
+          m_ref[qb] = m_new;
+          ref[qb] = r_new;
+        }
+      }
+      // P = 2^(S c - ref), packed to the input type; row sums
+      V8 bp[QB][4];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int kb = t >> 1, r0 = (t & 1) * 8;
+          u32x4 w;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const float e0 = fast_exp2(__builtin_fmaf(s[qb][kb][r0 + 2 * h], p.c, -ref[qb]));
+            const float e1 = fast_exp2(__builtin_fmaf(s[qb][kb][r0 + 2 * h + 1], p.c, -ref[qb]));
+            w[h] = pack2<T>(e0, e1);
+            if constexpr (sizeof(T) == 2 && __is_same(T, _Float16)) {
+              // fp16: sum the rounded values, the weights P V actually uses
+              l_run[qb] = add_pair<T>(w[h], l_run[qb]);
+            } else {
+              // bf16 rounding is too coarse for the LSE: sum in fp32
+              l_run[qb] += e0 + e1;
+            }
+          }
+          bp[qb][t] = __builtin_bit_cast(V8, w);
+        }
+      }
+      // 4. O^T += V^T P^T; k-step t covers keys 16t .. 16t+15
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const char* p0 = vs + (t * 16 + g * 4 + tr_row) * G::VP + (db * 32 + tr_col) * 2;
           const V8 a = lds_tr_operand<T>(p0, p0 + 8 * G::VP);
-          o[db] = mfma32(a, bp[t], o[db]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(a, bp[qb][t], o[qb][db]);
         }
       }
     }
@@ -200,42 +267,60 @@ void fwd_kernel(FwdParams p) {
   }
 
   // epilogue: deferred normalisation, natural-log LSE
-  const float lt = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (q < N) {
-    T* orow = (T*)p.o + head_off + (size_t)q * D;
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = qw0 + qb * 32 + l32;
+    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (q < N) {
+      T* orow = (T*)p.o + head_off + (size_t)q * D;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        u32x2 w;
-        w[0] = pack2<T>(o[db][rr * 4 + 0] * inv, o[db][rr * 4 + 1] * inv);
-        w[1] = pack2<T>(o[db][rr * 4 + 2] * inv, o[db][rr * 4 + 3] * inv);
-        *(u32x2*)(orow + db * 32 + rr * 8 + g * 4) = w;
-      }
-    if (g == 0)
-      p.lse[(size_t)head * N + q] = lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : kNegInf;
+      for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          u32x2 w;
+          w[0] = pack2<T>(o[qb][db][rr * 4 + 0] * inv, o[qb][db][rr * 4 + 1] * inv);
+          w[1] = pack2<T>(o[qb][db][rr * 4 + 2] * inv, o[qb][db][rr * 4 + 3] * inv);
+          *(u32x2*)(orow + db * 32 + rr * 8 + g * 4) = w;
+        }
+      if (g == 0)
+        p.lse[(size_t)head * N + q] = lt > 0.f ? (m_ref[qb] + fast_log2(lt)) * kLn2 : kNegInf;
+    }
   }
 }
 
-template <typename T, int D>
-static hipError_t launch_fwd_t(const FwdParams& p, bool causal, bool masked, hipStream_t s) {
-  dim3 grid(p.nheads * p.nqt), block(kThreads);
-  if (causal && masked) hipLaunchKernelGGL((fwd_kernel<T, D, true, true>), grid, block, 0, s, p);
-  else if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, true, false>), grid, block, 0, s, p);
-  else if (masked) hipLaunchKernelGGL((fwd_kernel<T, D, false, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((fwd_kernel<T, D, false, false>), grid, block, 0, s, p);
+template <typename T, int D, bool MASKED, int NW, int QB, int WPE>
+static hipError_t launch_fwd_t(FwdParams p, bool causal, hipStream_t s) {
+  constexpr int BR = NW * QB * 32;
+  p.nqt = (p.N + BR - 1) / BR;
+  dim3 grid(p.nheads * p.nqt), block(NW * 64);
+  if (causal)
+    hipLaunchKernelGGL((fwd_kernel<T, D, true, MASKED, NW, QB, WPE>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, false, MASKED, NW, QB, WPE>), grid, block, 0, s, p);
   return hipGetLastError();
+}
+
+// Workgroup shapes.  A block mask needs the workgroup's rows inside one
+// 128-row mask block.  Head dim 128 keeps 32 rows per wave at 2 waves per SIMD
+// (register budget: the O accumulator alone is 64 registers).
+template <typename T>
+static hipError_t launch_fwd_dtype(const FwdParams& p, int d, bool causal, bool masked,
+                                   hipStream_t s) {
+  constexpr int BR64 = FA_FWD64_NW * FA_FWD64_QB * 32;
+  if (d == 64) {
+    if (masked && BR64 != 128) return launch_fwd_t<T, 64, true, 4, 1, 4>(p, causal, s);
+    if (masked) return launch_fwd_t<T, 64, true, FA_FWD64_NW, FA_FWD64_QB, FA_FWD64_WPE>(p, causal, s);
+    return launch_fwd_t<T, 64, false, FA_FWD64_NW, FA_FWD64_QB, FA_FWD64_WPE>(p, causal, s);
+  }
+  if (masked) return launch_fwd_t<T, 128, true, 4, 1, 2>(p, causal, s);
+  return launch_fwd_t<T, 128, false, 4, 1, 2>(p, causal, s);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, bool causal, bool masked,
                       hipStream_t s) {
-  if (dtype == 1) {
-    return d == 64 ? launch_fwd_t<_Float16, 64>(p, causal, masked, s)
-                   : launch_fwd_t<_Float16, 128>(p, causal, masked, s);
-  }
-  return d == 64 ? launch_fwd_t<__bf16, 64>(p, causal, masked, s)
-                 : launch_fwd_t<__bf16, 128>(p, causal, masked, s);
+  if (dtype == 1) return launch_fwd_dtype<_Float16>(p, d, causal, masked, s);
+  return launch_fwd_dtype<__bf16>(p, d, causal, masked, s);
 }
 
 }  // namespace fa

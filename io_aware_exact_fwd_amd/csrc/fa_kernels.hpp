@@ -85,7 +85,8 @@ hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int d, bool causal, bool
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int d, bool causal, bool masked,
                            hipStream_t s);
 hipError_t launch_f32_fwd(const F32Params& p, hipStream_t s);
-hipError_t launch_f32_bwd(const F32Params& p, hipStream_t s);
+hipError_t launch_f32_dq(const F32Params& p, hipStream_t s);
+hipError_t launch_f32_dkdv(const F32Params& p, hipStream_t s);
 hipError_t launch_mask_compile(const uint8_t* mask, int nb, int32_t* row_ptr, int32_t* col_idx,
                                int32_t* col_ptr, int32_t* row_idx, hipStream_t s);
 

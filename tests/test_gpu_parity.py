@@ -164,3 +164,21 @@ def test_autograd_wrapper_matches_entry_points():
     assert torch.equal(o, o2)
     for a, b in zip((qr.grad, kr.grad, vr.grad), g):
         assert torch.equal(a, b)
+
+
+def test_backward_stages_equal_fused_entry_point():
+    from io_aware_exact_fwd_amd import bwd_workspace, fa_bwd_dkdv, fa_bwd_dq
+
+    dev = torch.device("cuda:0")
+    say("[case] backward stages")
+    bm = torch.as_tensor(_mask_with_holes(8), device=dev)
+    q, k, v, do = (t.to(dev) for t in make_inputs(1, 2, 1024, 64, "f16"))
+    o, lse = fa_fwd(q, k, v, causal=True, scale=0.125, block_mask=bm, mask_block=128)
+    g = fa_bwd(q, k, v, o, do, lse, causal=True, scale=0.125, block_mask=bm, mask_block=128)
+    p, ws, ws_n, _ = bwd_workspace(q, True, 0.125, bm, 128)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd_dq(p, q, k, v, o, do, lse, dq, ws, ws_n)
+    fa_bwd_dkdv(p, q, k, v, do, lse, dk, dv, ws, ws_n)
+    torch.cuda.synchronize()
+    for a, b in zip(g, (dq, dk, dv)):
+        assert torch.equal(a, b)
