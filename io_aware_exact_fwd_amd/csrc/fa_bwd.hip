@@ -6,7 +6,8 @@
 // "como funciona", tonho.wtf digest).  With dP = dO V^T and
 // D_i = dO_i . O_i (the d-length dot that replaces the N-length reduction
 // sum_j P_ij dP_ij, "como funciona", tonho.wtf digest):
-//     dS = P o (dP - D),   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+//     dS = P o (dP - D),   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO
+// (the scale is applied once to the finished dQ and dK).
 //
 // Two kernels, so that every output is reduced inside one workgroup and
 // written once (no atomics, no float32 dQ accumulator in memory, bitwise
@@ -24,6 +25,18 @@
 #include "fa_tiles.hpp"
 
 namespace fa {
+
+// Tuning knobs: waves per SIMD of the dQ kernel, query rows per step and waves
+// per SIMD of the head-dim-64 dK/dV kernel.
+#ifndef FA_DQ_WPE
+#define FA_DQ_WPE 2
+#endif
+#ifndef FA_DKDV_QT
+#define FA_DKDV_QT 64
+#endif
+#ifndef FA_DKDV64_WPE
+#define FA_DKDV64_WPE 2
+#endif
 
 // ============================================================================
 // dQ kernel
@@ -43,7 +56,8 @@ struct DqGeom {
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(FA_DQ_WPE, FA_DQ_WPE)))
 void bwd_dq_kernel(BwdParams p) {
   using G = DqGeom<D>;
   using V8 = typename Vec8<T>::type;
@@ -176,7 +190,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pr = fast_exp2(__builtin_fmaf(s[kb][r], p.c, -lse2));
-          s[kb][r] = pr * (dp[kb][r] - dq_d) * p.scale;  // dS^T (scaled)
+          s[kb][r] = pr * (dp[kb][r] - dq_d);  // dS^T (scale applied to dQ at the end)
         }
       // dQ^T += K^T dS^T : A = K^T via transpose reads of the K tile
       V8 bs[4];
@@ -206,8 +220,8 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         u32x2 w;
-        w[0] = pack2<T>(acc[db][rr * 4 + 0], acc[db][rr * 4 + 1]);
-        w[1] = pack2<T>(acc[db][rr * 4 + 2], acc[db][rr * 4 + 3]);
+        w[0] = pack2<T>(acc[db][rr * 4 + 0] * p.scale, acc[db][rr * 4 + 1] * p.scale);
+        w[1] = pack2<T>(acc[db][rr * 4 + 2] * p.scale, acc[db][rr * 4 + 3] * p.scale);
         *(u32x2*)(row + db * 32 + rr * 8 + g * 4) = w;
       }
   }
@@ -218,7 +232,7 @@ void bwd_dq_kernel(BwdParams p) {
 // ============================================================================
 template <int D>
 struct DkvGeom {
-  static constexpr int QT = 64;             // queries per step
+  static constexpr int QT = FA_DKDV_QT;     // queries per step
   static constexpr int P = D * 2 + 32;      // Q / dO tile pitch: rows and transpose
   static constexpr int TBYTES = QT * P;
   static constexpr int STAGE = 2 * TBYTES + 2 * QT * 4;  // Q, dO, lse2, D
@@ -227,7 +241,7 @@ struct DkvGeom {
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
   static constexpr int NQB = QT / 32;       // 32-query blocks per step
-  static constexpr int WPE = D == 64 ? 2 : 1;  // waves per SIMD the registers allow
+  static constexpr int WPE = D == 64 ? FA_DKDV64_WPE : 1;  // waves per SIMD the registers allow
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED>
@@ -378,7 +392,7 @@ void bwd_dkdv_kernel(BwdParams p) {
             const int r = rr * 4 + e;
             const float pr = fast_exp2(__builtin_fmaf(s[qb][r], p.c, -l4[e]));
             s[qb][r] = pr;                                   // P
-            dp[qb][r] = pr * (dp[qb][r] - d4[e]) * p.scale;  // dS (scaled)
+            dp[qb][r] = pr * (dp[qb][r] - d4[e]);  // dS (scale applied to dK at the end)
           }
         }
       // dV += P^T dO,  dK += dS^T Q ; k-step t covers queries 16t .. 16t+15
@@ -411,7 +425,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       const int kr = kw0 + (r >> 2) * 8 + g * 4 + (r & 3);
       if (kr < N) {
         const size_t idx = head_off + (size_t)kr * D + db * 32 + l32;
-        ((T*)p.dk)[idx] = (T)dka[db][r];
+        ((T*)p.dk)[idx] = (T)(dka[db][r] * p.scale);
         ((T*)p.dv)[idx] = (T)dva[db][r];
       }
     }

@@ -158,9 +158,6 @@ void fwd_kernel(FwdParams p) {
   wait_all_memory();
   __syncthreads();
 
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
     const bool more = it + 1 < ntiles;
@@ -201,64 +198,71 @@ void fwd_kernel(FwdParams p) {
               if (kb * 32 + (r >> 2) * 8 + (r & 3) > bound) s[qb][kb][r] = kNegInf;
         }
       }
-      // 3. tile row maxima; move the reference only past the threshold
-      float mxs[QB];
-      bool move = false;
+      // 3-4. per 32-key half kb: row maxima of the half, reference move if
+      // needed, P = 2^(S c - ref) packed to the input type, row sums, then
+      // O^T += V^T P^T for its two key steps.  The exponentials of half 0
+      // overlap the score products of half 1 still in flight, and those of
+      // half 1 the P V products of half 0.  The reference may move between
+      // the halves; O and l are rescaled with it, so the result is the same.
+      const int tr_row = (lane & 15) >> 2;
+      const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = vmax(s[qb][0][0], s[qb][1][0]);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = vmax(mx, vmax(s[qb][0][r], s[qb][1][r]));
-        mxs[qb] = wave_max_pair(mx) * p.c;
-        move |= mxs[qb] > m_ref[qb] + kRescaleTau;
-      }
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        FA_KEEP_BRANCH();
+      for (int kb = 0; kb < 2; ++kb) {
+        float mxs[QB];
+        bool move = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const float m_new = vmax(m_ref[qb], mxs[qb]);
-          const float r_new = (m_new == kNegInf) ? 0.f : m_new;
-          const float alpha = fast_exp2(m_ref[qb] - r_new);  // 0 while m_ref = -inf
-          l_run[qb] *= alpha;
+          float m4[4];
 #pragma unroll
-          for (int i = 0; i < G::NDB; ++i) o[qb][i] *= alpha;
-          m_ref[qb] = m_new;
-          ref[qb] = r_new;
+          for (int i = 0; i < 4; ++i) m4[i] = vmax(s[qb][kb][i], s[qb][kb][i + 4]);
+#pragma unroll
+          for (int r = 8; r < 16; ++r) m4[r & 3] = vmax(m4[r & 3], s[qb][kb][r]);
+          mxs[qb] = vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3])) * p.c;
+          move |= mxs[qb] > m_ref[qb] + kRescaleTau;
         }
-      }
-      // P = 2^(S c - ref), packed to the input type; row sums
-      V8 bp[QB][4];
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          FA_KEEP_BRANCH();
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+          for (int qb = 0; qb < QB; ++qb) {
+            const float m_new = vmax(m_ref[qb], vmax(mxs[qb], __shfl_xor(mxs[qb], 32, 64)));
+            const float r_new = (m_new == kNegInf) ? 0.f : m_new;
+            const float alpha = fast_exp2(m_ref[qb] - r_new);  // 0 while m_ref = -inf
+            l_run[qb] *= alpha;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int kb = t >> 1, r0 = (t & 1) * 8;
-          u32x4 w;
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const float e0 = fast_exp2(__builtin_fmaf(s[qb][kb][r0 + 2 * h], p.c, -ref[qb]));
-            const float e1 = fast_exp2(__builtin_fmaf(s[qb][kb][r0 + 2 * h + 1], p.c, -ref[qb]));
-            w[h] = pack2<T>(e0, e1);
-            if constexpr (sizeof(T) == 2 && __is_same(T, _Float16)) {
-              // fp16: sum the rounded values, the weights P V actually uses
-              l_run[qb] = add_pair<T>(w[h], l_run[qb]);
-            } else {
-              // bf16 rounding is too coarse for the LSE: sum in fp32
-              l_run[qb] += e0 + e1;
-            }
+            for (int i = 0; i < G::NDB; ++i) o[qb][i] *= alpha;
+            m_ref[qb] = m_new;
+            ref[qb] = r_new;
           }
-          bp[qb][t] = __builtin_bit_cast(V8, w);
         }
-      }
-      // 4. O^T += V^T P^T; k-step t covers keys 16t .. 16t+15
 #pragma unroll
-      for (int db = 0; db < G::NDB; ++db) {
+        for (int th = 0; th < 2; ++th) {
+          const int t = kb * 2 + th, r0 = th * 8;
+          V8 bp[QB];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const char* p0 = vs + (t * 16 + g * 4 + tr_row) * G::VP + (db * 32 + tr_col) * 2;
-          const V8 a = lds_tr_operand<T>(p0, p0 + 8 * G::VP);
+          for (int qb = 0; qb < QB; ++qb) {
+            u32x4 w;
+            float lp = 0.f;
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(a, bp[qb][t], o[qb][db]);
+            for (int h = 0; h < 4; ++h) {
+              const float e0 = fast_exp2(__builtin_fmaf(s[qb][kb][r0 + 2 * h], p.c, -ref[qb]));
+              const float e1 = fast_exp2(__builtin_fmaf(s[qb][kb][r0 + 2 * h + 1], p.c, -ref[qb]));
+              w[h] = pack2<T>(e0, e1);
+              if constexpr (__is_same(T, _Float16)) {
+                lp = add_pair<T>(w[h], lp);  // fp16: the rounded weights P V uses
+              } else {
+                lp += e0 + e1;  // bf16 rounding is too coarse for the LSE: fp32 sum
+              }
+            }
+            l_run[qb] += lp;
+            bp[qb] = __builtin_bit_cast(V8, w);
+          }
+#pragma unroll
+          for (int db = 0; db < G::NDB; ++db) {
+            const char* p0 = vs + (t * 16 + g * 4 + tr_row) * G::VP + (db * 32 + tr_col) * 2;
+            const V8 a = lds_tr_operand<T>(p0, p0 + 8 * G::VP);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(a, bp[qb], o[qb][db]);
+          }
         }
       }
     }
