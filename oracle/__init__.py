@@ -17,6 +17,11 @@ online
     The block-by-block online-softmax recurrence, in both loop orders the
     pages print.  Used only to check ``attention`` against an independent
     formulation of the method.
+philox
+    Philox4x32-10 from its published definition (Salmon et al., SC 2011)
+    and the dropout keep-mask built from it.  The attention dropout is
+    defined by this mask; the HIP library implements the same published
+    generator separately.
 
 Sources (cited by page title and section):
   [tonho] "FlashAttention: Fast and Memory-Efficient Exact Attention with
@@ -38,7 +43,8 @@ Sources (cited by page title and section):
           Flash 1 vs Flash 2", "Problemas de practica".
 
 Parity status: every function is pinned by CPU tests (closed forms,
-invariants, finite differences, library routines, the tiled recurrence);
+invariants, finite differences, library routines, the tiled recurrence,
+the generator's published known-answer vectors, binomial bounds);
 see tests/test_oracle_*.py.  No function here is "parity unpinned".
 """
 
@@ -48,4 +54,5 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_probs,
 )
+from .philox import dropout_keep, philox4x32_10  # noqa: F401
 from .online import tiled_forward_kv_outer, tiled_forward_q_outer  # noqa: F401

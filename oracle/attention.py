@@ -36,6 +36,24 @@ in the tests):
 Visibility of key j to query i (mask_block = side of a mask block):
   [not causal or j <= i] and [block_mask is None or
                               block_mask[i // mask_block, j // mask_block] != 0]
+  and [window == 0 or |i - j| < window]
+The window term is the sliding-window rule of [lynx] "Problemas de
+practica" (a window of W keys around each query).  The page poses it without
+fixing the boundary; the reading taken is |i - j| < W, which together with
+the causal rule keeps the W most recent keys i-W+1 .. i.
+
+Grouped heads (GQA/MQA, [ldl] sections 4-6): K and V may carry H_kv heads
+with H_kv dividing the H query heads; query head h reads K/V head
+h // (H / H_kv).  dK and dV of a K/V head are the sums of the contributions of
+the H / H_kv query heads that read it.
+
+Dropout ([tonho] "como funciona"; [agi] algorithm paragraph: the mask is
+applied inside the fused kernel and regenerated in the backward pass from
+the saved generator state): with keep mask Z01 from ``oracle.philox`` and
+Z = Z01 / (1 - p'),
+  O = (P o Z) V,  LSE unchanged (it is the normaliser of P, not of P o Z),
+  dV = (P o Z)^T dO,  dP = Z o (dO V^T),  D_i = sum_j P_ij dP_ij = dO_i . O_i,
+  dS = P o (dP - D).
 
 Fully masked rows (possible only with a general block mask): O_i = 0,
 LSE_i = -inf, and the row contributes nothing to any gradient.
@@ -53,6 +71,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .philox import dropout_keep
+
 __all__ = [
     "visibility",
     "attention_probs",
@@ -63,24 +83,28 @@ __all__ = [
 _CHUNK_ELEMS = 1 << 22  # rows * candidate columns per chunk (32 MiB of f64)
 
 
-def visibility(rows, cols, causal=False, block_mask=None, mask_block=128):
+def visibility(rows, cols, causal=False, block_mask=None, mask_block=128, window=0):
     """Boolean matrix vis[r, c]: is key ``cols[c]`` visible to query ``rows[r]``."""
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
     vis = np.ones((rows.size, cols.size), dtype=bool)
     if causal:
         vis &= cols[None, :] <= rows[:, None]
+    if window:
+        vis &= np.abs(cols[None, :] - rows[:, None]) < window
     if block_mask is not None:
         bm = np.asarray(block_mask) != 0
         vis &= bm[(rows // mask_block)[:, None], (cols // mask_block)[None, :]]
     return vis
 
 
-def _candidate_columns(r0, r1, n, causal, block_mask, mask_block):
+def _candidate_columns(r0, r1, n, causal, block_mask, mask_block, window=0):
     """Key columns that may be visible to some query row in [r0, r1)."""
     cols = np.arange(n, dtype=np.int64)
     if causal:
         cols = cols[cols < r1]
+    if window:
+        cols = cols[(cols > r0 - window) & (cols < r1 - 1 + window)]
     if block_mask is not None:
         bm = np.asarray(block_mask) != 0
         qblocks = np.unique(np.arange(r0, r1) // mask_block)
@@ -118,57 +142,96 @@ def _softmax_rows(s):
     return lse, p
 
 
-def attention_probs(q, k, scale, causal=False, block_mask=None, mask_block=128):
+def attention_probs(q, k, scale, causal=False, block_mask=None, mask_block=128, window=0):
     """Dense P (N x N) and LSE (N) for ONE head; small shapes only."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     n = q.shape[0]
     s = scale * (q @ k.T)
-    vis = visibility(np.arange(n), np.arange(k.shape[0]), causal, block_mask, mask_block)
+    vis = visibility(np.arange(n), np.arange(k.shape[0]), causal, block_mask, mask_block,
+                     window)
     s = np.where(vis, s, -np.inf)
     lse, p = _softmax_rows(s)
     return p, lse
 
 
-def _forward_head(q, k, v, scale, causal, block_mask, mask_block, row_chunk):
+class _Spec:
+    """Mask and dropout settings shared by the per-head routines."""
+
+    def __init__(self, scale, causal, block_mask, mask_block, window, dropout_p, seed,
+                 offset, row_chunk):
+        if window < 0:
+            raise ValueError("window must be >= 0")
+        if not 0.0 <= dropout_p < 1.0:
+            raise ValueError("dropout_p must be in [0, 1)")
+        self.scale, self.causal = scale, causal
+        self.block_mask, self.mask_block = block_mask, mask_block
+        self.window, self.row_chunk = window, row_chunk
+        self.dropout_p, self.seed, self.offset = dropout_p, seed, offset
+
+    def chunks(self, n):
+        return _row_chunks(n, self.causal, self.block_mask, self.mask_block, self.row_chunk)
+
+    def columns(self, r0, r1, n):
+        return _candidate_columns(r0, r1, n, self.causal, self.block_mask, self.mask_block,
+                                  self.window)
+
+    def scores(self, q, k, rows, cols):
+        s = self.scale * (q[rows] @ k[cols].T)
+        vis = visibility(rows, cols, self.causal, self.block_mask, self.mask_block,
+                         self.window)
+        return np.where(vis, s, -np.inf)
+
+    def drop(self, rows, cols, head):
+        """Dropout multiplier Z for the (rows x cols) block, or None if p = 0."""
+        if self.dropout_p == 0.0:
+            return None
+        keep, mult = dropout_keep(rows, cols, head, self.seed, self.offset, self.dropout_p)
+        return keep * mult
+
+
+def _forward_head(q, k, v, spec, head):
     n, d = q.shape
     o = np.zeros((n, v.shape[1]), dtype=np.float64)
     lse = np.full(n, -np.inf, dtype=np.float64)
-    for r0, r1 in _row_chunks(n, causal, block_mask, mask_block, row_chunk):
-        cols = _candidate_columns(r0, r1, k.shape[0], causal, block_mask, mask_block)
+    for r0, r1 in spec.chunks(n):
+        cols = spec.columns(r0, r1, k.shape[0])
         rows = np.arange(r0, r1)
         if cols.size == 0:
             continue
-        s = scale * (q[r0:r1] @ k[cols].T)
-        s = np.where(visibility(rows, cols, causal, block_mask, mask_block), s, -np.inf)
-        lse_c, p = _softmax_rows(s)
+        lse_c, p = _softmax_rows(spec.scores(q, k, rows, cols))
+        z = spec.drop(rows, cols, head)
+        if z is not None:
+            p = p * z
         lse[r0:r1] = lse_c
         o[r0:r1] = p @ v[cols]
     return o, lse
 
 
-def _backward_head(q, k, v, do, scale, causal, block_mask, mask_block, row_chunk):
+def _backward_head(q, k, v, do, spec, head):
     n, d = q.shape
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     d_vec = np.zeros(n)
     d_dot = np.zeros(n)
-    for r0, r1 in _row_chunks(n, causal, block_mask, mask_block, row_chunk):
-        cols = _candidate_columns(r0, r1, k.shape[0], causal, block_mask, mask_block)
+    for r0, r1 in spec.chunks(n):
+        cols = spec.columns(r0, r1, k.shape[0])
         rows = np.arange(r0, r1)
         if cols.size == 0:
             continue
-        s = scale * (q[r0:r1] @ k[cols].T)
-        s = np.where(visibility(rows, cols, causal, block_mask, mask_block), s, -np.inf)
-        _, p = _softmax_rows(s)
-        o_c = p @ v[cols]
-        dv[cols] += p.T @ do[r0:r1]
+        _, p = _softmax_rows(spec.scores(q, k, rows, cols))
+        z = spec.drop(rows, cols, head)
+        pz = p if z is None else p * z
+        o_c = pz @ v[cols]
+        dv[cols] += pz.T @ do[r0:r1]
         dp = do[r0:r1] @ v[cols].T
+        if z is not None:
+            dp = dp * z
         dd = (p * dp).sum(axis=1)
         ds = p * (dp - dd[:, None])
-        dq[r0:r1] = scale * (ds @ k[cols])
-        dk[cols] += scale * (ds.T @ q[r0:r1])
+        dq[r0:r1] = spec.scale * (ds @ k[cols])
+        dk[cols] += spec.scale * (ds.T @ q[r0:r1])
         d_vec[r0:r1] = dd
         d_dot[r0:r1] = (do[r0:r1] * o_c).sum(axis=1)
     return dq, dk, dv, d_vec, d_dot
@@ -189,20 +252,34 @@ def _select(x, heads):
     return [tuple(bh) for bh in heads]
 
 
+def _group(q, k, v):
+    """Query heads per K/V head; checks the grouped-head shapes."""
+    hq, hkv = q.shape[1], k.shape[1]
+    if k.shape[:2] != v.shape[:2] or k.shape[0] != q.shape[0] or hkv == 0 or hq % hkv:
+        raise ValueError("K/V heads must divide the query heads")
+    return hq // hkv
+
+
 def attention_forward(q, k, v, scale, causal=False, block_mask=None, mask_block=128,
-                      heads=None, row_chunk=None):
+                      heads=None, row_chunk=None, window=0, dropout_p=0.0, seed=0,
+                      offset=0):
     """O (float64) and natural-log LSE (float64) of the definition above.
 
-    q, k, v: (B, H, N, d) or (N, d) arrays of any float dtype (upcast exactly).
-    heads: optional list of (b, h); then the results are stacked in that order
-           with shapes (len(heads), N, d) and (len(heads), N).
+    q: (B, H, N, d); k, v: (B, H_kv, N, d) with H_kv dividing H; or all (N, d).
+    Any float dtype (upcast exactly).
+    heads: optional list of (b, h) query heads; then the results are stacked
+           in that order with shapes (len(heads), N, d) and (len(heads), N).
+    window: 0 (none) or W > 0, keys with |i - j| >= W hidden.
+    dropout_p, seed, offset: dropout of P as in ``oracle.philox.dropout_keep``
+           with head index b * H + h.
     """
     q, k, v = _as_bhnd(q), _as_bhnd(k), _as_bhnd(v)
-    sel = _select(q, heads)
+    g = _group(q, k, v)
+    spec = _Spec(scale, causal, block_mask, mask_block, window, dropout_p, seed, offset,
+                 row_chunk)
     outs, lses = [], []
-    for b, h in sel:
-        o, lse = _forward_head(q[b, h], k[b, h], v[b, h], scale, causal, block_mask,
-                               mask_block, row_chunk)
+    for b, h in _select(q, heads):
+        o, lse = _forward_head(q[b, h], k[b, h // g], v[b, h // g], spec, b * q.shape[1] + h)
         outs.append(o)
         lses.append(lse)
     o = np.stack(outs)
@@ -214,20 +291,30 @@ def attention_forward(q, k, v, scale, causal=False, block_mask=None, mask_block=
 
 
 def attention_backward(q, k, v, do, scale, causal=False, block_mask=None, mask_block=128,
-                       heads=None, row_chunk=None, return_d=False):
+                       heads=None, row_chunk=None, return_d=False, window=0, dropout_p=0.0,
+                       seed=0, offset=0):
     """dQ, dK, dV (float64) of f = <O(Q, K, V), dO>; P is rebuilt from Q and K.
 
+    Shapes as in ``attention_forward``; dK, dV have the shape of K, V, each
+    K/V head summing the contributions of its group of query heads.  With
+    ``heads`` given, the results are stacked per selected query head and
+    dK, dV hold that head's own contribution (not summed over the group).
     With return_d=True also returns (D, D_dot): D_i = sum_j P_ij dP_ij and the
     d-length dot dO_i . O_i, which the pages state are equal.
     """
     q, k, v, do = _as_bhnd(q), _as_bhnd(k), _as_bhnd(v), _as_bhnd(do)
+    g = _group(q, k, v)
+    spec = _Spec(scale, causal, block_mask, mask_block, window, dropout_p, seed, offset,
+                 row_chunk)
     sel = _select(q, heads)
-    res = [_backward_head(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, block_mask,
-                          mask_block, row_chunk) for b, h in sel]
+    res = [_backward_head(q[b, h], k[b, h // g], v[b, h // g], do[b, h], spec,
+                          b * q.shape[1] + h) for b, h in sel]
     dq, dk, dv, dd, ddot = (np.stack([r[i] for r in res]) for i in range(5))
     if heads is None:
         shp = (q.shape[0], q.shape[1])
-        dq, dk, dv = (x.reshape(*shp, *x.shape[1:]) for x in (dq, dk, dv))
+        dq = dq.reshape(*shp, *dq.shape[1:])
+        dk, dv = (x.reshape(q.shape[0], k.shape[1], g, *x.shape[1:]).sum(axis=2)
+                  for x in (dk, dv))
         dd, ddot = (x.reshape(*shp, -1) for x in (dd, ddot))
     if return_d:
         return dq, dk, dv, dd, ddot

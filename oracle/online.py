@@ -43,14 +43,15 @@ def _ref(m):
     return np.where(np.isfinite(m), m, 0.0)
 
 
-def _block_scores(q, k, scale, i0, i1, j0, j1, causal, block_mask, mask_block):
+def _block_scores(q, k, scale, i0, i1, j0, j1, causal, block_mask, mask_block, window):
     s = scale * (q[i0:i1] @ k[j0:j1].T)
-    vis = visibility(np.arange(i0, i1), np.arange(j0, j1), causal, block_mask, mask_block)
+    vis = visibility(np.arange(i0, i1), np.arange(j0, j1), causal, block_mask, mask_block,
+                     window)
     return np.where(vis, s, -np.inf)
 
 
 def tiled_forward_kv_outer(q, k, v, scale, br, bc, causal=False, block_mask=None,
-                           mask_block=128):
+                           mask_block=128, window=0):
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     n = q.shape[0]
     nk = k.shape[0]
@@ -62,7 +63,8 @@ def tiled_forward_kv_outer(q, k, v, scale, br, bc, causal=False, block_mask=None
         vj = v[j0:j1]  # one block of values (keys are sliced in _block_scores)
         for i0 in range(0, n, br):
             i1 = min(n, i0 + br)
-            s = _block_scores(q, k, scale, i0, i1, j0, j1, causal, block_mask, mask_block)
+            s = _block_scores(q, k, scale, i0, i1, j0, j1, causal, block_mask, mask_block,
+                              window)
             m_blk = s.max(axis=1)
             p_blk = np.exp(s - _ref(m_blk)[:, None])
             l_blk = p_blk.sum(axis=1)
@@ -81,7 +83,7 @@ def tiled_forward_kv_outer(q, k, v, scale, br, bc, causal=False, block_mask=None
 
 
 def tiled_forward_q_outer(q, k, v, scale, br, bc, causal=False, block_mask=None,
-                          mask_block=128):
+                          mask_block=128, window=0):
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     n = q.shape[0]
     nk = k.shape[0]
@@ -94,7 +96,8 @@ def tiled_forward_q_outer(q, k, v, scale, br, bc, causal=False, block_mask=None,
         l = np.zeros(i1 - i0)
         for j0 in range(0, nk, bc):
             j1 = min(nk, j0 + bc)
-            s = _block_scores(q, k, scale, i0, i1, j0, j1, causal, block_mask, mask_block)
+            s = _block_scores(q, k, scale, i0, i1, j0, j1, causal, block_mask, mask_block,
+                              window)
             m_new = np.maximum(m, s.max(axis=1))
             alpha = np.exp(m - _ref(m_new))
             p = np.exp(s - _ref(m_new)[:, None])
