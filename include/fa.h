@@ -22,15 +22,38 @@
  * Visibility of key j to query i:
  *   [causal == 0 or j <= i]   (future keys excluded -- the causal-mask section
  *                              of the marketmaker.cc article)
+ *   and [window == 0 or |i - j| < window]
+ *                             (sliding window -- the practice problems of the
+ *                              lynx-cortex page; with causal, the window most
+ *                              recent keys i - window + 1 .. i)
  *   and [block_mask == NULL or block_mask[i / mask_block][j / mask_block] != 0]
  *                             (block-sparse attention -- block-sparse paragraph
  *                              of the agihunt.info summary of the paper).
  * A query row with no visible key gets O = 0, LSE = -inf and contributes
  * nothing to the gradients.
  *
- * Layouts.  Q, K, V, O, dO, dQ, dK, dV are contiguous row-major tensors of
- * shape (B, H, N, d) in the problem's dtype; element (b, h, n, c) sits at
- * ((b * H + h) * N + n) * d + c.  LSE is float32 (B, H, N).  block_mask is
+ * Grouped K/V heads (multi-query and grouped-query attention, sections 4-6 of
+ * "Atencao Eficiente em Escala", living-dl-book): K and V may have H_kv heads,
+ * H_kv dividing H; query head h reads K/V head h / (H / H_kv), and dK, dV of a
+ * K/V head are the sums over the H / H_kv query heads that read it.
+ *
+ * Dropout (applied inside the fused kernels and regenerated in the backward
+ * from the generator state instead of being stored -- "como funciona" in the
+ * tonho.wtf digest; the algorithm paragraph of the agihunt.info summary).
+ * With t = floor(256 * dropout_p): for query i, key j of query head
+ * b * H + h, one Philox4x32-10 evaluation (Salmon et al., "Parallel Random
+ * Numbers: As Easy as 1, 2, 3", SC 2011) with counter
+ * (j / 4, i / 4, b * H + h, offset) and key (seed mod 2^32, seed / 2^32)
+ * gives four 32-bit words; the weight P_ij is kept iff byte (j mod 4) of word
+ * (i mod 4) is >= t, and kept weights are multiplied by 256 / (256 - t):
+ *   O = (P o Z) V with LSE the normaliser of P (not of P o Z),
+ *   dP = Z o (dO V^T), D_i = dO_i . O_i, dS = P o (dP - D).
+ * The drop probability actually used is t / 256.
+ *
+ * Layouts.  Q, O, dO, dQ are contiguous row-major tensors of shape
+ * (B, H, N, d) in the problem's dtype; element (b, h, n, c) sits at
+ * ((b * H + h) * N + n) * d + c.  K, V, dK, dV are (B, H_kv, N, d) in the same
+ * way.  LSE is float32 (B, H, N).  block_mask is
  * uint8 [N / mask_block][N / mask_block], row = query block, shared by all
  * (b, h).  Every tensor pointer is a DEVICE pointer (hipMalloc'd or equivalent)
  * unless stated otherwise; device pointers must be 16-byte aligned.
@@ -64,8 +87,10 @@ enum fa_dtype {
 
 enum fa_status {
   FA_OK = 0,
-  FA_ERR_ARG = -1,          /* null pointer, non-positive size, non-finite scale,
-                               misaligned pointer                              */
+  FA_ERR_ARG = -1,          /* null pointer, non-positive size, scale not finite
+                               and positive, misaligned pointer, negative
+                               window, H_kv not dividing H, dropout_p outside
+                               [0, 1), reserved field not 0                   */
   FA_ERR_UNSUPPORTED = -2,  /* d not in {64, 128}; unknown dtype; a block mask
                                whose block is not a positive multiple of 128 or
                                does not divide N                               */
@@ -74,12 +99,19 @@ enum fa_status {
 };
 
 typedef struct fa_problem {
-  int32_t B, H, N, d;         /* batch, heads, sequence length, head dim       */
+  int32_t B, H, N, d;         /* batch, query heads, sequence length, head dim */
   int32_t dtype;              /* enum fa_dtype                                 */
   int32_t causal;             /* 0 or 1                                        */
-  float scale;                /* multiplies Q K^T, e.g. 1/sqrt(d); finite      */
+  float scale;                /* multiplies Q K^T, e.g. 1/sqrt(d); finite, > 0 */
   const uint8_t* block_mask;  /* device pointer or NULL (dense)                */
   int32_t mask_block;         /* side of one mask block; used iff block_mask   */
+  int32_t window;             /* 0: no window; W > 0: |i - j| < W              */
+  int32_t H_kv;               /* heads of K and V; 0 means H; must divide H    */
+  float dropout_p;            /* in [0, 1); 0 disables dropout                 */
+  uint64_t seed;              /* dropout generator key                         */
+  uint32_t offset;            /* dropout counter word: one value per call that
+                                 must draw a fresh mask with the same seed     */
+  uint32_t reserved;          /* must be 0                                     */
 } fa_problem;
 
 /* Bytes of device workspace that fa_fwd (pass 0) or fa_bwd (pass 1) needs for
@@ -94,8 +126,9 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
            float* lse, void* workspace, size_t ws_bytes, void* stream);
 
 /* Backward of f = <O, dO>.  Reads q, k, v, o, dout and lse, which must be the
- * O and LSE that fa_fwd produced for the same q, k, v and problem.  Overwrites
- * (does not accumulate into) dq, dk, dv.  workspace: at least
+ * O and LSE that fa_fwd produced for the same q, k, v and problem (with
+ * dropout: the same seed and offset, so the same mask is regenerated).
+ * Overwrites (does not accumulate into) dq, dk, dv.  workspace: at least
  * fa_workspace_size(p, 1) bytes; it receives D_i = dO_i . O_i (float32, B*H*N)
  * and, with a block mask, the compiled block lists. */
 int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,

@@ -27,21 +27,28 @@ from .binding import (  # noqa: F401
 )
 
 
-def attention(q, k, v, causal=False, scale=None, block_mask=None, mask_block=128):
-    """softmax(scale * Q K^T, masked) V with a backward through ``fa_bwd``."""
+def attention(q, k, v, causal=False, scale=None, block_mask=None, mask_block=128, window=0,
+              dropout_p=0.0, seed=0, offset=0):
+    """softmax(scale * Q K^T, masked) V with a backward through ``fa_bwd``.
+
+    k, v may carry fewer heads than q (grouped / multi-query attention); with
+    dropout_p > 0 the same (seed, offset) regenerates the mask in the backward.
+    """
     import torch
+
+    opts = dict(causal=causal, scale=scale, block_mask=block_mask, mask_block=mask_block,
+                window=window, dropout_p=dropout_p, seed=seed, offset=offset)
 
     class _Attention(torch.autograd.Function):
         @staticmethod
         def forward(ctx, q_, k_, v_):
-            o, lse = fa_fwd(q_, k_, v_, causal, scale, block_mask, mask_block)
+            o, lse = fa_fwd(q_, k_, v_, **opts)
             ctx.save_for_backward(q_, k_, v_, o, lse)
             return o
 
         @staticmethod
         def backward(ctx, do):
             q_, k_, v_, o, lse = ctx.saved_tensors
-            return fa_bwd(q_, k_, v_, o, do.contiguous(), lse, causal, scale, block_mask,
-                          mask_block)
+            return fa_bwd(q_, k_, v_, o, do.contiguous(), lse, **opts)
 
     return _Attention.apply(q, k, v)

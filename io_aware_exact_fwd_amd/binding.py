@@ -36,6 +36,12 @@ class FaProblem(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("block_mask", ctypes.c_void_p),
         ("mask_block", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("H_kv", ctypes.c_int32),
+        ("dropout_p", ctypes.c_float),
+        ("seed", ctypes.c_uint64),
+        ("offset", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
     ]
 
 
@@ -97,8 +103,10 @@ def _dtype_code(t):
     return codes[t.dtype]
 
 
-def make_problem(q, causal=False, scale=None, block_mask=None, mask_block=128) -> FaProblem:
-    """Problem descriptor for (B, H, N, d) tensor q; scale defaults to 1/sqrt(d)."""
+def make_problem(q, causal=False, scale=None, block_mask=None, mask_block=128, k=None,
+                 window=0, dropout_p=0.0, seed=0, offset=0) -> FaProblem:
+    """Problem descriptor for (B, H, N, d) tensor q (and K/V tensor k, whose
+    head count gives H_kv); scale defaults to 1/sqrt(d)."""
     if q.dim() != 4:
         raise ValueError("expected (B, H, N, d) tensors")
     B, H, N, d = q.shape
@@ -111,6 +119,12 @@ def make_problem(q, causal=False, scale=None, block_mask=None, mask_block=128) -
     p.scale = float(scale)
     p.block_mask = block_mask.data_ptr() if block_mask is not None else None
     p.mask_block = int(mask_block) if block_mask is not None else 0
+    p.window = int(window)
+    p.H_kv = int(k.shape[1]) if k is not None else H
+    p.dropout_p = float(dropout_p)
+    p.seed = int(seed) & (2**64 - 1)
+    p.offset = int(offset) & (2**32 - 1)
+    p.reserved = 0
     return p
 
 
@@ -125,7 +139,16 @@ def _check_tensors(ref, *ts):
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous (B, H, N, d)")
         if t.dtype != ref.dtype or t.shape != ref.shape:
-            raise ValueError("q, k, v (and o, dO) must share dtype and shape")
+            raise ValueError("tensors must share dtype and shape")
+
+
+def _check_qkv(q, k, v):
+    _check_tensors(q)
+    _check_tensors(k, k, v)
+    if k.dim() != 4 or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
+        raise ValueError("k, v must be (B, H_kv, N, d) with q's B, N and d")
+    if k.shape[1] == 0 or q.shape[1] % k.shape[1]:
+        raise ValueError("the K/V head count must divide the query head count")
 
 
 def _mask_arg(block_mask, ref):
@@ -145,13 +168,14 @@ def _stream(t):
 
 
 def fa_fwd(q, k, v, causal=False, scale=None, block_mask=None, mask_block=128, out=None,
-           lse=None):
-    """Forward: returns (O, LSE); O like q, LSE float32 (B, H, N), natural log."""
+           lse=None, window=0, dropout_p=0.0, seed=0, offset=0):
+    """Forward: returns (O, LSE); O like q, LSE float32 (B, H, N), natural log.
+    k, v may have fewer heads than q (grouped / multi-query attention)."""
     import torch
 
-    _check_tensors(q, k, v)
+    _check_qkv(q, k, v)
     bm = _mask_arg(block_mask, q)
-    p = make_problem(q, causal, scale, bm, mask_block)
+    p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset)
     B, H, N, d = q.shape
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -165,15 +189,17 @@ def fa_fwd(q, k, v, causal=False, scale=None, block_mask=None, mask_block=128, o
     return o, lse_t
 
 
-def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, block_mask=None, mask_block=128):
-    """Backward of <O, dO>: returns (dQ, dK, dV) like q."""
+def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, block_mask=None, mask_block=128,
+           window=0, dropout_p=0.0, seed=0, offset=0):
+    """Backward of <O, dO>: returns (dQ, dK, dV); dQ like q, dK and dV like k."""
     import torch
 
-    _check_tensors(q, k, v, o, dout)
+    _check_qkv(q, k, v)
+    _check_tensors(q, o, dout)
     if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
         raise ValueError("lse must be a contiguous float32 GPU tensor")
     bm = _mask_arg(block_mask, q)
-    p = make_problem(q, causal, scale, bm, mask_block)
+    p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_n = fa_workspace_size(p, 1)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
@@ -185,12 +211,13 @@ def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, block_mask=None, mas
     return dq, dk, dv
 
 
-def bwd_workspace(q, causal=False, scale=None, block_mask=None, mask_block=128):
-    """(problem, workspace tensor, workspace bytes) for the two backward stages."""
+def bwd_workspace(q, causal=False, scale=None, block_mask=None, mask_block=128, k=None,
+                  window=0, dropout_p=0.0, seed=0, offset=0):
+    """(problem, workspace tensor, workspace bytes, mask) for the two backward stages."""
     import torch
 
     bm = _mask_arg(block_mask, q)
-    p = make_problem(q, causal, scale, bm, mask_block)
+    p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset)
     ws_n = fa_workspace_size(p, 1)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
     return p, ws, ws_n, bm

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -20,11 +20,20 @@ int elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
 
 bool uses_lists(const fa_problem* p) { return p->block_mask != nullptr && p->dtype != FA_F32; }
 
+int kv_heads(const fa_problem* p) { return p->H_kv == 0 ? p->H : p->H_kv; }
+
+int group_of(const fa_problem* p) { return p->H / kv_heads(p); }
+
 int check_problem(const fa_problem* p) {
   if (!p) return FA_ERR_ARG;
   if (p->B <= 0 || p->H <= 0 || p->N <= 0 || p->d <= 0) return FA_ERR_ARG;
-  if (!isfinite(p->scale)) return FA_ERR_ARG;
+  if (!isfinite(p->scale) || !(p->scale > 0.f)) return FA_ERR_ARG;
   if (p->causal != 0 && p->causal != 1) return FA_ERR_ARG;
+  if (p->window < 0) return FA_ERR_ARG;
+  if (p->H_kv < 0 || (p->H_kv > 0 && p->H % p->H_kv != 0)) return FA_ERR_ARG;
+  if (!(p->dropout_p >= 0.f && p->dropout_p < 1.f)) return FA_ERR_ARG;
+  if (p->reserved != 0) return FA_ERR_ARG;
+  if (p->dropout_p > 0.f) return FA_ERR_UNSUPPORTED;
   if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (p->d != 64 && p->d != 128) return FA_ERR_UNSUPPORTED;
   // one head must be addressable with 32-bit byte offsets
@@ -118,6 +127,8 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
     f.nheads = nheads;
     f.d = p->d;
     f.causal = p->causal;
+    f.window = p->window;
+    f.group = group_of(p);
     f.c = c;
     f.scale = p->scale;
     return fa::launch_f32_fwd(f, s) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -132,6 +143,8 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
   f.N = p->N;
   f.nheads = nheads;
   f.nqt = (p->N + fa::kFwdRows - 1) / fa::kFwdRows;
+  f.window = p->window;
+  f.group = group_of(p);
   f.c = c;
   f.m = no_lists();
   const bool masked = p->block_mask != nullptr;
@@ -181,6 +194,8 @@ int bwd_setup(const fa_problem* p, const void* q, const void* k, const void* v, 
   b->dvec = (float*)workspace;
   b->N = p->N;
   b->nheads = p->B * p->H;
+  b->window = p->window;
+  b->group = group_of(p);
   b->c = p->scale * fa::kLog2e;
   b->scale = p->scale;
   b->m = no_lists();
@@ -206,6 +221,8 @@ fa::F32Params f32_params(const fa_problem* p, const fa::BwdParams& b) {
   f.nheads = b.nheads;
   f.d = p->d;
   f.causal = p->causal;
+  f.window = p->window;
+  f.group = b.group;
   f.c = b.c;
   f.scale = p->scale;
   return f;
@@ -227,6 +244,7 @@ int run_dq(const fa_problem* p, fa::BwdParams b, hipStream_t s) {
 }
 
 int run_dkdv(const fa_problem* p, fa::BwdParams b, hipStream_t s) {
+  b.nheads = p->B * kv_heads(p);  // one workgroup column per K/V head
   if (p->dtype == FA_F32)
     return fa::launch_f32_dkdv(f32_params(p, b), s) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
   b.ntiles = (p->N + fa::kBwdKeys - 1) / fa::kBwdKeys;

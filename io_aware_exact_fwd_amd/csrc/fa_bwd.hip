@@ -80,15 +80,16 @@ void bwd_dq_kernel(BwdParams p) {
   const int q_hi = min(q0 + kFwdRows, N) - 1;
 
   const size_t head_off = (size_t)head * N * D;
+  const size_t kv_off = (size_t)(head / p.group) * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * sizeof(T);
   const Buf bq = make_buf((const T*)p.q + head_off, head_bytes);
-  const Buf bk = make_buf((const T*)p.k + head_off, head_bytes);
-  const Buf bv = make_buf((const T*)p.v + head_off, head_bytes);
+  const Buf bk = make_buf((const T*)p.k + kv_off, head_bytes);
+  const Buf bv = make_buf((const T*)p.v + kv_off, head_bytes);
   const Buf bo = make_buf((const T*)p.o + head_off, head_bytes);
   const Buf bdo = make_buf((const T*)p.dout + head_off, head_bytes);
 
-  KeyTileList<G::KT, CAUSAL, MASKED> tiles;
-  tiles.init(p.m, N, q0, q_hi);
+  const Band band{N, p.window, CAUSAL};
+  const auto tiles = key_tiles<G::KT, MASKED>(p.m, band, q0, q_hi);
 
   // Q and dO fragments (B operands, k = head dim); D_i = dO_i . O_i
   V8 qf[G::NKS], dof[G::NKS];
@@ -116,7 +117,7 @@ void bwd_dq_kernel(BwdParams p) {
 
   u32x4 pk[G::CPT], pv[G::CPT];
   auto gload = [&](int it) {
-    const int k0 = tiles.key0(it);
+    const int k0 = tiles.pos0(it);
 #pragma unroll
     for (int i = 0; i < G::CPT; ++i) {
       const int ci = tid + i * kThreads;
@@ -154,10 +155,11 @@ void bwd_dq_kernel(BwdParams p) {
     const bool more = it + 1 < ntiles;
     if (more) gload(it + 1);
 
-    const int k0 = tiles.key0(it);
+    const int k0 = tiles.pos0(it);
     const char* ks = smem + cur * G::STAGE;
     const char* vs = ks + G::KBYTES;
-    const bool active = !CAUSAL || k0 <= qw0 + 31;
+    const int qw_last = qw0 + 31;
+    const bool active = k0 <= band.hi(qw_last) && k0 + G::KT - 1 >= band.lo(qw0);
     if (active) {
       f32x16 s[2], dp[2];
 #pragma unroll
@@ -172,18 +174,20 @@ void bwd_dq_kernel(BwdParams p) {
           dp[kb] = mfma32(b, dof[t], dp[kb]);
         }
       }
-      // hide keys in the future of the query and past the end: key of register
-      // r is k0 + g*4 + C(kb, r) with C = kb*32 + (r/4)*8 + r%4; hidden iff
-      // C > bound
-      const bool need_mask = (CAUSAL && k0 + G::KT - 1 > qw0) || (k0 + G::KT > N);
+      // hide keys outside the row's band (future, outside the window, past
+      // the end): key of register r is k0 + g*4 + C(kb, r) with
+      // C = kb*32 + (r/4)*8 + r%4; hidden iff C < lb or C > ub
+      const bool need_mask = k0 < band.lo(qw_last) || k0 + G::KT - 1 > band.hi(qw0);
       if (need_mask) {
-        int bound = N - 1 - k0 - g * 4;
-        if (CAUSAL) bound = min(bound, q - k0 - g * 4);
+        const int ub = band.hi(q) - k0 - g * 4;
+        const int lb = band.lo(q) - k0 - g * 4;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + (r >> 2) * 8 + (r & 3) > bound) s[kb][r] = kNegInf;
+          for (int r = 0; r < 16; ++r) {
+            const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
+            if (C > ub || C < lb) s[kb][r] = kNegInf;
+          }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -259,24 +263,24 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int l32 = lane & 31;
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = logical / p.ntiles;
-  const int kt = logical % p.ntiles;  // ascending: under causal, longest first
+  const int kvh = logical / p.ntiles;  // K/V head
+  const int kt = logical % p.ntiles;   // ascending: under causal, longest first
   const int N = p.N;
   const int k0 = kt * kBwdKeys;
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + l32;          // this lane's key
 
-  const size_t head_off = (size_t)head * N * D;
+  const size_t kv_off = (size_t)kvh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * sizeof(T);
-  const Buf bq = make_buf((const T*)p.q + head_off, head_bytes);
-  const Buf bk = make_buf((const T*)p.k + head_off, head_bytes);
-  const Buf bv = make_buf((const T*)p.v + head_off, head_bytes);
-  const Buf bdo = make_buf((const T*)p.dout + head_off, head_bytes);
-  const float* lse_h = p.lse + (size_t)head * N;
-  const float* dvec_h = p.dvec + (size_t)head * N;
+  const Buf bk = make_buf((const T*)p.k + kv_off, head_bytes);
+  const Buf bv = make_buf((const T*)p.v + kv_off, head_bytes);
 
-  QueryTileList<G::QT, CAUSAL, MASKED> tiles;
-  tiles.init(p.m, N, k0);
+  // The same query tiles are visited for each of the `group` query heads that
+  // read this K/V head; iteration it covers head it / nqt, tile it % nqt, and
+  // dK, dV sum over all of them in registers.
+  const Band band{N, p.window, CAUSAL};
+  const auto tiles = query_tiles<G::QT, MASKED>(p.m, band, k0, k0 + kBwdKeys - 1);
+  const int nqt = tiles.count;
 
   // K and V fragments: B operands of S = Q K^T and dP = dO V^T (k = head dim)
   V8 kf[G::NKS], vf[G::NKS];
@@ -297,7 +301,11 @@ void bwd_dkdv_kernel(BwdParams p) {
   u32x4 pq[G::CPT], pd[G::CPT];
   float plse = 0.f, pdv = 0.f;
   auto gload = [&](int it) {
-    const int qs = tiles.query0(it);
+    const int r = it / nqt;
+    const int qs = tiles.pos0(it - r * nqt);
+    const size_t qh = (size_t)kvh * p.group + r;  // query head
+    const Buf bq = make_buf((const T*)p.q + qh * N * D, head_bytes);
+    const Buf bdo = make_buf((const T*)p.dout + qh * N * D, head_bytes);
 #pragma unroll
     for (int i = 0; i < G::CPT; ++i) {
       const int ci = tid + i * kThreads;
@@ -311,9 +319,9 @@ void bwd_dkdv_kernel(BwdParams p) {
       plse = __builtin_huge_valf();
       pdv = 0.f;
       if (qq < N) {
-        const float l = lse_h[qq];
+        const float l = p.lse[qh * N + qq];
         if (l != kNegInf) plse = l * kLog2e;
-        pdv = dvec_h[qq];
+        pdv = p.dvec[qh * N + qq];
       }
     }
   };
@@ -334,7 +342,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  const int ntiles = tiles.count;
+  const int ntiles = nqt * p.group;
   if (ntiles > 0) {
     gload(0);
     lstore(0);
@@ -350,11 +358,14 @@ void bwd_dkdv_kernel(BwdParams p) {
     const bool more = it + 1 < ntiles;
     if (more) gload(it + 1);
 
-    const int qs0 = tiles.query0(it);
+    const int qs0 = tiles.pos0(it % nqt);
     const char* qsm = smem + cur * G::STAGE;
     const char* dsm = qsm + G::TBYTES;
     const float* lsm = (const float*)(dsm + G::TBYTES);
-    const bool active = !CAUSAL || qs0 + G::QT - 1 >= kw0;
+    // the wave's keys [kw0, kw_last] are seen by queries [qlo(kw0), qhi(kw_last)]
+    // between them, and by all of them in [qlo(kw_last), qhi(kw0)]
+    const int kw_last = kw0 + 31;
+    const bool active = qs0 <= band.qhi(kw_last) && qs0 + G::QT - 1 >= band.qlo(kw0);
     if (active) {
       f32x16 s[G::NQB], dp[G::NQB];
 #pragma unroll
@@ -369,17 +380,21 @@ void bwd_dkdv_kernel(BwdParams p) {
           dp[qb] = mfma32(b, vf[t], dp[qb]);
         }
       }
-      // causal: hide queries before this lane's key.  Query of register r in
+      // hide queries outside this lane's key band (before the key under
+      // causal, outside the window, past the end).  Query of register r in
       // block qb is qs0 + g*4 + C(qb, r), C = qb*32 + (r/4)*8 + r%4; hidden
-      // iff C < key - qs0 - g*4
-      const bool need_mask = CAUSAL && qs0 < kw0 + 31;
+      // iff C < lb or C > ub
+      const bool need_mask = qs0 < band.qlo(kw_last) || qs0 + G::QT - 1 > band.qhi(kw0);
       if (need_mask) {
-        const int bound = key - qs0 - g * 4;
+        const int lb = band.qlo(key) - qs0 - g * 4;
+        const int ub = band.qhi(key) - qs0 - g * 4;
 #pragma unroll
         for (int qb = 0; qb < G::NQB; ++qb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (qb * 32 + (r >> 2) * 8 + (r & 3) < bound) s[qb][r] = kNegInf;
+          for (int r = 0; r < 16; ++r) {
+            const int C = qb * 32 + (r >> 2) * 8 + (r & 3);
+            if (C < lb || C > ub) s[qb][r] = kNegInf;
+          }
       }
 #pragma unroll
       for (int qb = 0; qb < G::NQB; ++qb)
@@ -424,7 +439,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     for (int r = 0; r < 16; ++r) {
       const int kr = kw0 + (r >> 2) * 8 + g * 4 + (r & 3);
       if (kr < N) {
-        const size_t idx = head_off + (size_t)kr * D + db * 32 + l32;
+        const size_t idx = kv_off + (size_t)kr * D + db * 32 + l32;
         ((T*)p.dk)[idx] = (T)(dka[db][r] * p.scale);
         ((T*)p.dv)[idx] = (T)dva[db][r];
       }

@@ -19,6 +19,7 @@ constexpr int kF32Threads = 64;
 __device__ __forceinline__ bool f32_visible(const F32Params& p, int qi, int kj) {
   if (kj >= p.N || qi >= p.N) return false;
   if (p.causal && kj > qi) return false;
+  if (p.window > 0 && (kj - qi >= p.window || qi - kj >= p.window)) return false;
   if (p.block_mask) {
     const int nb = p.N / p.mask_block;
     return p.block_mask[(qi / p.mask_block) * nb + kj / p.mask_block] != 0;
@@ -33,6 +34,7 @@ __global__ __launch_bounds__(kF32Threads) void f32_fwd_kernel(F32Params p) {
   const int head = blockIdx.x;
   const int q = blockIdx.y * kF32Threads + threadIdx.x;
   const size_t hoff = (size_t)head * p.N * D;
+  const size_t kvoff = (size_t)(head / p.group) * p.N * D;
   float qv[D], o[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) {
@@ -45,8 +47,8 @@ __global__ __launch_bounds__(kF32Threads) void f32_fwd_kernel(F32Params p) {
     for (int e = threadIdx.x; e < kF32Tile * D; e += kF32Threads) {
       const int r = e / D, c = e % D;
       const bool in = j0 + r < p.N;
-      ks[r][c] = in ? p.k[hoff + (size_t)(j0 + r) * D + c] : 0.f;
-      vs[r][c] = in ? p.v[hoff + (size_t)(j0 + r) * D + c] : 0.f;
+      ks[r][c] = in ? p.k[kvoff + (size_t)(j0 + r) * D + c] : 0.f;
+      vs[r][c] = in ? p.v[kvoff + (size_t)(j0 + r) * D + c] : 0.f;
     }
     __syncthreads();
     // serial running max / sum over the staged keys (one key at a time)
@@ -85,6 +87,7 @@ __global__ __launch_bounds__(kF32Threads) void f32_dq_kernel(F32Params p) {
   const int head = blockIdx.x;
   const int q = blockIdx.y * kF32Threads + threadIdx.x;
   const size_t hoff = (size_t)head * p.N * D;
+  const size_t kvoff = (size_t)(head / p.group) * p.N * D;
   float qv[D], dov[D], dq[D];
   float dd = 0.f;
 #pragma unroll
@@ -106,8 +109,8 @@ __global__ __launch_bounds__(kF32Threads) void f32_dq_kernel(F32Params p) {
     for (int e = threadIdx.x; e < kF32Tile * D; e += kF32Threads) {
       const int r = e / D, c = e % D;
       const bool in = j0 + r < p.N;
-      ks[r][c] = in ? p.k[hoff + (size_t)(j0 + r) * D + c] : 0.f;
-      vs[r][c] = in ? p.v[hoff + (size_t)(j0 + r) * D + c] : 0.f;
+      ks[r][c] = in ? p.k[kvoff + (size_t)(j0 + r) * D + c] : 0.f;
+      vs[r][c] = in ? p.v[kvoff + (size_t)(j0 + r) * D + c] : 0.f;
     }
     __syncthreads();
 #pragma unroll 1
@@ -137,61 +140,65 @@ __global__ __launch_bounds__(kF32Threads) void f32_dkdv_kernel(F32Params p) {
   __shared__ float dos[kF32Tile][D];
   __shared__ float l2s[kF32Tile];
   __shared__ float dds[kF32Tile];
-  const int head = blockIdx.x;
+  const int kvh = blockIdx.x;  // K/V head; its query heads are kvh * group + r
   const int kj = blockIdx.y * kF32Threads + threadIdx.x;
-  const size_t hoff = (size_t)head * p.N * D;
+  const size_t kvoff = (size_t)kvh * p.N * D;
   float kv[D], vv[D], dk[D], dv[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) {
     const bool in = kj < p.N;
-    kv[c] = in ? p.k[hoff + (size_t)kj * D + c] : 0.f;
-    vv[c] = in ? p.v[hoff + (size_t)kj * D + c] : 0.f;
+    kv[c] = in ? p.k[kvoff + (size_t)kj * D + c] : 0.f;
+    vv[c] = in ? p.v[kvoff + (size_t)kj * D + c] : 0.f;
     dk[c] = 0.f;
     dv[c] = 0.f;
   }
-  for (int i0 = 0; i0 < p.N; i0 += kF32Tile) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < kF32Tile * D; e += kF32Threads) {
-      const int r = e / D, c = e % D;
-      const bool in = i0 + r < p.N;
-      qs[r][c] = in ? p.q[hoff + (size_t)(i0 + r) * D + c] : 0.f;
-      dos[r][c] = in ? p.dout[hoff + (size_t)(i0 + r) * D + c] : 0.f;
-    }
-    if (threadIdx.x < kF32Tile) {
-      const int qi = i0 + threadIdx.x;
-      float l2 = INFINITY, dd = 0.f;
-      if (qi < p.N) {
-        const float l = p.lse[(size_t)head * p.N + qi];
-        if (l != -INFINITY) l2 = l * kLog2e;
-        dd = p.dvec[(size_t)head * p.N + qi];
+  for (int r = 0; r < p.group; ++r) {
+    const int head = kvh * p.group + r;
+    const size_t hoff = (size_t)head * p.N * D;
+    for (int i0 = 0; i0 < p.N; i0 += kF32Tile) {
+      __syncthreads();
+      for (int e = threadIdx.x; e < kF32Tile * D; e += kF32Threads) {
+        const int rr = e / D, c = e % D;
+        const bool in = i0 + rr < p.N;
+        qs[rr][c] = in ? p.q[hoff + (size_t)(i0 + rr) * D + c] : 0.f;
+        dos[rr][c] = in ? p.dout[hoff + (size_t)(i0 + rr) * D + c] : 0.f;
       }
-      l2s[threadIdx.x] = l2;
-      dds[threadIdx.x] = dd;
-    }
-    __syncthreads();
+      if (threadIdx.x < kF32Tile) {
+        const int qi = i0 + threadIdx.x;
+        float l2 = INFINITY, dd = 0.f;
+        if (qi < p.N) {
+          const float l = p.lse[(size_t)head * p.N + qi];
+          if (l != -INFINITY) l2 = l * kLog2e;
+          dd = p.dvec[(size_t)head * p.N + qi];
+        }
+        l2s[threadIdx.x] = l2;
+        dds[threadIdx.x] = dd;
+      }
+      __syncthreads();
 #pragma unroll 1
-    for (int ii = 0; ii < kF32Tile; ++ii) {
-      if (!f32_visible(p, i0 + ii, kj)) continue;
-      float s = 0.f, dp = 0.f;
+      for (int ii = 0; ii < kF32Tile; ++ii) {
+        if (!f32_visible(p, i0 + ii, kj)) continue;
+        float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        s = fmaf(qs[ii][c], kv[c], s);
-        dp = fmaf(dos[ii][c], vv[c], dp);
-      }
-      const float pr = exp2f(s * p.c - l2s[ii]);
-      const float ds = pr * (dp - dds[ii]) * p.scale;
+        for (int c = 0; c < D; ++c) {
+          s = fmaf(qs[ii][c], kv[c], s);
+          dp = fmaf(dos[ii][c], vv[c], dp);
+        }
+        const float pr = exp2f(s * p.c - l2s[ii]);
+        const float ds = pr * (dp - dds[ii]) * p.scale;
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        dv[c] = fmaf(pr, dos[ii][c], dv[c]);
-        dk[c] = fmaf(ds, qs[ii][c], dk[c]);
+        for (int c = 0; c < D; ++c) {
+          dv[c] = fmaf(pr, dos[ii][c], dv[c]);
+          dk[c] = fmaf(ds, qs[ii][c], dk[c]);
+        }
       }
     }
   }
   if (kj < p.N) {
 #pragma unroll
     for (int c = 0; c < D; ++c) {
-      p.dk[hoff + (size_t)kj * D + c] = dk[c];
-      p.dv[hoff + (size_t)kj * D + c] = dv[c];
+      p.dk[kvoff + (size_t)kj * D + c] = dk[c];
+      p.dv[kvoff + (size_t)kj * D + c] = dv[c];
     }
   }
 }

@@ -98,13 +98,14 @@ void fwd_kernel(FwdParams p) {
   const int q_hi = min(q0 + BR, N) - 1;
 
   const size_t head_off = (size_t)head * N * D;
+  const size_t kv_off = (size_t)(head / p.group) * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * sizeof(T);
   const Buf bq = make_buf((const T*)p.q + head_off, head_bytes);
-  const Buf bk = make_buf((const T*)p.k + head_off, head_bytes);
-  const Buf bv = make_buf((const T*)p.v + head_off, head_bytes);
+  const Buf bk = make_buf((const T*)p.k + kv_off, head_bytes);
+  const Buf bv = make_buf((const T*)p.v + kv_off, head_bytes);
 
-  KeyTileList<G::KT, CAUSAL, MASKED> tiles;
-  tiles.init(p.m, N, q0, q_hi);
+  const Band band{N, p.window, CAUSAL};
+  const auto tiles = key_tiles<G::KT, MASKED>(p.m, band, q0, q_hi);
 
   // Q fragments: B operands of S^T = K Q^T (k = head dim), rows >= N read as 0.
   V8 qf[QB][G::NKS];
@@ -128,7 +129,7 @@ void fwd_kernel(FwdParams p) {
 
   u32x4 pk[G::CPT], pv[G::CPT];
   auto gload = [&](int it) {
-    const int k0 = tiles.key0(it);
+    const int k0 = tiles.pos0(it);
 #pragma unroll
     for (int i = 0; i < G::CPT; ++i) {
       const int ci = tid + i * G::THREADS;
@@ -163,10 +164,13 @@ void fwd_kernel(FwdParams p) {
     const bool more = it + 1 < ntiles;
     if (more) gload(it + 1);
 
-    const int k0 = tiles.key0(it);
+    const int k0 = tiles.pos0(it);
     const char* ks = smem + cur * G::STAGE;
     const char* vs = ks + G::KBYTES;
-    const bool active = !CAUSAL || k0 <= qw0 + WQ - 1;
+    // the wave's rows [qw0, qw_last] see keys [lo(qw0), hi(qw_last)] between
+    // them, and every row sees [lo(qw_last), hi(qw0)]
+    const int qw_last = qw0 + WQ - 1;
+    const bool active = k0 <= band.hi(qw_last) && k0 + G::KT - 1 >= band.lo(qw0);
     if (active) {
       // 1. S^T = K Q^T for each (key block kb, query block qb)
       f32x16 s[QB][2];
@@ -181,21 +185,24 @@ void fwd_kernel(FwdParams p) {
           for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][t], s[qb][kb]);
         }
       }
-      // 2. mask keys in the future of the query, and keys past the end.
-      // Key of register r is k0 + g*4 + C(kb, r), C = kb*32 + (r/4)*8 + r%4;
-      // it is hidden iff C > bound with one per-lane bound for both rules.
-      const bool need_mask = (CAUSAL && k0 + G::KT - 1 > qw0) || (k0 + G::KT > N);
+      // 2. mask keys outside the row's band (future keys, keys outside the
+      // window, keys past the end).  Key of register r is k0 + g*4 + C(kb, r),
+      // C = kb*32 + (r/4)*8 + r%4; it is hidden iff C < lb or C > ub.
+      const bool need_mask = k0 < band.lo(qw_last) || k0 + G::KT - 1 > band.hi(qw0);
       if (need_mask) {
         FA_KEEP_BRANCH();
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          int bound = N - 1 - k0 - g * 4;
-          if (CAUSAL) bound = min(bound, qw0 + qb * 32 + l32 - k0 - g * 4);
+          const int i = qw0 + qb * 32 + l32;
+          const int ub = band.hi(i) - k0 - g * 4;
+          const int lb = band.lo(i) - k0 - g * 4;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (kb * 32 + (r >> 2) * 8 + (r & 3) > bound) s[qb][kb][r] = kNegInf;
+            for (int r = 0; r < 16; ++r) {
+              const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
+              if (C > ub || C < lb) s[qb][kb][r] = kNegInf;
+            }
         }
       }
       // 3-4. per 32-key half kb: row maxima of the half, reference move if

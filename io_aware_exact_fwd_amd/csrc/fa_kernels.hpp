@@ -30,8 +30,10 @@ struct FwdParams {
   void* o;
   float* lse;
   int N;
-  int nheads;     // B * H
+  int nheads;     // B * H (query heads)
   int nqt;        // query tiles per head
+  int window;     // 0: none; W > 0: |i - j| < W
+  int group;      // query heads per K/V head; K/V head of query head h is h / group
   float c;        // scale * log2(e)
   MaskLists m;
 };
@@ -48,8 +50,10 @@ struct BwdParams {
   void* dv;
   float* dvec;    // D_i = dO_i . O_i, float32 [B*H*N]
   int N;
-  int nheads;
+  int nheads;     // dQ kernel: query heads B*H; dK/dV kernel: K/V heads B*H_kv
   int ntiles;     // query tiles (dQ kernel) or key tiles (dK/dV kernel) per head
+  int window;     // 0: none; W > 0: |i - j| < W
+  int group;      // query heads per K/V head
   float c;        // scale * log2(e)
   float scale;
   MaskLists m;
@@ -70,9 +74,11 @@ struct F32Params {
   const uint8_t* block_mask;
   int mask_block;
   int N;
-  int nheads;
+  int nheads;       // forward / dQ: query heads; dK/dV: K/V heads
   int d;
   int causal;
+  int window;
+  int group;
   float c;
   float scale;
 };

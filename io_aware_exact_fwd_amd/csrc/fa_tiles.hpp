@@ -1,110 +1,122 @@
 // fa_tiles.hpp -- which key tiles a query tile visits, and which query tiles a
-// key tile visits, under the three visibility rules: all keys, causal
-// (key <= query; key tiles entirely in the future are never loaded -- the
-// causal-mask section of the marketmaker.cc article), and block-sparse (only
-// tiles inside kept mask blocks -- block-sparse paragraph of the agihunt.info
-// summary).  Lists are ascending, so under causal the visible part is a prefix.
+// key tile visits.  Visibility is a band per row -- all keys, causal (key <=
+// query: key tiles entirely in the future are never loaded, the causal-mask
+// section of the marketmaker.cc article), a sliding window |i - j| < W (the
+// practice problems of the lynx-cortex page) -- intersected with a block-sparse
+// mask (only tiles inside kept mask blocks, block-sparse paragraph of the
+// agihunt.info summary).  Lists are ascending and cover one contiguous range of
+// the band, so the visited tiles are a contiguous run of the kept-block list.
 #pragma once
 
 #include "fa_kernels.hpp"
 
 namespace fa {
 
+// Band of visible positions, before the block mask.  Key j is visible to
+// query i iff lo(i) <= j <= hi(i); equivalently query i sees key j iff
+// qlo(j) <= i <= qhi(j).  All four are non-decreasing, so for a run of rows
+// [a, b] the union of their bands is [lo(a), hi(b)] and the part common to all
+// of them is [lo(b), hi(a)].
+struct Band {
+  int N;
+  int window;  // 0: none
+  bool causal;
+
+  __device__ __forceinline__ int lo(int i) const { return window > 0 ? max(0, i - window + 1) : 0; }
+  __device__ __forceinline__ int hi(int i) const {
+    if (causal) return min(N - 1, i);
+    return window > 0 ? min(N - 1, i + window - 1) : N - 1;
+  }
+  __device__ __forceinline__ int qlo(int j) const {
+    if (causal) return j;
+    return window > 0 ? max(0, j - window + 1) : 0;
+  }
+  __device__ __forceinline__ int qhi(int j) const {
+    return window > 0 ? min(N - 1, j + window - 1) : N - 1;
+  }
+};
+
+// Tiles of size TS that meet positions [lo, hi] (inclusive).  Dense: tiles
+// first .. first + count - 1.  MASKED: entries first .. first + count - 1 of the
+// flattened list "each kept block of `list`, split into mask_block / TS tiles".
+template <int TS, bool MASKED>
+struct TileRun {
+  int count;
+  int first;
+  int base;  // MASKED: first entry of the block list
+  int per;   // MASKED: tiles per mask block
+  int mb;
+  const int32_t* blocks;
+
+  __device__ __forceinline__ void init(int lo, int hi, const int32_t* list, int list_base,
+                                       int nblocks, int mask_block) {
+    first = count = 0;
+    blocks = list;
+    base = list_base;
+    mb = mask_block;
+    per = MASKED ? mask_block / TS : 0;
+    if (hi < lo) return;
+    if constexpr (!MASKED) {
+      first = lo / TS;
+      count = hi / TS - first + 1;
+    } else {
+      int skip = 0, c = 0;
+      for (int i = 0; i < nblocks; ++i) {
+        const int t0 = blocks[base + i] * mb;
+        if (t0 + mb - 1 < lo) {
+          skip += per;
+          continue;
+        }
+        if (t0 > hi) break;
+        const int ta = (max(lo, t0) - t0) / TS;
+        const int tb = (min(hi, t0 + mb - 1) - t0) / TS;
+        if (c == 0) skip += ta;
+        c += tb - ta + 1;
+      }
+      first = skip;
+      count = c;
+    }
+  }
+  // first position of the it-th visited tile
+  __device__ __forceinline__ int pos0(int it) const {
+    const int j = first + it;
+    if constexpr (!MASKED) {
+      return j * TS;
+    } else {
+      return blocks[base + j / per] * mb + (j % per) * TS;
+    }
+  }
+};
+
 // Key tiles of width KT for the query rows [q_lo, q_hi] (inclusive, q_hi < N).
-template <int KT, bool CAUSAL, bool MASKED>
-struct KeyTileList {
-  int count;
-  int base;   // MASKED: first entry of the query block's kept-block list
-  int per;    // MASKED: key tiles per mask block
-  int start0; // dense: first key (always 0)
-  const int32_t* cols;
-  int mb;
+template <int KT, bool MASKED>
+__device__ __forceinline__ TileRun<KT, MASKED> key_tiles(const MaskLists& m, const Band& b,
+                                                        int q_lo, int q_hi) {
+  TileRun<KT, MASKED> t;
+  if constexpr (MASKED) {
+    const int qb = q_lo / m.mask_block;
+    const int base = m.row_ptr[qb];
+    t.init(b.lo(q_lo), b.hi(q_hi), m.col_idx, base, m.row_ptr[qb + 1] - base, m.mask_block);
+  } else {
+    t.init(b.lo(q_lo), b.hi(q_hi), nullptr, 0, 0, 0);
+  }
+  return t;
+}
 
-  __device__ __forceinline__ void init(const MaskLists& m, int N, int q_lo, int q_hi) {
-    const int nkt = (N + KT - 1) / KT;
-    if constexpr (!MASKED) {
-      count = CAUSAL ? min(nkt, q_hi / KT + 1) : nkt;
-      cols = nullptr;
-      base = per = mb = 0;
-    } else {
-      mb = m.mask_block;
-      per = mb / KT;
-      const int qb = q_lo / mb;
-      base = m.row_ptr[qb];
-      const int nk = m.row_ptr[qb + 1] - base;
-      cols = m.col_idx;
-      if constexpr (!CAUSAL) {
-        count = nk * per;
-      } else {
-        int c = 0;
-        for (int i = 0; i < nk; ++i) {
-          const int k0 = cols[base + i] * mb;
-          if (k0 > q_hi) break;
-          c += min(per, (q_hi - k0) / KT + 1);
-        }
-        count = c;
-      }
-    }
-    start0 = 0;
+// Query tiles of height QT for the keys [k_lo, k_hi] (inclusive, k_lo < N).
+template <int QT, bool MASKED>
+__device__ __forceinline__ TileRun<QT, MASKED> query_tiles(const MaskLists& m, const Band& b,
+                                                          int k_lo, int k_hi) {
+  TileRun<QT, MASKED> t;
+  k_hi = min(k_hi, b.N - 1);
+  if constexpr (MASKED) {
+    const int kb = k_lo / m.mask_block;
+    const int base = m.col_ptr[kb];
+    t.init(b.qlo(k_lo), b.qhi(k_hi), m.row_idx, base, m.col_ptr[kb + 1] - base, m.mask_block);
+  } else {
+    t.init(b.qlo(k_lo), b.qhi(k_hi), nullptr, 0, 0, 0);
   }
-  __device__ __forceinline__ int key0(int it) const {
-    if constexpr (!MASKED) {
-      return it * KT;
-    } else {
-      return cols[base + it / per] * mb + (it % per) * KT;
-    }
-  }
-};
-
-// Query tiles of height QT for the keys [k_lo, k_hi] (inclusive).
-template <int QT, bool CAUSAL, bool MASKED>
-struct QueryTileList {
-  int count;
-  int first;  // dense: first query tile
-  int base;
-  int per;
-  const int32_t* rows;
-  int mb;
-
-  __device__ __forceinline__ void init(const MaskLists& m, int N, int k_lo) {
-    const int nqt = (N + QT - 1) / QT;
-    if constexpr (!MASKED) {
-      first = CAUSAL ? k_lo / QT : 0;
-      count = nqt - first;
-      rows = nullptr;
-      base = per = mb = 0;
-    } else {
-      mb = m.mask_block;
-      per = mb / QT;
-      const int kb = k_lo / mb;
-      base = m.col_ptr[kb];
-      const int nq = m.col_ptr[kb + 1] - base;
-      rows = m.row_idx;
-      first = 0;
-      if constexpr (!CAUSAL) {
-        count = nq * per;
-      } else {
-        // skip query tiles that end before k_lo; ascending, so they lead
-        int skip = 0, total = nq * per;
-        for (int i = 0; i < nq; ++i) {
-          const int q0 = rows[base + i] * mb;
-          if (q0 + mb - 1 < k_lo) { skip += per; continue; }
-          if (q0 < k_lo) skip += (k_lo - q0) / QT;
-          break;
-        }
-        first = skip;
-        count = total - skip;
-      }
-    }
-  }
-  __device__ __forceinline__ int query0(int it) const {
-    if constexpr (!MASKED) {
-      return (first + it) * QT;
-    } else {
-      const int j = first + it;
-      return rows[base + j / per] * mb + (j % per) * QT;
-    }
-  }
-};
+  return t;
+}
 
 }  // namespace fa

@@ -19,10 +19,20 @@ tasks; these synthetic tensors stand in for them -- no dataset is used):
                 power of two (block-sparse attention with a fixed butterfly
                 pattern, agihunt.info summary, block-sparse paragraph)
 
-Input recipe: torch.Generator('cpu').manual_seed(1000 + N); Q, K, V, dO drawn
-in that order as float32 N(0, 1) of shape (B, H, N, d), then rounded to the
-workload dtype with round-to-nearest-even.  Both the GPU path and the oracle
-receive these same rounded values.
+Extensions of the method (sliding window, grouped K/V heads, dropout):
+
+  long_window   long_wide with a sliding window of W=512 keys (the window
+                and length of the lynx-cortex practice problem on sliding
+                window attention)
+  gqa_h64_kv8   B=1  H=64 H_kv=8 N=8192 d=128 bf16 causal: the head
+                configuration the living-dl-book chapter gives for Llama-3
+                70B (64 query heads sharing 8 K/V heads, head dim 128)
+  gpt2_medium_dropout  gpt2_medium with attention dropout p = 0.1
+
+Input recipe: torch.Generator('cpu').manual_seed(1000 + N); Q (B, H, N, d),
+K and V (B, H_kv, N, d), dO (B, H, N, d) drawn in that order as float32
+N(0, 1), then rounded to the workload dtype with round-to-nearest-even.  Both
+the GPU path and the oracle receive these same rounded values.
 """
 
 from __future__ import annotations
@@ -57,10 +67,17 @@ class Workload:
     scale: float
     mask: str | None = None  # None | "butterfly"
     mask_block: int = 128
+    window: int = 0          # 0: none; W > 0: |i - j| < W
+    hkv: int = 0             # K/V heads; 0 means H
+    dropout: float = 0.0
 
     @property
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
+
+    @property
+    def H_kv(self) -> int:
+        return self.hkv or self.H
 
     def block_mask(self):
         if self.mask is None:
@@ -76,6 +93,12 @@ WORKLOADS = {
     "gpt2_medium": Workload("gpt2_medium", 64, 16, 1024, 64, "f16", True, 1.0 / 8.0),
     "long_wide": Workload("long_wide", 2, 16, 8192, 128, "bf16", True, 1.0 / math.sqrt(128.0)),
     "butterfly": Workload("butterfly", 1, 8, 65536, 64, "f16", False, 1.0 / 8.0, "butterfly", 128),
+    "long_window": Workload("long_window", 2, 16, 8192, 128, "bf16", True, 1.0 / math.sqrt(128.0),
+                            window=512),
+    "gqa_h64_kv8": Workload("gqa_h64_kv8", 1, 64, 8192, 128, "bf16", True,
+                            1.0 / math.sqrt(128.0), hkv=8),
+    "gpt2_medium_dropout": Workload("gpt2_medium_dropout", 64, 16, 1024, 64, "f16", True,
+                                    1.0 / 8.0, dropout=0.1),
 }
 
 
@@ -85,8 +108,9 @@ def _torch_dtype(name):
     return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[name]
 
 
-def make_inputs(B, H, N, d, dtype="f16", seed=None):
-    """Q, K, V, dO as CPU torch tensors (B, H, N, d) in ``dtype``.
+def make_inputs(B, H, N, d, dtype="f16", seed=None, hkv=None):
+    """Q, K, V, dO as CPU torch tensors in ``dtype``: Q and dO (B, H, N, d),
+    K and V (B, hkv or H, N, d).
 
     Drawn as float32 N(0, 1) from torch.Generator('cpu').manual_seed(seed),
     seed defaulting to 1000 + N, in the order Q, K, V, dO; then rounded to
@@ -97,8 +121,8 @@ def make_inputs(B, H, N, d, dtype="f16", seed=None):
     g = torch.Generator("cpu")
     g.manual_seed(1000 + N if seed is None else seed)
     out = []
-    for _ in range(4):
-        x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    for heads in (H, hkv or H, hkv or H, H):
+        x = torch.randn((B, heads, N, d), generator=g, dtype=torch.float32)
         out.append(x.to(_torch_dtype(dtype)).contiguous())
     return tuple(out)
 
@@ -112,20 +136,39 @@ def butterfly_block_mask(nblocks: int) -> np.ndarray:
     return keep.astype(np.uint8)
 
 
-def kept_pairs_per_head(N: int, causal: bool, block_mask=None, mask_block: int = 128) -> int:
+def _band(N, causal, window):
+    """Per query row i, the band [lo_i, hi_i] of keys that causal and window allow."""
+    i = np.arange(N, dtype=np.int64)
+    lo = np.maximum(0, i - window + 1) if window else np.zeros(N, np.int64)
+    if causal:
+        hi = i
+    elif window:
+        hi = np.minimum(N - 1, i + window - 1)
+    else:
+        hi = np.full(N, N - 1, np.int64)
+    return lo, hi
+
+
+def kept_pairs_per_head(N: int, causal: bool, block_mask=None, mask_block: int = 128,
+                        window: int = 0) -> int:
     """Number of (query, key) pairs whose probability can be non-zero, per head."""
+    lo, hi = _band(N, causal, window)
     if block_mask is None:
-        return N * (N + 1) // 2 if causal else N * N
+        return int((hi - lo + 1).sum())
     bm = np.asarray(block_mask) != 0
-    nb = bm.shape[0]
     total = 0
-    for bi in range(nb):
+    for bi in range(bm.shape[0]):
+        rl = lo[bi * mask_block:(bi + 1) * mask_block]
+        rh = hi[bi * mask_block:(bi + 1) * mask_block]
         for bj in np.nonzero(bm[bi])[0]:
-            if not causal or bj < bi:
-                total += mask_block * mask_block
-            elif bj == bi:
-                total += mask_block * (mask_block + 1) // 2
+            a = np.maximum(rl, bj * mask_block)
+            b = np.minimum(rh, (bj + 1) * mask_block - 1)
+            total += int(np.maximum(0, b - a + 1).sum())
     return int(total)
+
+
+def _pairs(w: Workload) -> int:
+    return kept_pairs_per_head(w.N, w.causal, w.block_mask(), w.mask_block, w.window)
 
 
 # FLOP convention: matrix-core work only, 2 FLOP per multiply-add, counted over
@@ -133,21 +176,21 @@ def kept_pairs_per_head(N: int, causal: bool, block_mask=None, mask_block: int =
 # recompute, dV, dP, dK and dQ products (10 d per pair).
 
 def fwd_flops(w: Workload) -> float:
-    return 4.0 * w.d * kept_pairs_per_head(w.N, w.causal, w.block_mask(), w.mask_block) * w.B * w.H
+    return 4.0 * w.d * _pairs(w) * w.B * w.H
 
 
 def bwd_flops(w: Workload) -> float:
-    return 10.0 * w.d * kept_pairs_per_head(w.N, w.causal, w.block_mask(), w.mask_block) * w.B * w.H
+    return 10.0 * w.d * _pairs(w) * w.B * w.H
 
 
 def fwd_compulsory_bytes(w: Workload) -> float:
     """Read Q, K, V once; write O and the fp32 LSE once."""
     x = w.N * w.d * w.elem_bytes
-    return float(w.B * w.H * (4 * x + 4 * w.N))
+    return float(w.B * (w.H * (2 * x + 4 * w.N) + w.H_kv * 2 * x))
 
 
 def bwd_compulsory_bytes(w: Workload) -> float:
     """Pre-pass reads O, dO and writes D; main pass reads Q, K, V, dO, LSE, D
     and writes dQ, dK, dV."""
     x = w.N * w.d * w.elem_bytes
-    return float(w.B * w.H * (9 * x + 12 * w.N))
+    return float(w.B * (w.H * (5 * x + 12 * w.N) + w.H_kv * 4 * x))

@@ -35,33 +35,57 @@ def rel_fro(x, ref):
     return num / den if den > 0 else num
 
 
-def run_gpu(q, k, v, do, causal, scale, block_mask, mask_block, backward=True):
+def run_gpu(q, k, v, do, causal, scale, block_mask, mask_block, backward=True, **ext):
     dev = torch.device("cuda:0")
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
     bm = None if block_mask is None else torch.as_tensor(block_mask, dtype=torch.uint8, device=dev)
-    o, lse = fa_fwd(qd, kd, vd, causal=causal, scale=scale, block_mask=bm, mask_block=mask_block)
+    o, lse = fa_fwd(qd, kd, vd, causal=causal, scale=scale, block_mask=bm, mask_block=mask_block,
+                    **ext)
     grads = None
     if backward:
         grads = fa_bwd(qd, kd, vd, o, dod, lse, causal=causal, scale=scale, block_mask=bm,
-                       mask_block=mask_block)
+                       mask_block=mask_block, **ext)
     torch.cuda.synchronize()
     return o, lse, grads
 
 
+def _kv_sums(sel, g, per_head):
+    """Sum per-query-head dK/dV contributions of the oracle into K/V heads.
+    Every K/V head touched by ``sel`` must have all g of its query heads in it."""
+    kv = []
+    for b, h in sel:
+        if (b, h // g) not in kv:
+            kv.append((b, h // g))
+    out = []
+    for b, j in kv:
+        rows = [t for t, (bb, hh) in enumerate(sel) if bb == b and hh // g == j]
+        assert len(rows) == g, "select whole groups of query heads"
+        out.append(per_head[rows].sum(axis=0))
+    return kv, np.stack(out)
+
+
 def check_case(name, B, H, N, d, dtype, causal, scale=None, block_mask=None, mask_block=128,
-               heads=None, backward=True, seed=None):
+               heads=None, backward=True, seed=None, window=0, hkv=None, dropout=None):
     """Run one case on the GPU and compare the selected heads with the oracle.
 
+    hkv: K/V heads (grouped-query attention); dropout: (p, seed, offset).
     Returns a dict of the observed errors."""
     scale = 1.0 / np.sqrt(d) if scale is None else scale
-    say(f"[case] {name}: B={B} H={H} N={N} d={d} {dtype} causal={causal} "
-        f"mask={'none' if block_mask is None else 'blocks'} heads={heads}")
-    q, k, v, do = make_inputs(B, H, N, d, dtype, seed)
-    o, lse, grads = run_gpu(q, k, v, do, causal, scale, block_mask, mask_block, backward)
+    ext = {"window": window}
+    okw = {"window": window}
+    if dropout is not None:
+        ext.update(dropout_p=dropout[0], seed=dropout[1], offset=dropout[2])
+        okw.update(dropout_p=dropout[0], seed=dropout[1], offset=dropout[2])
+    say(f"[case] {name}: B={B} H={H} H_kv={hkv or H} N={N} d={d} {dtype} causal={causal} "
+        f"mask={'none' if block_mask is None else 'blocks'} window={window} "
+        f"dropout={dropout} heads={heads}")
+    q, k, v, do = make_inputs(B, H, N, d, dtype, seed, hkv=hkv)
+    g = H // (hkv or H)
+    o, lse, grads = run_gpu(q, k, v, do, causal, scale, block_mask, mask_block, backward, **ext)
     sel = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     qn, kn, vn, don = (x.float().numpy() for x in (q, k, v, do))
     o_ref, lse_ref = attention_forward(qn, kn, vn, scale, causal, block_mask, mask_block,
-                                       heads=sel)
+                                       heads=sel, **okw)
     idx_b = [b for b, _ in sel]
     idx_h = [h for _, h in sel]
     o_g = to_np(o)[idx_b, idx_h]
@@ -75,11 +99,16 @@ def check_case(name, B, H, N, d, dtype, causal, scale=None, block_mask=None, mas
     err["lse"] = float(np.abs(lse_g[live] - lse_ref[live]).max()) if live.any() else 0.0
     if backward:
         dq_ref, dk_ref, dv_ref = attention_backward(qn, kn, vn, don, scale, causal, block_mask,
-                                                    mask_block, heads=sel)
-        for nm, g_t, ref in zip(("dq", "dk", "dv"), grads, (dq_ref, dk_ref, dv_ref)):
-            g = to_np(g_t)[idx_b, idx_h]
-            assert np.all(np.isfinite(g)), f"{name}: non-finite {nm}"
-            err[nm] = float(rel_fro(g, ref))
+                                                    mask_block, heads=sel, **okw)
+        kv, dk_ref = _kv_sums(sel, g, dk_ref)
+        _, dv_ref = _kv_sums(sel, g, dv_ref)
+        kb = [b for b, _ in kv]
+        kh = [j for _, j in kv]
+        gq, gk, gv = (to_np(t) for t in grads)
+        for nm, gsel, ref in (("dq", gq[idx_b, idx_h], dq_ref), ("dk", gk[kb, kh], dk_ref),
+                              ("dv", gv[kb, kh], dv_ref)):
+            assert np.all(np.isfinite(gsel)), f"{name}: non-finite {nm}"
+            err[nm] = float(rel_fro(gsel, ref))
     say(f"[case] {name}: errors {err}")
     assert err["o"] <= O_TOL[dtype], (name, "O", err)
     assert err["lse"] <= LSE_TOL, (name, "LSE", err)

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.fa_version() == 10000
+    assert B.fa_version() == 10100
     assert B.fa_status_string(0) == "ok"
     assert "workspace" in B.fa_status_string(B.FA_ERR_WORKSPACE)
     assert B.fa_status_string(12345) == "unknown status"
@@ -48,7 +48,23 @@ def _problem(**kw):
     p.scale = kw.get("scale", 0.125)
     p.block_mask = kw.get("block_mask", None)
     p.mask_block = kw.get("mask_block", 0)
+    p.window = kw.get("window", 0)
+    p.H_kv = kw.get("H_kv", 0)
+    p.dropout_p = kw.get("dropout_p", 0.0)
+    p.seed = kw.get("seed", 0)
+    p.offset = kw.get("offset", 0)
+    p.reserved = kw.get("reserved", 0)
     return p
+
+
+def test_problem_struct_layout_matches_header():
+    """Field offsets of the ctypes mirror follow the C layout of fa_problem
+    (natural alignment: the pointer and the 64-bit seed on 8-byte boundaries)."""
+    off = {name: getattr(B.FaProblem, name).offset for name, _ in B.FaProblem._fields_}
+    assert off["scale"] == 24 and off["block_mask"] == 32 and off["mask_block"] == 40
+    assert off["window"] == 44 and off["H_kv"] == 48 and off["dropout_p"] == 52
+    assert off["seed"] == 56 and off["offset"] == 64 and off["reserved"] == 68
+    assert ctypes.sizeof(B.FaProblem) == 72
 
 
 def test_workspace_sizes():
@@ -87,6 +103,15 @@ def _fwd(p, ws=None, ws_n=0, ptrs=(FAKE,) * 5):
     ({"block_mask": FAKE, "mask_block": 64}, B.FA_ERR_UNSUPPORTED),
     ({"block_mask": FAKE, "mask_block": 128, "N": 200}, B.FA_ERR_UNSUPPORTED),
     ({"N": 1 << 24, "d": 128}, B.FA_ERR_UNSUPPORTED),
+    ({"scale": 0.0}, B.FA_ERR_ARG),
+    ({"scale": -0.125}, B.FA_ERR_ARG),
+    ({"window": -1}, B.FA_ERR_ARG),
+    ({"H_kv": 2}, B.FA_ERR_ARG),          # does not divide H = 3
+    ({"H_kv": -3}, B.FA_ERR_ARG),
+    ({"dropout_p": 1.0}, B.FA_ERR_ARG),
+    ({"dropout_p": -0.1}, B.FA_ERR_ARG),
+    ({"dropout_p": math.nan}, B.FA_ERR_ARG),
+    ({"reserved": 1}, B.FA_ERR_ARG),
 ])
 def test_invalid_problems_rejected(kw, status):
     assert _fwd(_problem(**kw)) == status

@@ -30,6 +30,29 @@ def test_kept_pairs():
     assert wl.kept_pairs_per_head(32, True, small, 4) == causal_dense.sum()
 
 
+def test_kept_pairs_with_window_match_the_oracle_visibility():
+    from oracle import visibility
+
+    for n, causal, w, bm, mb in ((40, True, 7, None, 4), (40, False, 7, None, 4),
+                                 (32, True, 5, wl.butterfly_block_mask(8), 4),
+                                 (32, False, 100, wl.butterfly_block_mask(8), 4),
+                                 (33, False, 1, None, 4)):
+        want = visibility(np.arange(n), np.arange(n), causal, bm, mb, w).sum()
+        assert wl.kept_pairs_per_head(n, causal, bm, mb, w) == want
+    # the pages' sliding-window example: N = 8192, W = 512, causal
+    assert wl.kept_pairs_per_head(8192, True, window=512) == 512 * 513 // 2 + (8192 - 512) * 512
+
+
+def test_grouped_inputs_share_the_stream():
+    q, k, v, do = wl.make_inputs(2, 4, 16, 8, "f16", hkv=2)
+    assert q.shape == (2, 4, 16, 8) and k.shape == (2, 2, 16, 8) and do.shape == q.shape
+    q1, k1, *_ = wl.make_inputs(2, 4, 16, 8, "f16")
+    assert torch.equal(q, q1) and not torch.equal(k, k1[:, :2])
+    w = wl.WORKLOADS["gqa_h64_kv8"]
+    x = w.N * w.d * 2
+    assert wl.fwd_compulsory_bytes(w) == w.B * (w.H * (2 * x + 4 * w.N) + w.H_kv * 2 * x)
+
+
 def test_headline_flops():
     w = wl.WORKLOADS["gpt2_medium"]
     assert abs(wl.fwd_flops(w) / 1e9 - 137.57) < 0.01
