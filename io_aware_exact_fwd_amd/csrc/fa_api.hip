@@ -33,7 +33,6 @@ int check_problem(const fa_problem* p) {
   if (p->H_kv < 0 || (p->H_kv > 0 && p->H % p->H_kv != 0)) return FA_ERR_ARG;
   if (!(p->dropout_p >= 0.f && p->dropout_p < 1.f)) return FA_ERR_ARG;
   if (p->reserved != 0) return FA_ERR_ARG;
-  if (p->dropout_p > 0.f) return FA_ERR_UNSUPPORTED;
   if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (p->d != 64 && p->d != 128) return FA_ERR_UNSUPPORTED;
   // one head must be addressable with 32-bit byte offsets
@@ -84,6 +83,18 @@ fa::MaskLists mask_lists(const fa_problem* p, const Lists& l) {
   return m;
 }
 
+// Dropout constants: t8 = floor(256 p) of the float32 p (exact: scaling by
+// 256 is exact), keep scale 256 / (256 - t8).  t8 = 0 means no dropout.
+fa::DropParams drop_params(const fa_problem* p) {
+  fa::DropParams d;
+  d.t8 = (uint32_t)floorf(p->dropout_p * 256.0f);
+  d.mult = 256.0f / (float)(256u - d.t8);
+  d.k0 = (uint32_t)(p->seed & 0xFFFFFFFFu);
+  d.k1 = (uint32_t)(p->seed >> 32);
+  d.offset = p->offset;
+  return d;
+}
+
 fa::MaskLists no_lists() {
   fa::MaskLists m;
   m.row_ptr = m.col_idx = m.col_ptr = m.row_idx = nullptr;
@@ -131,6 +142,7 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
     f.group = group_of(p);
     f.c = c;
     f.scale = p->scale;
+    f.drop = drop_params(p);
     return fa::launch_f32_fwd(f, s) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
   }
 
@@ -147,6 +159,7 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
   f.group = group_of(p);
   f.c = c;
   f.m = no_lists();
+  f.drop = drop_params(p);
   const bool masked = p->block_mask != nullptr;
   if (masked) {
     Lists l = carve_lists(p, (char*)workspace);
@@ -155,8 +168,9 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
       return FA_ERR_LAUNCH;
     f.m = mask_lists(p, l);
   }
-  return fa::launch_fwd(f, p->dtype, p->d, p->causal != 0, masked, s) == hipSuccess ? FA_OK
-                                                                                    : FA_ERR_LAUNCH;
+  const hipError_t e = f.drop.t8 ? fa::launch_fwd_drop(f, p->dtype, p->d, p->causal != 0, masked, s)
+                                 : fa::launch_fwd(f, p->dtype, p->d, p->causal != 0, masked, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // extern "C"
@@ -199,6 +213,7 @@ int bwd_setup(const fa_problem* p, const void* q, const void* k, const void* v, 
   b->c = p->scale * fa::kLog2e;
   b->scale = p->scale;
   b->m = no_lists();
+  b->drop = drop_params(p);
   if (p->block_mask) b->m = mask_lists(p, carve_lists(p, (char*)workspace + dvec_bytes(p)));
   return FA_OK;
 }
@@ -225,6 +240,7 @@ fa::F32Params f32_params(const fa_problem* p, const fa::BwdParams& b) {
   f.group = b.group;
   f.c = b.c;
   f.scale = p->scale;
+  f.drop = b.drop;
   return f;
 }
 
@@ -238,9 +254,10 @@ int run_dq(const fa_problem* p, fa::BwdParams b, hipStream_t s) {
                                         s) != hipSuccess)
     return FA_ERR_LAUNCH;
   b.ntiles = (p->N + fa::kFwdRows - 1) / fa::kFwdRows;
-  return fa::launch_bwd_dq(b, p->dtype, p->d, p->causal != 0, masked, s) == hipSuccess
-             ? FA_OK
-             : FA_ERR_LAUNCH;
+  const hipError_t e = b.drop.t8
+                           ? fa::launch_bwd_dq_drop(b, p->dtype, p->d, p->causal != 0, masked, s)
+                           : fa::launch_bwd_dq(b, p->dtype, p->d, p->causal != 0, masked, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 int run_dkdv(const fa_problem* p, fa::BwdParams b, hipStream_t s) {
@@ -248,10 +265,11 @@ int run_dkdv(const fa_problem* p, fa::BwdParams b, hipStream_t s) {
   if (p->dtype == FA_F32)
     return fa::launch_f32_dkdv(f32_params(p, b), s) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
   b.ntiles = (p->N + fa::kBwdKeys - 1) / fa::kBwdKeys;
-  return fa::launch_bwd_dkdv(b, p->dtype, p->d, p->causal != 0, p->block_mask != nullptr, s) ==
-                 hipSuccess
-             ? FA_OK
-             : FA_ERR_LAUNCH;
+  const bool masked = p->block_mask != nullptr;
+  const hipError_t e = b.drop.t8
+                           ? fa::launch_bwd_dkdv_drop(b, p->dtype, p->d, p->causal != 0, masked, s)
+                           : fa::launch_bwd_dkdv(b, p->dtype, p->d, p->causal != 0, masked, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // namespace

@@ -21,6 +21,7 @@
 // The price is computing S and dP in both kernels: 14 d multiply-add FLOPs
 // per visible pair instead of 10 d.
 #include "fa_common.hpp"
+#include "fa_dropout.hpp"
 #include "fa_kernels.hpp"
 #include "fa_tiles.hpp"
 
@@ -53,15 +54,17 @@ struct DqGeom {
   static constexpr int CPT = KT * CPR / kThreads;
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
+  // waves per SIMD: dropout at head dim 128 needs the full register file
+  static constexpr int wpe(bool drop) { return drop && D == 128 ? 1 : FA_DQ_WPE; }
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED>
+template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(FA_DQ_WPE, FA_DQ_WPE)))
+                          amdgpu_waves_per_eu(DqGeom<D>::wpe(DROP), DqGeom<D>::wpe(DROP))))
 void bwd_dq_kernel(BwdParams p) {
   using G = DqGeom<D>;
   using V8 = typename Vec8<T>::type;
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,6 +107,9 @@ void bwd_dq_kernel(BwdParams p) {
     for (int i = 0; i < 8; ++i) dpart += to_f32(dof[t][i]) * to_f32(of[i]);
   }
   const float dq_d = dpart + __shfl_xor(dpart, 32, 64);
+  // Under dropout dS = mult * P o (keep o dP' - D / mult), dP' = dO V^T: the
+  // mask selects dP', and mult joins the scale of the finished dQ.
+  const float d_sub = DROP ? dq_d / p.drop.mult : dq_d;
   float lse2 = __builtin_huge_valf();  // rows past the end or with no visible key: P = 0
   if (q < N) {
     const float lse = p.lse[(size_t)head * N + q];
@@ -190,12 +196,19 @@ void bwd_dq_kernel(BwdParams p) {
           }
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        u32x4 kw;
+        if constexpr (DROP)
+          kw = drop_bytes_query_lanes(p.drop, (uint32_t)head, k0 + kb * 32, qw0,
+                                      smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pr = fast_exp2(__builtin_fmaf(s[kb][r], p.c, -lse2));
-          s[kb][r] = pr * (dp[kb][r] - dq_d);  // dS^T (scale applied to dQ at the end)
+          float dpr = dp[kb][r];
+          if constexpr (DROP) dpr = keep_byte(kw[r >> 2], r & 3, p.drop.t8) ? dpr : 0.f;
+          s[kb][r] = pr * (dpr - d_sub);  // dS^T (scale applied to dQ at the end)
         }
+      }
       // dQ^T += K^T dS^T : A = K^T via transpose reads of the K tile
       V8 bs[4];
 #pragma unroll
@@ -219,13 +232,14 @@ void bwd_dq_kernel(BwdParams p) {
 
   if (q < N) {
     T* row = (T*)p.dq + head_off + (size_t)q * D;
+    const float f = DROP ? p.scale * p.drop.mult : p.scale;
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         u32x2 w;
-        w[0] = pack2<T>(acc[db][rr * 4 + 0] * p.scale, acc[db][rr * 4 + 1] * p.scale);
-        w[1] = pack2<T>(acc[db][rr * 4 + 2] * p.scale, acc[db][rr * 4 + 3] * p.scale);
+        w[0] = pack2<T>(acc[db][rr * 4 + 0] * f, acc[db][rr * 4 + 1] * f);
+        w[1] = pack2<T>(acc[db][rr * 4 + 2] * f, acc[db][rr * 4 + 3] * f);
         *(u32x2*)(row + db * 32 + rr * 8 + g * 4) = w;
       }
   }
@@ -248,13 +262,13 @@ struct DkvGeom {
   static constexpr int WPE = D == 64 ? FA_DKDV64_WPE : 1;  // waves per SIMD the registers allow
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED>
+template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(DkvGeom<D>::WPE, DkvGeom<D>::WPE)))
 void bwd_dkdv_kernel(BwdParams p) {
   using G = DkvGeom<D>;
   using V8 = typename Vec8<T>::type;
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -322,6 +336,7 @@ void bwd_dkdv_kernel(BwdParams p) {
         const float l = p.lse[qh * N + qq];
         if (l != kNegInf) plse = l * kLog2e;
         pdv = p.dvec[qh * N + qq];
+        if (DROP) pdv /= p.drop.mult;  // see the dS step
       }
     }
   };
@@ -359,6 +374,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     if (more) gload(it + 1);
 
     const int qs0 = tiles.pos0(it % nqt);
+    const int qh = kvh * p.group + it / nqt;  // query head of this step
     const char* qsm = smem + cur * G::STAGE;
     const char* dsm = qsm + G::TBYTES;
     const float* lsm = (const float*)(dsm + G::TBYTES);
@@ -396,8 +412,15 @@ void bwd_dkdv_kernel(BwdParams p) {
             if (C < lb || C > ub) s[qb][r] = kNegInf;
           }
       }
+      // Under dropout (keep mask Z01, scale mult): dV = mult (Z01 o P)^T dO and
+      // dS = mult * P o (Z01 o dP' - D / mult); both mult factors join the
+      // finished dV and dK, and the D loaded with the tile is already / mult.
 #pragma unroll
-      for (int qb = 0; qb < G::NQB; ++qb)
+      for (int qb = 0; qb < G::NQB; ++qb) {
+        u32x4 kw;
+        if constexpr (DROP)
+          kw = drop_bytes_key_lanes(p.drop, (uint32_t)qh, kw0, qs0 + qb * 32,
+                                    smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const f32x4 l4 = *(const f32x4*)(lsm + qb * 32 + rr * 8 + g * 4);
@@ -406,10 +429,17 @@ void bwd_dkdv_kernel(BwdParams p) {
           for (int e = 0; e < 4; ++e) {
             const int r = rr * 4 + e;
             const float pr = fast_exp2(__builtin_fmaf(s[qb][r], p.c, -l4[e]));
-            s[qb][r] = pr;                                   // P
-            dp[qb][r] = pr * (dp[qb][r] - d4[e]);  // dS (scale applied to dK at the end)
+            if constexpr (DROP) {
+              const bool keep = keep_byte(kw[rr], e, p.drop.t8);
+              s[qb][r] = keep ? pr : 0.f;                              // Z01 o P
+              dp[qb][r] = pr * ((keep ? dp[qb][r] : 0.f) - d4[e]);  // dS / mult
+            } else {
+              s[qb][r] = pr;                                   // P
+              dp[qb][r] = pr * (dp[qb][r] - d4[e]);  // dS (scale applied to dK at the end)
+            }
           }
         }
+      }
       // dV += P^T dO,  dK += dS^T Q ; k-step t covers queries 16t .. 16t+15
 #pragma unroll
       for (int t = 0; t < G::QT / 16; ++t) {
@@ -433,6 +463,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
 
   // C layout: lane -> head-dim column, register -> key row
+  const float fk = DROP ? p.scale * p.drop.mult : p.scale;
+  const float fv = DROP ? p.drop.mult : 1.f;
 #pragma unroll
   for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
@@ -440,48 +472,78 @@ void bwd_dkdv_kernel(BwdParams p) {
       const int kr = kw0 + (r >> 2) * 8 + g * 4 + (r & 3);
       if (kr < N) {
         const size_t idx = kv_off + (size_t)kr * D + db * 32 + l32;
-        ((T*)p.dk)[idx] = (T)(dka[db][r] * p.scale);
-        ((T*)p.dv)[idx] = (T)dva[db][r];
+        ((T*)p.dk)[idx] = (T)(dka[db][r] * fk);
+        ((T*)p.dv)[idx] = (T)(dva[db][r] * fv);
       }
     }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool DROP>
 static hipError_t launch_dq_t(const BwdParams& p, bool causal, bool masked, hipStream_t s) {
   dim3 grid(p.nheads * p.ntiles), block(kThreads);
-  if (causal && masked) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, true>), grid, block, 0, s, p);
-  else if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, false>), grid, block, 0, s, p);
-  else if (masked) hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, false>), grid, block, 0, s, p);
+  if (causal && masked)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, true, DROP>), grid, block, 0, s, p);
+  else if (causal)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, false, DROP>), grid, block, 0, s, p);
+  else if (masked)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, true, DROP>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, false, DROP>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool DROP>
 static hipError_t launch_dkdv_t(const BwdParams& p, bool causal, bool masked, hipStream_t s) {
   dim3 grid(p.nheads * p.ntiles), block(kThreads);
-  if (causal && masked) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, true>), grid, block, 0, s, p);
-  else if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, false>), grid, block, 0, s, p);
-  else if (masked) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, false>), grid, block, 0, s, p);
+  if (causal && masked)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, true, DROP>), grid, block, 0, s, p);
+  else if (causal)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, false, DROP>), grid, block, 0, s, p);
+  else if (masked)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, true, DROP>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, false, DROP>), grid, block, 0, s, p);
   return hipGetLastError();
+}
+
+template <bool DROP>
+static hipError_t dq_dispatch(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                              hipStream_t s) {
+  if (dtype == 1)
+    return d == 64 ? launch_dq_t<_Float16, 64, DROP>(p, causal, masked, s)
+                   : launch_dq_t<_Float16, 128, DROP>(p, causal, masked, s);
+  return d == 64 ? launch_dq_t<__bf16, 64, DROP>(p, causal, masked, s)
+                 : launch_dq_t<__bf16, 128, DROP>(p, causal, masked, s);
+}
+
+template <bool DROP>
+static hipError_t dkdv_dispatch(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                                hipStream_t s) {
+  if (dtype == 1)
+    return d == 64 ? launch_dkdv_t<_Float16, 64, DROP>(p, causal, masked, s)
+                   : launch_dkdv_t<_Float16, 128, DROP>(p, causal, masked, s);
+  return d == 64 ? launch_dkdv_t<__bf16, 64, DROP>(p, causal, masked, s)
+                 : launch_dkdv_t<__bf16, 128, DROP>(p, causal, masked, s);
 }
 
 hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int d, bool causal, bool masked,
                          hipStream_t s) {
-  if (dtype == 1)
-    return d == 64 ? launch_dq_t<_Float16, 64>(p, causal, masked, s)
-                   : launch_dq_t<_Float16, 128>(p, causal, masked, s);
-  return d == 64 ? launch_dq_t<__bf16, 64>(p, causal, masked, s)
-                 : launch_dq_t<__bf16, 128>(p, causal, masked, s);
+  return dq_dispatch<false>(p, dtype, d, causal, masked, s);
 }
 
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int d, bool causal, bool masked,
                            hipStream_t s) {
-  if (dtype == 1)
-    return d == 64 ? launch_dkdv_t<_Float16, 64>(p, causal, masked, s)
-                   : launch_dkdv_t<_Float16, 128>(p, causal, masked, s);
-  return d == 64 ? launch_dkdv_t<__bf16, 64>(p, causal, masked, s)
-                 : launch_dkdv_t<__bf16, 128>(p, causal, masked, s);
+  return dkdv_dispatch<false>(p, dtype, d, causal, masked, s);
+}
+
+hipError_t launch_bwd_dq_drop(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                              hipStream_t s) {
+  return dq_dispatch<true>(p, dtype, d, causal, masked, s);
+}
+
+hipError_t launch_bwd_dkdv_drop(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                                hipStream_t s) {
+  return dkdv_dispatch<true>(p, dtype, d, causal, masked, s);
 }
 
 }  // namespace fa

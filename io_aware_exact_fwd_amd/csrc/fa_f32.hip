@@ -9,6 +9,7 @@
 #include <math.h>
 
 #include "fa_common.hpp"
+#include "fa_dropout.hpp"
 #include "fa_kernels.hpp"
 
 namespace fa {
@@ -25,6 +26,16 @@ __device__ __forceinline__ bool f32_visible(const F32Params& p, int qi, int kj) 
     return p.block_mask[(qi / p.mask_block) * nb + kj / p.mask_block] != 0;
   }
   return true;
+}
+
+// Dropout multiplier of weight (qi, kj) of query head `head`: 0 if dropped,
+// the scale of kept weights otherwise (one generator evaluation per weight:
+// this path is not tuned).
+__device__ __forceinline__ float f32_drop(const F32Params& p, int head, int qi, int kj) {
+  if (p.drop.t8 == 0) return 1.f;
+  const u32x4 x = philox4x32_10((uint32_t)kj >> 2, (uint32_t)qi >> 2, (uint32_t)head,
+                                p.drop.offset, p.drop.k0, p.drop.k1);
+  return keep_byte(x[qi & 3], kj & 3, p.drop.t8) ? p.drop.mult : 0.f;
 }
 
 template <int D>
@@ -67,9 +78,10 @@ __global__ __launch_bounds__(kF32Threads) void f32_fwd_kernel(F32Params p) {
         m = sc;
       }
       const float e = exp2f(sc - m);
-      l += e;
+      l += e;  // the row sum normalises P itself; dropout acts on the weights only
+      const float ez = e * f32_drop(p, head, q, j0 + jj);
 #pragma unroll
-      for (int c = 0; c < D; ++c) o[c] = fmaf(e, vs[jj][c], o[c]);
+      for (int c = 0; c < D; ++c) o[c] = fmaf(ez, vs[jj][c], o[c]);
     }
   }
   if (q < p.N) {
@@ -123,7 +135,7 @@ __global__ __launch_bounds__(kF32Threads) void f32_dq_kernel(F32Params p) {
         dp = fmaf(dov[c], vs[jj][c], dp);
       }
       const float pr = exp2f(s * p.c - lse2);
-      const float ds = pr * (dp - dd) * p.scale;
+      const float ds = pr * (dp * f32_drop(p, head, q, j0 + jj) - dd) * p.scale;
 #pragma unroll
       for (int c = 0; c < D; ++c) dq[c] = fmaf(ds, ks[jj][c], dq[c]);
     }
@@ -185,10 +197,12 @@ __global__ __launch_bounds__(kF32Threads) void f32_dkdv_kernel(F32Params p) {
           dp = fmaf(dos[ii][c], vv[c], dp);
         }
         const float pr = exp2f(s * p.c - l2s[ii]);
-        const float ds = pr * (dp - dds[ii]) * p.scale;
+        const float z = f32_drop(p, head, i0 + ii, kj);
+        const float ds = pr * (dp * z - dds[ii]) * p.scale;
+        const float pz = pr * z;
 #pragma unroll
         for (int c = 0; c < D; ++c) {
-          dv[c] = fmaf(pr, dos[ii][c], dv[c]);
+          dv[c] = fmaf(pz, dos[ii][c], dv[c]);
           dk[c] = fmaf(ds, qs[ii][c], dk[c]);
         }
       }

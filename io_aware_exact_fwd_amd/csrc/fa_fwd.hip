@@ -34,6 +34,7 @@
 // exchange with lane l^32, and the probabilities are already laid out as the
 // B operand of the P V product (see fa_common.hpp for the MFMA layouts).
 #include "fa_common.hpp"
+#include "fa_dropout.hpp"
 #include "fa_kernels.hpp"
 #include "fa_tiles.hpp"
 
@@ -72,7 +73,7 @@ struct FwdGeom {
   static_assert(KT * CPR % THREADS == 0, "tile must split evenly over threads");
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED, int NW, int QB, int WPE>
+template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP, int NW, int QB, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(FwdParams p) {
@@ -80,7 +81,7 @@ void fwd_kernel(FwdParams p) {
   using V8 = typename Vec8<T>::type;
   constexpr int BR = NW * QB * 32;  // query rows per workgroup
   constexpr int WQ = QB * 32;       // query rows per wave
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? NW * kDropLdsPerWave : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,6 +107,7 @@ void fwd_kernel(FwdParams p) {
 
   const Band band{N, p.window, CAUSAL};
   const auto tiles = key_tiles<G::KT, MASKED>(p.m, band, q0, q_hi);
+  const uint32_t bias = (0x8000u - p.drop.t8) * 0x10001u;  // dropout byte test, see keep_pair_mask
 
   // Q fragments: B operands of S^T = K Q^T (k = head dim), rows >= N read as 0.
   V8 qf[QB][G::NKS];
@@ -215,6 +217,15 @@ void fwd_kernel(FwdParams p) {
       const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        // dropout: generator bytes of this half's keys (byte e of kw[qb][rr]
+        // decides the key of register rr * 4 + e)
+        u32x4 kw[QB];
+        if constexpr (DROP) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            kw[qb] = drop_bytes_query_lanes(p.drop, (uint32_t)head, k0 + kb * 32, qw0 + qb * 32,
+                                            smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
+        }
         float mxs[QB];
         bool move = false;
 #pragma unroll
@@ -259,6 +270,8 @@ void fwd_kernel(FwdParams p) {
               } else {
                 lp += e0 + e1;  // bf16 rounding is too coarse for the LSE: fp32 sum
               }
+              // dropout zeroes weights after the row sum: LSE normalises P itself
+              if constexpr (DROP) w[h] &= keep_pair_mask(kw[qb][th * 2 + (h >> 1)], h & 1, bias);
             }
             l_run[qb] += lp;
             bp[qb] = __builtin_bit_cast(V8, w);
@@ -277,12 +290,13 @@ void fwd_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  // epilogue: deferred normalisation, natural-log LSE
+  // epilogue: deferred normalisation (and the scale of kept weights under
+  // dropout), natural-log LSE
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int q = qw0 + qb * 32 + l32;
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float inv = lt > 0.f ? (DROP ? p.drop.mult : 1.f) / lt : 0.f;
     if (q < N) {
       T* orow = (T*)p.o + head_off + (size_t)q * D;
 #pragma unroll
@@ -300,38 +314,53 @@ void fwd_kernel(FwdParams p) {
   }
 }
 
-template <typename T, int D, bool MASKED, int NW, int QB, int WPE>
+template <typename T, int D, bool MASKED, bool DROP, int NW, int QB, int WPE>
 static hipError_t launch_fwd_t(FwdParams p, bool causal, hipStream_t s) {
   constexpr int BR = NW * QB * 32;
   p.nqt = (p.N + BR - 1) / BR;
   dim3 grid(p.nheads * p.nqt), block(NW * 64);
   if (causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, true, MASKED, NW, QB, WPE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<T, D, true, MASKED, DROP, NW, QB, WPE>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, false, MASKED, NW, QB, WPE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<T, D, false, MASKED, DROP, NW, QB, WPE>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
 // Workgroup shapes.  A block mask needs the workgroup's rows inside one
 // 128-row mask block.  Head dim 128 keeps 32 rows per wave at 2 waves per SIMD
-// (register budget: the O accumulator alone is 64 registers).
+// (register budget: the O accumulator alone is 64 registers); so does dropout
+// at head dim 64 (the generator needs registers of its own).
 template <typename T>
-static hipError_t launch_fwd_dtype(const FwdParams& p, int d, bool causal, bool masked,
+static hipError_t launch_fwd_dtype(const FwdParams& p, int d, bool causal, bool masked, bool drop,
                                    hipStream_t s) {
   constexpr int BR64 = FA_FWD64_NW * FA_FWD64_QB * 32;
-  if (d == 64) {
-    if (masked && BR64 != 128) return launch_fwd_t<T, 64, true, 4, 1, 4>(p, causal, s);
-    if (masked) return launch_fwd_t<T, 64, true, FA_FWD64_NW, FA_FWD64_QB, FA_FWD64_WPE>(p, causal, s);
-    return launch_fwd_t<T, 64, false, FA_FWD64_NW, FA_FWD64_QB, FA_FWD64_WPE>(p, causal, s);
+  if (drop) {
+    if (d == 64)
+      return masked ? launch_fwd_t<T, 64, true, true, 4, 1, 2>(p, causal, s)
+                    : launch_fwd_t<T, 64, false, true, 4, 1, 2>(p, causal, s);
+    return masked ? launch_fwd_t<T, 128, true, true, 4, 1, 2>(p, causal, s)
+                  : launch_fwd_t<T, 128, false, true, 4, 1, 2>(p, causal, s);
   }
-  if (masked) return launch_fwd_t<T, 128, true, 4, 1, 2>(p, causal, s);
-  return launch_fwd_t<T, 128, false, 4, 1, 2>(p, causal, s);
+  if (d == 64) {
+    if (masked && BR64 != 128) return launch_fwd_t<T, 64, true, false, 4, 1, 4>(p, causal, s);
+    if (masked)
+      return launch_fwd_t<T, 64, true, false, FA_FWD64_NW, FA_FWD64_QB, FA_FWD64_WPE>(p, causal, s);
+    return launch_fwd_t<T, 64, false, false, FA_FWD64_NW, FA_FWD64_QB, FA_FWD64_WPE>(p, causal, s);
+  }
+  if (masked) return launch_fwd_t<T, 128, true, false, 4, 1, 2>(p, causal, s);
+  return launch_fwd_t<T, 128, false, false, 4, 1, 2>(p, causal, s);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, bool causal, bool masked,
                       hipStream_t s) {
-  if (dtype == 1) return launch_fwd_dtype<_Float16>(p, d, causal, masked, s);
-  return launch_fwd_dtype<__bf16>(p, d, causal, masked, s);
+  if (dtype == 1) return launch_fwd_dtype<_Float16>(p, d, causal, masked, false, s);
+  return launch_fwd_dtype<__bf16>(p, d, causal, masked, false, s);
+}
+
+hipError_t launch_fwd_drop(const FwdParams& p, int dtype, int d, bool causal, bool masked,
+                           hipStream_t s) {
+  if (dtype == 1) return launch_fwd_dtype<_Float16>(p, d, causal, masked, true, s);
+  return launch_fwd_dtype<__bf16>(p, d, causal, masked, true, s);
 }
 
 }  // namespace fa

@@ -23,6 +23,14 @@ struct MaskLists {
   int32_t mask_block;      // multiple of 128
 };
 
+// Dropout of P (see fa_dropout.hpp).  Active iff t8 > 0.
+struct DropParams {
+  uint32_t t8;      // floor(256 p): a weight is kept iff its generator byte >= t8
+  float mult;       // 256 / (256 - t8), the scale of kept weights
+  uint32_t k0, k1;  // generator key: seed mod 2^32, seed / 2^32
+  uint32_t offset;  // counter word 3
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -36,6 +44,7 @@ struct FwdParams {
   int group;      // query heads per K/V head; K/V head of query head h is h / group
   float c;        // scale * log2(e)
   MaskLists m;
+  DropParams drop;
 };
 
 struct BwdParams {
@@ -57,6 +66,7 @@ struct BwdParams {
   float c;        // scale * log2(e)
   float scale;
   MaskLists m;
+  DropParams drop;
 };
 
 struct F32Params {
@@ -81,6 +91,7 @@ struct F32Params {
   int group;
   float c;
   float scale;
+  DropParams drop;
 };
 
 // Each launcher returns hipSuccess or the launch error.
@@ -90,6 +101,13 @@ hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int d, bool causal, bool
                          hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int d, bool causal, bool masked,
                            hipStream_t s);
+// Dropout variants (p.drop.t8 > 0); same arguments.
+hipError_t launch_fwd_drop(const FwdParams& p, int dtype, int d, bool causal, bool masked,
+                           hipStream_t s);
+hipError_t launch_bwd_dq_drop(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                              hipStream_t s);
+hipError_t launch_bwd_dkdv_drop(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                                hipStream_t s);
 hipError_t launch_f32_fwd(const F32Params& p, hipStream_t s);
 hipError_t launch_f32_dq(const F32Params& p, hipStream_t s);
 hipError_t launch_f32_dkdv(const F32Params& p, hipStream_t s);

@@ -90,3 +90,57 @@ def test_zero_queries_lse_counts_window(N, causal, w, d):
     got = lse.cpu().numpy().astype(np.float64)
     for h in range(2):
         assert np.abs(got[0, h] - want).max() <= 1e-5
+
+
+# ------------------------------------------------------------------ dropout
+
+DROPOUT = [("f16", 64, 300, True, 0.5, 0, 0), ("bf16", 128, 513, False, 0.2, 0, 0),
+           ("f16", 64, 1000, True, 0.1, 200, 0), ("bf16", 64, 257, False, 0.75, 0, 0),
+           ("f16", 128, 130, True, 0.3, 0, 0), ("f32", 64, 100, True, 0.5, 0, 0),
+           ("f32", 128, 70, False, 0.25, 20, 0)]
+
+
+@pytest.mark.parametrize("dtype,d,N,causal,p,w,_", DROPOUT)
+def test_small_dropout(dtype, d, N, causal, p, w, _):
+    check_case(f"dropout-{dtype}-d{d}-N{N}-c{int(causal)}-p{p}-w{w}", 2, 2, N, d, dtype, causal,
+               window=w, dropout=(p, 0x1234_5678_9ABC_DEF0 + N, 7))
+
+
+def test_dropout_grouped_heads_block_mask():
+    N, mb = 1024, 256
+    check_case("dropout-gqa-blocks", 1, 4, N, 64, "f16", True,
+               block_mask=butterfly_block_mask(N // mb), mask_block=mb, hkv=2,
+               dropout=(0.5, 99, 3))
+
+
+def test_workload_dropout_full_size():
+    w = WORKLOADS["gpt2_medium_dropout"]
+    check_case(w.name, w.B, w.H, w.N, w.d, w.dtype, w.causal, w.scale,
+               dropout=(w.dropout, 2024, 1), heads=[(0, 0), (31, 5), (63, 15)])
+
+
+@pytest.mark.parametrize("causal,p,d", [(False, 0.5, 64), (True, 0.25, 64), (False, 0.1, 128)])
+def test_dropout_keep_mask_bit_exact(causal, p, d):
+    """Q = 0 makes every visible weight 1/count; with V[j, c] = [j mod d == c]
+    the output times count / mult is the number of kept keys j = c (mod d) of
+    row i, an exact integer to compare with the oracle's keep mask."""
+    from oracle.philox import dropout_keep
+
+    dev = torch.device("cuda:0")
+    N, H, seed, offset = 384, 2, 0xDEADBEEF12345, 11
+    say(f"[case] dropout keep mask causal={causal} p={p} d={d}")
+    q = torch.zeros((1, H, N, d), dtype=torch.float16)
+    _, k, _, _ = make_inputs(1, H, N, d, "f16")
+    v = torch.zeros((1, H, N, d), dtype=torch.float16)
+    v[:, :, torch.arange(N), torch.arange(N) % d] = 1
+    o, _ = fa_fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=0.125, dropout_p=p,
+                  seed=seed, offset=offset)
+    got = o.float().cpu().numpy().astype(np.float64)
+    count = (np.arange(N) + 1 if causal else np.full(N, N)).astype(np.float64)
+    for h in range(H):
+        keep, mult = dropout_keep(np.arange(N), np.arange(N), h, seed, offset, p)
+        if causal:
+            keep &= np.tril(np.ones((N, N), bool))
+        want = np.stack([keep[:, c::d].sum(axis=1) for c in range(d)], axis=1)
+        kept = np.rint(got[0, h] * count[:, None] / mult)
+        assert np.array_equal(kept, want), h
