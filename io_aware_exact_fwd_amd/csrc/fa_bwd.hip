@@ -106,7 +106,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) dpart += to_f32(dof[t][i]) * to_f32(of[i]);
   }
-  const float dq_d = dpart + __shfl_xor(dpart, 32, 64);
+  const float dq_d = pair_sum(dpart);
   // Under dropout dS = mult * P o (keep o dP' - D / mult), dP' = dO V^T: the
   // mask selects dP', and mult joins the scale of the finished dQ.
   const float d_sub = DROP ? dq_d / p.drop.mult : dq_d;
@@ -183,16 +183,27 @@ void bwd_dq_kernel(BwdParams p) {
       // hide keys outside the row's band (future, outside the window, past
       // the end): key of register r is k0 + g*4 + C(kb, r) with
       // C = kb*32 + (r/4)*8 + r%4; hidden iff C < lb or C > ub
-      const bool need_mask = k0 < band.lo(qw_last) || k0 + G::KT - 1 > band.hi(qw0);
-      if (need_mask) {
+      // one compare-and-select per bound, each only where some row needs it
+      // (an OR of the two compares would route every element through the
+      // scalar unit)
+      if (k0 + G::KT - 1 > band.hi(qw0)) {
         const int ub = band.hi(q) - k0 - g * 4;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
+            s[kb][r] = C > ub ? kNegInf : s[kb][r];
+          }
+      }
+      if (k0 < band.lo(qw_last)) {
         const int lb = band.lo(q) - k0 - g * 4;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
-            if (C > ub || C < lb) s[kb][r] = kNegInf;
+            s[kb][r] = C < lb ? kNegInf : s[kb][r];
           }
       }
 #pragma unroll
@@ -400,16 +411,24 @@ void bwd_dkdv_kernel(BwdParams p) {
       // causal, outside the window, past the end).  Query of register r in
       // block qb is qs0 + g*4 + C(qb, r), C = qb*32 + (r/4)*8 + r%4; hidden
       // iff C < lb or C > ub
-      const bool need_mask = qs0 < band.qlo(kw_last) || qs0 + G::QT - 1 > band.qhi(kw0);
-      if (need_mask) {
+      if (qs0 < band.qlo(kw_last)) {
         const int lb = band.qlo(key) - qs0 - g * 4;
+#pragma unroll
+        for (int qb = 0; qb < G::NQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int C = qb * 32 + (r >> 2) * 8 + (r & 3);
+            s[qb][r] = C < lb ? kNegInf : s[qb][r];
+          }
+      }
+      if (qs0 + G::QT - 1 > band.qhi(kw0)) {
         const int ub = band.qhi(key) - qs0 - g * 4;
 #pragma unroll
         for (int qb = 0; qb < G::NQB; ++qb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int C = qb * 32 + (r >> 2) * 8 + (r & 3);
-            if (C < lb || C > ub) s[qb][r] = kNegInf;
+            s[qb][r] = C > ub ? kNegInf : s[qb][r];
           }
       }
       // Under dropout (keep mask Z01, scale mult): dV = mult (Z01 o P)^T dO and

@@ -144,6 +144,34 @@ __device__ __forceinline__ float wave_max_pair(float v) {
   return vmax(v, __shfl_xor(v, 32, 64));
 }
 
+// Lanes l and l ^ 32 exchanged without LDS: v_permlane32_swap_b32 swaps the
+// upper 32 lanes of its first operand with the lower 32 lanes of its second,
+// so with both operands = v, lo holds v[l % 32] and hi holds v[l % 32 + 32] on
+// every lane.  Sum and max of the pair, identical (same operand order) in both
+// lanes.
+struct LanePair {
+  float lo, hi;
+};
+__device__ __forceinline__ LanePair lane_pair(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return LanePair{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const LanePair p = lane_pair(v);
+  return p.lo + p.hi;
+}
+__device__ __forceinline__ float pair_max(float v) {
+  const LanePair p = lane_pair(v);
+  return vmax(p.lo, p.hi);
+}
+
+// Compile-time integer as a value (selects unrolled loop bodies).
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 // Marks a rarely taken uniform branch so the compiler keeps it a branch
 // instead of executing its body on every pass with selects.
 #define FA_KEEP_BRANCH() __asm__ volatile("" ::: "memory")

@@ -193,18 +193,29 @@ void fwd_kernel(FwdParams p) {
       const bool need_mask = k0 < band.lo(qw_last) || k0 + G::KT - 1 > band.hi(qw0);
       if (need_mask) {
         FA_KEEP_BRANCH();
+        // one compare-and-select per bound on the VALU (an OR of the two
+        // compares would route every element through the scalar unit)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const int i = qw0 + qb * 32 + l32;
           const int ub = band.hi(i) - k0 - g * 4;
-          const int lb = band.lo(i) - k0 - g * 4;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
-              if (C > ub || C < lb) s[qb][kb][r] = kNegInf;
+              s[qb][kb][r] = C > ub ? kNegInf : s[qb][kb][r];
             }
+          if (p.window > 0) {
+            const int lb = band.lo(i) - k0 - g * 4;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
+                s[qb][kb][r] = C < lb ? kNegInf : s[qb][kb][r];
+              }
+          }
         }
       }
       // 3-4. per 32-key half kb: row maxima of the half, reference move if
@@ -242,7 +253,7 @@ void fwd_kernel(FwdParams p) {
           FA_KEEP_BRANCH();
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
-            const float m_new = vmax(m_ref[qb], vmax(mxs[qb], __shfl_xor(mxs[qb], 32, 64)));
+            const float m_new = vmax(m_ref[qb], pair_max(mxs[qb]));
             const float r_new = (m_new == kNegInf) ? 0.f : m_new;
             const float alpha = fast_exp2(m_ref[qb] - r_new);  // 0 while m_ref = -inf
             l_run[qb] *= alpha;
@@ -295,7 +306,7 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int q = qw0 + qb * 32 + l32;
-    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    const float lt = pair_sum(l_run[qb]);
     const float inv = lt > 0.f ? (DROP ? p.drop.mult : 1.f) / lt : 0.f;
     if (q < N) {
       T* orow = (T*)p.o + head_off + (size_t)q * D;
