@@ -30,7 +30,10 @@ namespace fa {
 // Tuning knobs: waves per SIMD of the dQ kernel, query rows per step and waves
 // per SIMD of the head-dim-64 dK/dV kernel.
 #ifndef FA_DQ_WPE
-#define FA_DQ_WPE 2
+#define FA_DQ_WPE 3
+#endif
+#ifndef FA_DQ128_WPE
+#define FA_DQ128_WPE 2
 #endif
 #ifndef FA_DKDV_QT
 #define FA_DKDV_QT 64
@@ -45,17 +48,13 @@ namespace fa {
 template <int D>
 struct DqGeom {
   static constexpr int KT = kKeyTile;
-  static constexpr int KP = D * 2 + 32;   // K tile: read by rows and by transpose
-  static constexpr int VP = D * 2 + 16;   // V tile: read by rows
-  static constexpr int KBYTES = KT * KP;
-  static constexpr int VBYTES = KT * VP;
+  static constexpr int KBYTES = KT * D * 2;  // K tile (read by rows and by transpose), swizzled
+  static constexpr int VBYTES = KT * D * 2;  // V tile (read by rows), swizzled
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int CPR = D / 8;
-  static constexpr int CPT = KT * CPR / kThreads;
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
-  // waves per SIMD: dropout at head dim 128 needs the full register file
-  static constexpr int wpe(bool drop) { return drop && D == 128 ? 1 : FA_DQ_WPE; }
+  // waves per SIMD the registers allow
+  static constexpr int wpe(bool drop) { return D == 128 ? (drop ? 1 : FA_DQ128_WPE) : FA_DQ_WPE; }
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
@@ -121,35 +120,16 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < G::NDB; ++i) acc[i] = f32x16{0};
 
-  u32x4 pk[G::CPT], pv[G::CPT];
-  auto gload = [&](int it) {
+  // K and V tiles go straight from global memory to LDS
+  auto gload = [&](int it, int stage) {
     const int k0 = tiles.pos0(it);
-#pragma unroll
-    for (int i = 0; i < G::CPT; ++i) {
-      const int ci = tid + i * kThreads;
-      const int row = ci / G::CPR, cc = ci % G::CPR;
-      const uint32_t off = (uint32_t)((k0 + row) * D * sizeof(T) + cc * 16);
-      pk[i] = buf_load16(bk, off);
-      pv[i] = buf_load16(bv, off);
-    }
-  };
-  auto lstore = [&](int stage) {
     char* ks = smem + stage * G::STAGE;
-    char* vs = ks + G::KBYTES;
-#pragma unroll
-    for (int i = 0; i < G::CPT; ++i) {
-      const int ci = tid + i * kThreads;
-      const int row = ci / G::CPR, cc = ci % G::CPR;
-      *(u32x4*)(ks + row * G::KP + cc * 16) = pk[i];
-      *(u32x4*)(vs + row * G::VP + cc * 16) = pv[i];
-    }
+    dma_tile<D, G::KT>(bk, k0, ks, wave, lane);
+    dma_tile<D, G::KT>(bv, k0, ks + G::KBYTES, wave, lane);
   };
 
   const int ntiles = tiles.count;
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
+  if (ntiles > 0) gload(0, 0);
   wait_all_memory();
   __syncthreads();
 
@@ -159,7 +139,7 @@ void bwd_dq_kernel(BwdParams p) {
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
     const bool more = it + 1 < ntiles;
-    if (more) gload(it + 1);
+    if (more) gload(it + 1, cur ^ 1);
 
     const int k0 = tiles.pos0(it);
     const char* ks = smem + cur * G::STAGE;
@@ -174,9 +154,10 @@ void bwd_dq_kernel(BwdParams p) {
         dp[kb] = f32x16{0};
 #pragma unroll
         for (int t = 0; t < G::NKS; ++t) {
-          const V8 a = lds_read8<T>(ks + (kb * 32 + l32) * G::KP + t * 32 + g * 16);
+          const int ro = swz_off<D>(kb * 32 + l32, t * 16 + g * 8);
+          const V8 a = lds_read8<T>(ks + ro);
           s[kb] = mfma32(a, qf[t], s[kb]);
-          const V8 b = lds_read8<T>(vs + (kb * 32 + l32) * G::VP + t * 32 + g * 16);
+          const V8 b = lds_read8<T>(vs + ro);
           dp[kb] = mfma32(b, dof[t], dp[kb]);
         }
       }
@@ -232,12 +213,11 @@ void bwd_dq_kernel(BwdParams p) {
       for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const char* p0 = ks + (t * 16 + g * 4 + tr_row) * G::KP + (db * 32 + tr_col) * 2;
-          const V8 a = lds_tr_operand<T>(p0, p0 + 8 * G::KP);
+          const V8 a = swz_tr_operand<T, D>(ks, t * 16 + g * 4 + tr_row, db * 32 + tr_col);
           acc[db] = mfma32(a, bs[t], acc[db]);
         }
     }
-    if (more) lstore(cur ^ 1);
+    wait_all_memory();  // this thread's copies into the next stage have landed
     __syncthreads();
   }
 
@@ -262,11 +242,8 @@ void bwd_dq_kernel(BwdParams p) {
 template <int D>
 struct DkvGeom {
   static constexpr int QT = FA_DKDV_QT;     // queries per step
-  static constexpr int P = D * 2 + 32;      // Q / dO tile pitch: rows and transpose
-  static constexpr int TBYTES = QT * P;
+  static constexpr int TBYTES = QT * D * 2;  // Q / dO tile, swizzled (no padding)
   static constexpr int STAGE = 2 * TBYTES + 2 * QT * 4;  // Q, dO, lse2, D
-  static constexpr int CPR = D / 8;
-  static constexpr int CPT = QT * CPR / kThreads;
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
   static constexpr int NQB = QT / 32;       // 32-query blocks per step
@@ -323,54 +300,41 @@ void bwd_dkdv_kernel(BwdParams p) {
     dva[i] = f32x16{0};
   }
 
-  u32x4 pq[G::CPT], pd[G::CPT];
+  // Q and dO tiles go straight from global memory to LDS (no registers, no
+  // store instructions); LSE and D through registers.
   float plse = 0.f, pdv = 0.f;
-  auto gload = [&](int it) {
+  int pqq = 0;
+  auto gload = [&](int it, int stage) {
     const int r = it / nqt;
     const int qs = tiles.pos0(it - r * nqt);
     const size_t qh = (size_t)kvh * p.group + r;  // query head
     const Buf bq = make_buf((const T*)p.q + qh * N * D, head_bytes);
     const Buf bdo = make_buf((const T*)p.dout + qh * N * D, head_bytes);
-#pragma unroll
-    for (int i = 0; i < G::CPT; ++i) {
-      const int ci = tid + i * kThreads;
-      const int row = ci / G::CPR, cc = ci % G::CPR;
-      const uint32_t off = (uint32_t)((qs + row) * D * sizeof(T) + cc * 16);
-      pq[i] = buf_load16(bq, off);
-      pd[i] = buf_load16(bdo, off);
-    }
+    char* qs_ = smem + stage * G::STAGE;
+    dma_tile<D, G::QT>(bq, qs, qs_, wave, lane);
+    dma_tile<D, G::QT>(bdo, qs, qs_ + G::TBYTES, wave, lane);
+    // raw values now (rows clamped into the sequence), converted when stored,
+    // so that nothing waits for these loads before the tile's work
     if (tid < G::QT) {
-      const int qq = qs + tid;
-      plse = __builtin_huge_valf();
-      pdv = 0.f;
-      if (qq < N) {
-        const float l = p.lse[qh * N + qq];
-        if (l != kNegInf) plse = l * kLog2e;
-        pdv = p.dvec[qh * N + qq];
-        if (DROP) pdv /= p.drop.mult;  // see the dS step
-      }
+      pqq = qs + tid;
+      const size_t row = qh * N + min(pqq, N - 1);
+      plse = p.lse[row];
+      pdv = p.dvec[row];
     }
   };
   auto lstore = [&](int stage) {
-    char* qs = smem + stage * G::STAGE;
-    char* ds = qs + G::TBYTES;
-    float* ls = (float*)(ds + G::TBYTES);
-#pragma unroll
-    for (int i = 0; i < G::CPT; ++i) {
-      const int ci = tid + i * kThreads;
-      const int row = ci / G::CPR, cc = ci % G::CPR;
-      *(u32x4*)(qs + row * G::P + cc * 16) = pq[i];
-      *(u32x4*)(ds + row * G::P + cc * 16) = pd[i];
-    }
+    float* ls = (float*)(smem + stage * G::STAGE + 2 * G::TBYTES);
     if (tid < G::QT) {
-      ls[tid] = plse;
-      ls[G::QT + tid] = pdv;
+      // rows past the end or with no visible key: P = 0 (LSE2 = +inf)
+      const bool live = pqq < N && plse != kNegInf;
+      ls[tid] = live ? plse * kLog2e : __builtin_huge_valf();
+      ls[G::QT + tid] = pqq < N ? (DROP ? pdv / p.drop.mult : pdv) : 0.f;  // D / mult: see the dS step
     }
   };
 
   const int ntiles = nqt * p.group;
   if (ntiles > 0) {
-    gload(0);
+    gload(0, 0);
     lstore(0);
   }
   wait_all_memory();
@@ -382,7 +346,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
     const bool more = it + 1 < ntiles;
-    if (more) gload(it + 1);
+    if (more) gload(it + 1, cur ^ 1);
 
     const int qs0 = tiles.pos0(it % nqt);
     const int qh = kvh * p.group + it / nqt;  // query head of this step
@@ -401,9 +365,10 @@ void bwd_dkdv_kernel(BwdParams p) {
         dp[qb] = f32x16{0};
 #pragma unroll
         for (int t = 0; t < G::NKS; ++t) {
-          const V8 a = lds_read8<T>(qsm + (qb * 32 + l32) * G::P + t * 32 + g * 16);
+          const int ro = swz_off<D>(qb * 32 + l32, t * 16 + g * 8);
+          const V8 a = lds_read8<T>(qsm + ro);
           s[qb] = mfma32(a, kf[t], s[qb]);
-          const V8 b = lds_read8<T>(dsm + (qb * 32 + l32) * G::P + t * 32 + g * 16);
+          const V8 b = lds_read8<T>(dsm + ro);
           dp[qb] = mfma32(b, vf[t], dp[qb]);
         }
       }
@@ -469,15 +434,15 @@ void bwd_dkdv_kernel(BwdParams p) {
                                dp[qb][r0 + 4], dp[qb][r0 + 5], dp[qb][r0 + 6], dp[qb][r0 + 7]);
 #pragma unroll
         for (int db = 0; db < G::NDB; ++db) {
-          const int off = (t * 16 + g * 4 + tr_row) * G::P + (db * 32 + tr_col) * 2;
-          const V8 bdo_ = lds_tr_operand<T>(dsm + off, dsm + off + 8 * G::P);
+          const V8 bdo_ = swz_tr_operand<T, D>(dsm, t * 16 + g * 4 + tr_row, db * 32 + tr_col);
           dva[db] = mfma32(ap, bdo_, dva[db]);
-          const V8 bq_ = lds_tr_operand<T>(qsm + off, qsm + off + 8 * G::P);
+          const V8 bq_ = swz_tr_operand<T, D>(qsm, t * 16 + g * 4 + tr_row, db * 32 + tr_col);
           dka[db] = mfma32(ad, bq_, dka[db]);
         }
       }
     }
     if (more) lstore(cur ^ 1);
+    wait_all_memory();  // this thread's copies into the next stage have landed
     __syncthreads();
   }
 

@@ -124,6 +124,72 @@ __device__ __forceinline__ u32x4 buf_load16(const Buf& b, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b.r, byte_off, 0, 0));
 }
 
+// ---- swizzled LDS tiles filled by direct global -> LDS copies --------------
+// buffer_load_dwordx4 ... lds writes lane i's 16 bytes at (M0 base) + 16 i: one
+// 1 KiB block of LDS per wave and instruction, whatever global offsets the
+// lanes read; lanes whose offset is past the buffer's range write zeros
+// (both confirmed on the device).  A tile of ROWS x D 16-bit elements is kept
+// row-major in 16-byte chunks, chunk c of row r at position
+// r * D/8 + (c ^ swz(r)).  The XOR pattern is a linear map of the four low row
+// bits chosen (by exhaustive search over all such maps) so that both access
+// patterns of the kernels are free of bank conflicts with 32 or with 64
+// four-byte banks: 16 lanes reading 16 bytes each from 16 consecutive rows at
+// one chunk (MFMA operands read by rows), and 32 lanes reading 8 bytes each
+// from 4 rows x 64 bytes (transpose reads).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 64) {  // 8 chunks per row: bits r1, r0^r2, r0^r1^r3
+    return ((r >> 1) & 1) | (((r ^ (r >> 2)) & 1) << 1) | (((r ^ (r >> 1) ^ (r >> 3)) & 1) << 2);
+  } else {                   // 16 chunks per row: bits r0, r1, r0^r2, r1^r3
+    return (r & 3) | (((r ^ (r >> 2)) & 1) << 2) | ((((r >> 1) ^ (r >> 3)) & 1) << 3);
+  }
+}
+// byte offset of element column `col` of row r in a swizzled tile
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int col) {
+  return (r * (D / 8) + ((col >> 3) ^ swz<D>(r))) * 16 + (col & 7) * 2;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte-per-lane copy into the 1 KiB LDS block at `block`.  Written as
+// inline assembly on purpose: the compiler's wait-count pass treats an LDS DMA
+// it knows about as a store to all of LDS and waits for it before every later
+// LDS read, including reads of the other buffer stage, which would stall each
+// iteration until its prefetch lands.  The caller therefore waits for the
+// copies itself (wait_all_memory) before the barrier that publishes them.
+__device__ __forceinline__ void dma16(const Buf& b, uint32_t byte_off, char* block) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)block;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(byte_off), "s"(b.r)
+               : "memory", "m0");
+}
+
+// Copy rows [r0, r0 + ROWS) of a row-major (rows x D) 16-bit tensor held by
+// buffer b into the swizzled tile at `tile` (256 threads; each issues
+// ROWS*D/2048 copies, copy n of wave w filling 1 KiB block 4n + w).
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_tile(const Buf& b, int r0, char* tile, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int NI = ROWS * CPR / 256;
+  static_assert(ROWS * CPR % 256 == 0, "tile must be a whole number of 1 KiB blocks per wave");
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int P = (n * 4 + wave) * 64 + lane;
+    const int r = P / CPR, pc = P % CPR;
+    const uint32_t off = (uint32_t)(((r0 + r) * D + ((pc ^ swz<D>(r)) << 3)) * 2);
+    dma16(b, off, tile + (n * 4 + wave) * 1024);
+  }
+}
+
+// A/B operand of 8 x 16-bit from two transpose reads of a swizzled tile:
+// rows r and r + 8, element columns col .. col + 3 per lane (see header).
+template <typename T, int D>
+__device__ __forceinline__ typename Vec8<T>::type swz_tr_operand(const char* tile, int r, int col) {
+  return lds_tr_operand<T>(tile + swz_off<D>(r, col), tile + swz_off<D>(r + 8, col));
+}
+
 // ---- workgroup -> work-item mapping -----------------------------------------
 // Workgroups are handed to the 8 XCDs round-robin by linear id.  Remap so that
 // each XCD receives one contiguous range of the logical order (head-major):

@@ -60,17 +60,12 @@ constexpr float kRescaleTau = 8.0f;
 template <int D, int NW>
 struct FwdGeom {
   static constexpr int KT = kKeyTile;           // keys per tile
-  static constexpr int KP = D * 2 + 16;         // K tile pitch (bytes)
-  static constexpr int VP = D * 2 + 32;         // V tile pitch (bytes)
-  static constexpr int KBYTES = KT * KP;
-  static constexpr int VBYTES = KT * VP;
+  static constexpr int KBYTES = KT * D * 2;    // K tile (read by rows), swizzled
+  static constexpr int VBYTES = KT * D * 2;    // V tile (read by transpose), swizzled
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int THREADS = NW * 64;
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int CPT = KT * CPR / THREADS;  // chunks per thread per tensor
   static constexpr int NDB = D / 32;            // 32-wide blocks of the head dim
   static constexpr int NKS = D / 16;            // k-steps of the QK^T product
-  static_assert(KT * CPR % THREADS == 0, "tile must split evenly over threads");
+  static_assert(NW == 4, "the tile copies assume 4 waves");
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP, int NW, int QB, int WPE>
@@ -129,42 +124,23 @@ void fwd_kernel(FwdParams p) {
     l_run[qb] = 0.f;
   }
 
-  u32x4 pk[G::CPT], pv[G::CPT];
-  auto gload = [&](int it) {
+  // K and V tiles go straight from global memory to LDS
+  auto gload = [&](int it, int stage) {
     const int k0 = tiles.pos0(it);
-#pragma unroll
-    for (int i = 0; i < G::CPT; ++i) {
-      const int ci = tid + i * G::THREADS;
-      const int row = ci / G::CPR, cc = ci % G::CPR;
-      const uint32_t off = (uint32_t)((k0 + row) * D * sizeof(T) + cc * 16);
-      pk[i] = buf_load16(bk, off);
-      pv[i] = buf_load16(bv, off);
-    }
-  };
-  auto lstore = [&](int stage) {
     char* ks = smem + stage * G::STAGE;
-    char* vs = ks + G::KBYTES;
-#pragma unroll
-    for (int i = 0; i < G::CPT; ++i) {
-      const int ci = tid + i * G::THREADS;
-      const int row = ci / G::CPR, cc = ci % G::CPR;
-      *(u32x4*)(ks + row * G::KP + cc * 16) = pk[i];
-      *(u32x4*)(vs + row * G::VP + cc * 16) = pv[i];
-    }
+    dma_tile<D, G::KT>(bk, k0, ks, wave, lane);
+    dma_tile<D, G::KT>(bv, k0, ks + G::KBYTES, wave, lane);
   };
 
   const int ntiles = tiles.count;
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
+  if (ntiles > 0) gload(0, 0);
   wait_all_memory();
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
     const bool more = it + 1 < ntiles;
-    if (more) gload(it + 1);
+    if (more) gload(it + 1, cur ^ 1);
 
     const int k0 = tiles.pos0(it);
     const char* ks = smem + cur * G::STAGE;
@@ -182,7 +158,7 @@ void fwd_kernel(FwdParams p) {
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{0};
 #pragma unroll
         for (int t = 0; t < G::NKS; ++t) {
-          const V8 a = lds_read8<T>(ks + (kb * 32 + l32) * G::KP + t * 32 + g * 16);
+          const V8 a = lds_read8<T>(ks + swz_off<D>(kb * 32 + l32, t * 16 + g * 8));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][t], s[qb][kb]);
         }
@@ -289,15 +265,14 @@ void fwd_kernel(FwdParams p) {
           }
 #pragma unroll
           for (int db = 0; db < G::NDB; ++db) {
-            const char* p0 = vs + (t * 16 + g * 4 + tr_row) * G::VP + (db * 32 + tr_col) * 2;
-            const V8 a = lds_tr_operand<T>(p0, p0 + 8 * G::VP);
+            const V8 a = swz_tr_operand<T, D>(vs, t * 16 + g * 4 + tr_row, db * 32 + tr_col);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(a, bp[qb], o[qb][db]);
           }
         }
       }
     }
-    if (more) lstore(cur ^ 1);
+    wait_all_memory();  // this thread's copies into the next stage have landed
     __syncthreads();
   }
 
