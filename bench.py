@@ -169,6 +169,59 @@ def summarize_pmc(path):
         print(f"{k:60s} dispatches={n} per-dispatch: {vals}")
 
 
+def _counter_means(path, counter):
+    """Per-kernel mean of one counter (KiB per dispatch) from a rocprofv3
+    counter_collection.csv."""
+    import collections
+    import csv
+
+    tot = collections.defaultdict(float)
+    disp = collections.defaultdict(set)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        tot[r["Kernel_Name"]] += float(r["Counter_Value"])
+        disp[r["Kernel_Name"]].add(r["Dispatch_Id"])
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def record_traffic(fetch_csv, write_csv, cfetch_csv, cwrite_csv, workload):
+    """Calibrate FETCH_SIZE / WRITE_SIZE against the copy probe (512 MiB read
+    and written per launch), scale the attention kernels' counters to HBM
+    bytes per launch, write profiles/traffic.json with the digest of the
+    kernel sources, and print a summary."""
+    copy_kib = 512 * 1024
+    cf = [v for k, v in _counter_means(cfetch_csv, "FETCH_SIZE").items() if "elementwise" in k]
+    cw = [v for k, v in _counter_means(cwrite_csv, "WRITE_SIZE").items() if "elementwise" in k]
+    if not cf or not cw:
+        raise SystemExit("copy-probe counters not found")
+    fs, ws = copy_kib / max(cf), copy_kib / max(cw)
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    from io_aware_exact_fwd_amd.workloads import WORKLOADS
+
+    work = kernel_work(WORKLOADS[workload])
+    rec = {"source_sha256": source_digest(), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+           "calibration": f"plain elementwise copy (torch.mul(x, 1.0, out=y)) of 512 MiB fp16: "
+                          f"FETCH_SIZE {max(cf):.0f} KiB per launch for {copy_kib} KiB read, "
+                          f"WRITE_SIZE {max(cw):.0f} KiB for {copy_kib} KiB written",
+           "kernels": {}}
+    print(f"# calibration: fetch scale {fs:.4f}, write scale {ws:.4f}")
+    for key, tag in (("fwd", "fwd_kernel"), ("dq", "bwd_dq_kernel"), ("dkdv", "bwd_dkdv_kernel")):
+        fk = [v for k, v in fetch.items() if tag in k and "f32" not in k]
+        wk = [v for k, v in write.items() if tag in k and "f32" not in k]
+        if not fk or not wk:
+            continue
+        b = int(round((fs * fk[0] + ws * wk[0]) * 1024))
+        rec["kernels"][f"{key}/{workload}"] = {"fetch_kib_raw": round(fk[0]), "write_kib_raw": round(wk[0]),
+                                              "bytes_per_launch": b}
+        print(f"#   {key:5s} FETCH {fk[0]:10.0f} KiB  WRITE {wk[0]:10.0f} KiB  -> {b / 1e6:8.1f} MB per launch "
+              f"(compulsory {work[key]['bytes'] / 1e6:.1f} MB)")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"# wrote {os.path.relpath(TRAFFIC_FILE, ROOT)}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,7 +236,14 @@ def main():
                     help="print a summary of a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--summarize-pmc", metavar="CSV",
                     help="print per-kernel means of a rocprofv3 counter_collection.csv and exit")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="turn four counter_collection.csv files (FETCH_SIZE and WRITE_SIZE of "
+                         "the bench, then of --copy-probe) into profiles/traffic.json and exit")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        record_traffic(*args.record_traffic, args.workload)
+        return
 
     if args.summarize_stats:
         summarize_stats(args.summarize_stats)
