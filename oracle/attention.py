@@ -58,6 +58,14 @@ Z = Z01 / (1 - p'),
 Fully masked rows (possible only with a general block mask): O_i = 0,
 LSE_i = -inf, and the row contributes nothing to any gradient.
 
+Queries at an offset (the decode shape of the survey's next rows: a few
+queries against a long key sequence, as in incremental decoding after the
+[ldl] sections 4-6 discussion of grouped heads): query row r sits at position
+q_offset + r of the key sequence, and every visibility rule above uses that
+position (causal: key j <= q_offset + r; window: |q_offset + r - j| < W).
+q_offset = 0 with as many queries as keys is the square case; decoding the
+last n_q positions of N keys is q_offset = N - n_q.
+
 Memory: rows are processed in chunks, and each chunk only touches the key
 columns that can be visible to some row of the chunk (a causal prefix, or the
 kept key blocks of the chunk's query blocks).  Columns left out are exactly
@@ -159,9 +167,12 @@ class _Spec:
     """Mask and dropout settings shared by the per-head routines."""
 
     def __init__(self, scale, causal, block_mask, mask_block, window, dropout_p, seed,
-                 offset, row_chunk):
+                 offset, row_chunk, q_offset=0):
         if window < 0:
             raise ValueError("window must be >= 0")
+        if q_offset < 0:
+            raise ValueError("q_offset must be >= 0")
+        self.q_offset = q_offset
         if not 0.0 <= dropout_p < 1.0:
             raise ValueError("dropout_p must be in [0, 1)")
         self.scale, self.causal = scale, causal
@@ -173,20 +184,22 @@ class _Spec:
         return _row_chunks(n, self.causal, self.block_mask, self.mask_block, self.row_chunk)
 
     def columns(self, r0, r1, n):
-        return _candidate_columns(r0, r1, n, self.causal, self.block_mask, self.mask_block,
-                                  self.window)
+        """Candidate key columns of query rows [r0, r1) (positions shifted by q_offset)."""
+        return _candidate_columns(r0 + self.q_offset, r1 + self.q_offset, n, self.causal,
+                                  self.block_mask, self.mask_block, self.window)
 
     def scores(self, q, k, rows, cols):
         s = self.scale * (q[rows] @ k[cols].T)
-        vis = visibility(rows, cols, self.causal, self.block_mask, self.mask_block,
-                         self.window)
+        vis = visibility(rows + self.q_offset, cols, self.causal, self.block_mask,
+                         self.mask_block, self.window)
         return np.where(vis, s, -np.inf)
 
     def drop(self, rows, cols, head):
         """Dropout multiplier Z for the (rows x cols) block, or None if p = 0."""
         if self.dropout_p == 0.0:
             return None
-        keep, mult = dropout_keep(rows, cols, head, self.seed, self.offset, self.dropout_p)
+        keep, mult = dropout_keep(rows + self.q_offset, cols, head, self.seed, self.offset,
+                                  self.dropout_p)
         return keep * mult
 
 
@@ -262,7 +275,7 @@ def _group(q, k, v):
 
 def attention_forward(q, k, v, scale, causal=False, block_mask=None, mask_block=128,
                       heads=None, row_chunk=None, window=0, dropout_p=0.0, seed=0,
-                      offset=0):
+                      offset=0, q_offset=0):
     """O (float64) and natural-log LSE (float64) of the definition above.
 
     q: (B, H, N, d); k, v: (B, H_kv, N, d) with H_kv dividing H; or all (N, d).
@@ -272,11 +285,13 @@ def attention_forward(q, k, v, scale, causal=False, block_mask=None, mask_block=
     window: 0 (none) or W > 0, keys with |i - j| >= W hidden.
     dropout_p, seed, offset: dropout of P as in ``oracle.philox.dropout_keep``
            with head index b * H + h.
+    q_offset: position of query row 0 in the key sequence (decode: N_k - N_q);
+           q may then have fewer rows than k and v.
     """
     q, k, v = _as_bhnd(q), _as_bhnd(k), _as_bhnd(v)
     g = _group(q, k, v)
     spec = _Spec(scale, causal, block_mask, mask_block, window, dropout_p, seed, offset,
-                 row_chunk)
+                 row_chunk, q_offset)
     outs, lses = [], []
     for b, h in _select(q, heads):
         o, lse = _forward_head(q[b, h], k[b, h // g], v[b, h // g], spec, b * q.shape[1] + h)
