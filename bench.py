@@ -87,6 +87,54 @@ def kernel_work(w):
     }
 
 
+def decode_bench(w, args, dev):
+    """Decode workload: n_q queries per head against N keys.  Bound by HBM:
+    its algorithmic bytes are K and V once plus Q, O and LSE.  Prints one
+    JSON line like the headline path."""
+    import torch
+
+    from io_aware_exact_fwd_amd import fa_fwd_decode
+    from io_aware_exact_fwd_amd.workloads import make_decode_inputs
+
+    q, k, v = (t.to(dev) for t in make_decode_inputs(w.B, w.H, w.N, w.d, w.nq, w.dtype,
+                                                      hkv=w.H_kv))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.nq), dtype=torch.float32, device=dev)
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} H_kv={w.H_kv} N={w.N} n_q={w.nq} d={w.d} "
+        f"{w.dtype} causal={w.causal}; warmup {args.warmup}, steps {args.steps}")
+    for _ in range(args.warmup):
+        fa_fwd_decode(q, k, v, causal=w.causal, scale=w.scale, window=w.window, out=o, lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        fa_fwd_decode(q, k, v, causal=w.causal, scale=w.scale, window=w.window, out=o, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms_ev = e0.elapsed_time(e1) / args.steps
+    e = 2  # bf16 / fp16
+    nbytes = 2 * w.B * w.H_kv * w.N * w.d * e + 2 * w.B * w.H * w.nq * w.d * e + w.B * w.H * w.nq * 4
+    gbs = nbytes / (ms_step / 1e3) / 1e9
+    log(f"[bench] decode {ms_step * 1e3:.1f} us per call ({ms_ev * 1e3:.1f} us by events), "
+        f"{nbytes / 1e6:.1f} MB -> {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of HBM peak)")
+    out = {
+        "metric": f"decode attention forward HBM GB/s ({w.name})", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "n_q": w.nq,
+                   "d": w.d, "dtype": w.dtype, "causal": w.causal, "scale": w.scale},
+        "roofline": {"kernel": "decode", "bound": "hbm", "achieved": round(ms_ev and nbytes / (ms_ev / 1e3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (ms_ev / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def roofline(name, work, ms):
     """Roofline entry for one kernel: bound = the larger of its compulsory-byte
     time at peak HBM and its FLOP time at peak matrix rate."""
@@ -278,6 +326,9 @@ def main():
         log(f"[bench] copy probe: 5 launches, each reads {2 * n} B and writes {2 * n} B")
         return
     w = WORKLOADS[args.workload]
+    if w.nq:
+        decode_bench(w, args, dev)
+        return
     inputs = make_inputs(w.B, w.H, w.N, w.d, w.dtype)
     q, k, v, do = (t.to(dev) for t in inputs)
     bm = w.block_mask()

@@ -159,6 +159,27 @@ int fa_bwd_dkdv(const fa_problem* p, const void* q, const void* k, const void* v
 int fa_mask_compile(const uint8_t* mask, int32_t nb, int32_t* row_ptr, int32_t* col_idx,
                     int32_t* col_ptr, int32_t* row_idx, void* stream);
 
+/* Decode-shaped forward (a few queries against many keys, the survey's
+ * decode workload next to grouped heads).  q and o are (B, H, n_q, d) in the
+ * problem's dtype, lse is float32 (B, H, n_q); k and v are (B, H_kv, N, d) with
+ * N = p->N.  Query i of each head sits at position N - n_q + i of the key
+ * sequence, and causal / window visibility use that position (with causal and
+ * n_q = 1 the query sees every key).  The result is the attention defined at
+ * the top of this file restricted to those rows.  Inside, the key range is cut
+ * into splits computed by separate workgroups, each leaving the running
+ * maximum / running sum result of its keys (O_s normalised, LSE_s), and a
+ * second kernel merges them with LSE = log sum_s exp(LSE_s),
+ * O = sum_s exp(LSE_s - LSE) O_s -- the merge step of the online softmax
+ * ("A recorrencia do softmax online", marketmaker.cc article).
+ * Requirements: 1 <= n_q <= N; dtype FA_F16 or FA_BF16 (FA_F32 ->
+ * FA_ERR_UNSUPPORTED); block_mask == NULL and dropout_p == 0 (else
+ * FA_ERR_UNSUPPORTED); the other fields as for fa_fwd.  workspace: at least
+ * fa_decode_workspace_size(p, n_q) bytes (float32 partial results; may be NULL
+ * when that is 0).  The split count depends only on the problem. */
+size_t fa_decode_workspace_size(const fa_problem* p, int32_t n_q);
+int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k, const void* v,
+                  void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
 /* Static string for a status code. */
 const char* fa_status_string(int status);
 

@@ -7,6 +7,7 @@ arguments to its C ABI (``include/fa.h``) and never computes on the CPU.
     o, lse = fa_fwd(q, k, v, causal=True, scale=0.125)
     dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=True, scale=0.125)
     o = attention(q, k, v, causal=True)        # differentiable wrapper
+    o, lse = fa_fwd_decode(q_last, k, v)       # last n_q positions vs N keys
 """
 
 from .binding import (  # noqa: F401
@@ -16,9 +17,11 @@ from .binding import (  # noqa: F401
     FaError,
     bwd_workspace,
     fa_bwd,
+    fa_decode_workspace_size,
     fa_bwd_dkdv,
     fa_bwd_dq,
     fa_fwd,
+    fa_fwd_decode,
     fa_mask_compile,
     fa_status_string,
     fa_version,

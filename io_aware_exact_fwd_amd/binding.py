@@ -6,7 +6,8 @@ is missing, or a tensor is not a contiguous GPU tensor of a supported type,
 the call raises -- there is no CPU or PyTorch fallback.
 
 Names follow the C ABI: ``fa_fwd``, ``fa_bwd``, ``fa_mask_compile``,
-``fa_workspace_size``, ``fa_status_string``, ``fa_version``.
+``fa_workspace_size``, ``fa_fwd_decode``, ``fa_decode_workspace_size``,
+``fa_status_string``, ``fa_version``.
 """
 
 from __future__ import annotations
@@ -22,7 +23,8 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = 0, -1, -2, -3, -4
 
 EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv",
-           "fa_mask_compile", "fa_status_string", "fa_version")
+           "fa_mask_compile", "fa_decode_workspace_size", "fa_fwd_decode",
+           "fa_status_string", "fa_version")
 
 
 class FaProblem(ctypes.Structure):
@@ -78,6 +80,10 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_dkdv.restype = ctypes.c_int
     L.fa_mask_compile.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     L.fa_mask_compile.restype = ctypes.c_int
+    L.fa_decode_workspace_size.argtypes = [pp, i32]
+    L.fa_decode_workspace_size.restype = sz
+    L.fa_fwd_decode.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.fa_fwd_decode.restype = ctypes.c_int
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -186,6 +192,40 @@ def fa_fwd(q, k, v, causal=False, scale=None, block_mask=None, mask_block=128, o
                       lse_t.data_ptr(), ws.data_ptr(), ws_n, _stream(q))
     if st != FA_OK:
         raise FaError("fa_fwd", st)
+    return o, lse_t
+
+
+def fa_decode_workspace_size(p: FaProblem, n_q: int) -> int:
+    return int(lib().fa_decode_workspace_size(ctypes.byref(p), int(n_q)))
+
+
+def fa_fwd_decode(q, k, v, causal=True, scale=None, window=0, out=None, lse=None):
+    """Decode-shaped forward: q (B, H, n_q, d) holds the LAST n_q positions of
+    a sequence whose N keys and values are k, v (B, H_kv, N, d).  Returns
+    (O like q, LSE float32 (B, H, n_q), natural log).  The keys are split over
+    workgroups and the partial results merged inside the library."""
+    import torch
+
+    _check_tensors(q)
+    _check_tensors(k, k, v)
+    if q.dim() != 4 or k.dim() != 4 or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("q must be (B, H, n_q, d) and k, v (B, H_kv, N, d)")
+    if k.shape[1] == 0 or q.shape[1] % k.shape[1]:
+        raise ValueError("the K/V head count must divide the query head count")
+    if k.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    B, H, n_q, d = q.shape
+    p = make_problem(k, causal, scale, None, 128, k, window)
+    p.H = H  # query heads; N and H_kv come from k
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensors(q, o)
+    ws_n = fa_decode_workspace_size(p, n_q)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    st = lib().fa_fwd_decode(ctypes.byref(p), n_q, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             o.data_ptr(), lse_t.data_ptr(), ws.data_ptr(), ws_n, _stream(q))
+    if st != FA_OK:
+        raise FaError("fa_fwd_decode", st)
     return o, lse_t
 
 

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -171,6 +171,94 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
   const hipError_t e = f.drop.t8 ? fa::launch_fwd_drop(f, p->dtype, p->d, p->causal != 0, masked, s)
                                  : fa::launch_fwd(f, p->dtype, p->d, p->causal != 0, masked, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Decode geometry: rows per K/V head, row blocks, key tiles and splits.  The
+// split count aims at >= 2048 workgroups (8 per CU) and depends only on the
+// problem, so the workspace size is known before any launch.
+struct DecodeShape {
+  int rows, nrb, nkv, tile0, ntiles, tps, nsplit;
+};
+
+DecodeShape decode_shape(const fa_problem* p, int n_q) {
+  DecodeShape g;
+  const int group = group_of(p);
+  g.rows = group * n_q;
+  g.nrb = (g.rows + 127) / 128;
+  g.nkv = p->B * kv_heads(p);
+  // keys some row sees: the rows sit at positions N - n_q .. N - 1
+  const int lo = p->window > 0 ? (p->N - n_q - p->window + 1 > 0 ? p->N - n_q - p->window + 1 : 0) : 0;
+  g.tile0 = lo / 64;
+  g.ntiles = (p->N - 1) / 64 - g.tile0 + 1;
+  const int64_t wgs = (int64_t)g.nkv * g.nrb;
+  int want = (int)((2048 + wgs - 1) / wgs);
+  if (want < 1) want = 1;
+  if (want > g.ntiles) want = g.ntiles;
+  g.tps = (g.ntiles + want - 1) / want;
+  g.nsplit = (g.ntiles + g.tps - 1) / g.tps;
+  return g;
+}
+
+int check_decode(const fa_problem* p, int32_t n_q) {
+  int st = check_problem(p);
+  if (st != FA_OK) return st;
+  if (n_q < 1 || n_q > p->N) return FA_ERR_ARG;
+  if (p->dtype == FA_F32 || p->block_mask != nullptr || p->dropout_p != 0.f)
+    return FA_ERR_UNSUPPORTED;
+  if ((int64_t)p->B * p->H * n_q > (int64_t)INT32_MAX / 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_decode_workspace_size(const fa_problem* p, int32_t n_q) {
+  if (check_decode(p, n_q) != FA_OK) return 0;
+  const DecodeShape g = decode_shape(p, n_q);
+  if (g.nsplit == 1) return 0;
+  const size_t rows = (size_t)p->B * p->H * n_q;
+  return align_up(rows * g.nsplit * p->d * sizeof(float)) + align_up(rows * g.nsplit * sizeof(float));
+}
+
+int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k, const void* v,
+                  void* o, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_decode(p, n_q);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
+    return FA_ERR_ARG;
+  const size_t need = fa_decode_workspace_size(p, n_q);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
+  const DecodeShape g = decode_shape(p, n_q);
+  fa::DecParams d;
+  d.q = q;
+  d.k = k;
+  d.v = v;
+  d.o = o;
+  d.lse = lse;
+  const size_t rows = (size_t)p->B * p->H * n_q;
+  d.part_o = g.nsplit > 1 ? (float*)workspace : nullptr;
+  d.part_lse = g.nsplit > 1 ? (float*)((char*)workspace + align_up(rows * g.nsplit * p->d * sizeof(float)))
+                            : nullptr;
+  d.N = p->N;
+  d.nq = n_q;
+  d.rows = g.rows;
+  d.nrb = g.nrb;
+  d.nkv = g.nkv;
+  d.nsplit = g.nsplit;
+  d.tiles_per_split = g.tps;
+  d.tile0 = g.tile0;
+  d.ntiles = g.ntiles;
+  d.window = p->window;
+  d.c = p->scale * fa::kLog2e;
+  return fa::launch_decode(d, p->dtype, p->d, p->causal != 0, (hipStream_t)stream) == hipSuccess
+             ? FA_OK
+             : FA_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -69,6 +69,29 @@ struct BwdParams {
   DropParams drop;
 };
 
+// Decode-shaped forward (fa_decode.hip): n_q queries per head at positions
+// N - n_q .. N - 1, keys split over workgroups, partials merged.
+struct DecParams {
+  const void* q;     // (B, H, n_q, d)
+  const void* k;     // (B, H_kv, N, d)
+  const void* v;
+  void* o;           // (B, H, n_q, d)
+  float* lse;        // (B, H, n_q)
+  float* part_o;     // [B*H*n_q][nsplit][d] float32 partial outputs (nsplit > 1)
+  float* part_lse;   // [B*H*n_q][nsplit]
+  int N;             // keys
+  int nq;            // queries per head
+  int rows;          // rows per K/V head: group * n_q
+  int nrb;           // row blocks of 128 per K/V head
+  int nkv;           // B * H_kv
+  int nsplit;        // key splits
+  int tiles_per_split;
+  int tile0;         // first 64-key tile any row sees
+  int ntiles;        // tiles from tile0 through the last one any row sees
+  int window;        // 0: none; W > 0: |pos - j| < W
+  float c;           // scale * log2(e)
+};
+
 struct F32Params {
   const float* q;
   const float* k;
@@ -108,6 +131,7 @@ hipError_t launch_bwd_dq_drop(const BwdParams& p, int dtype, int d, bool causal,
                               hipStream_t s);
 hipError_t launch_bwd_dkdv_drop(const BwdParams& p, int dtype, int d, bool causal, bool masked,
                                 hipStream_t s);
+hipError_t launch_decode(const DecParams& p, int dtype, int d, bool causal, hipStream_t s);
 hipError_t launch_f32_fwd(const F32Params& p, hipStream_t s);
 hipError_t launch_f32_dq(const F32Params& p, hipStream_t s);
 hipError_t launch_f32_dkdv(const F32Params& p, hipStream_t s);

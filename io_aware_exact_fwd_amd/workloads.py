@@ -29,10 +29,19 @@ Extensions of the method (sliding window, grouped K/V heads, dropout):
                 70B (64 query heads sharing 8 K/V heads, head dim 128)
   gpt2_medium_dropout  gpt2_medium with attention dropout p = 0.1
 
+Decode shape (a few new queries against a long key sequence, the survey's
+workload next to grouped heads; forward only):
+
+  decode_gqa    B=16 H=64 H_kv=8 N=8192 d=128 bf16, n_q=1 (the last position),
+                causal: one token of a batch of 16 sequences with the
+                grouped-head layout above and an 8K-token context
+
 Input recipe: torch.Generator('cpu').manual_seed(1000 + N); Q (B, H, N, d),
 K and V (B, H_kv, N, d), dO (B, H, N, d) drawn in that order as float32
 N(0, 1), then rounded to the workload dtype with round-to-nearest-even.  Both
-the GPU path and the oracle receive these same rounded values.
+the GPU path and the oracle receive these same rounded values.  Decode
+workloads draw Q (B, H, n_q, d), K, V (B, H_kv, N, d) in that order from the
+same seed (``make_decode_inputs``).
 """
 
 from __future__ import annotations
@@ -46,6 +55,7 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "make_inputs",
+    "make_decode_inputs",
     "butterfly_block_mask",
     "kept_pairs_per_head",
     "fwd_flops",
@@ -70,6 +80,7 @@ class Workload:
     window: int = 0          # 0: none; W > 0: |i - j| < W
     hkv: int = 0             # K/V heads; 0 means H
     dropout: float = 0.0
+    nq: int = 0              # decode: queries per head (the last nq positions); 0: N
 
     @property
     def elem_bytes(self) -> int:
@@ -99,6 +110,8 @@ WORKLOADS = {
                             1.0 / math.sqrt(128.0), hkv=8),
     "gpt2_medium_dropout": Workload("gpt2_medium_dropout", 64, 16, 1024, 64, "f16", True,
                                     1.0 / 8.0, dropout=0.1),
+    "decode_gqa": Workload("decode_gqa", 16, 64, 8192, 128, "bf16", True, 1.0 / math.sqrt(128.0),
+                           hkv=8, nq=1),
 }
 
 
@@ -123,6 +136,21 @@ def make_inputs(B, H, N, d, dtype="f16", seed=None, hkv=None):
     out = []
     for heads in (H, hkv or H, hkv or H, H):
         x = torch.randn((B, heads, N, d), generator=g, dtype=torch.float32)
+        out.append(x.to(_torch_dtype(dtype)).contiguous())
+    return tuple(out)
+
+
+def make_decode_inputs(B, H, N, d, nq, dtype="bf16", seed=None, hkv=None):
+    """Decode-shaped inputs as CPU torch tensors in ``dtype``: Q (B, H, nq, d),
+    K and V (B, hkv or H, N, d), drawn in that order as float32 N(0, 1) from
+    torch.Generator('cpu').manual_seed(seed or 1000 + N), then rounded."""
+    import torch
+
+    g = torch.Generator("cpu")
+    g.manual_seed(1000 + N if seed is None else seed)
+    out = []
+    for shape in ((B, H, nq, d), (B, hkv or H, N, d), (B, hkv or H, N, d)):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
         out.append(x.to(_torch_dtype(dtype)).contiguous())
     return tuple(out)
 

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.fa_version() == 10100
+    assert B.fa_version() == 10200
     assert B.fa_status_string(0) == "ok"
     assert "workspace" in B.fa_status_string(B.FA_ERR_WORKSPACE)
     assert B.fa_status_string(12345) == "unknown status"
@@ -141,3 +141,53 @@ def test_mask_compile_argument_checks():
     L = B.lib()
     assert L.fa_mask_compile(None, 4, FAKE, FAKE, FAKE, FAKE, None) == B.FA_ERR_ARG
     assert L.fa_mask_compile(FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == B.FA_ERR_ARG
+
+
+def _decode_splits(B_, Hkv, N, n_q, group, window=0):
+    """The split rule the library documents: >= 2048 workgroups of (K/V head,
+    128-row block, key split), never more splits than 64-key tiles."""
+    rows = group * n_q
+    nrb = (rows + 127) // 128
+    lo = max(0, N - n_q - window + 1) if window else 0
+    ntiles = (N - 1) // 64 - lo // 64 + 1
+    wgs = B_ * Hkv * nrb
+    want = min(max(1, -(-2048 // wgs)), ntiles)
+    tps = -(-ntiles // want)
+    return -(-ntiles // tps)
+
+
+@pytest.mark.parametrize("B_,H,Hkv,N,d,n_q,window", [
+    (2, 8, 2, 4096, 64, 1, 0), (1, 64, 8, 8192, 128, 1, 0), (3, 4, 4, 1000, 64, 7, 0),
+    (2, 8, 2, 4096, 128, 4, 300), (64, 16, 16, 64, 64, 1, 0)])
+def test_decode_workspace_size(B_, H, Hkv, N, d, n_q, window):
+    p = _problem(B=B_, H=H, H_kv=Hkv, N=N, d=d, causal=1, window=window)
+    ns = _decode_splits(B_, Hkv, N, n_q, H // Hkv, window)
+    rows = B_ * H * n_q
+    want = 0 if ns == 1 else (-(-rows * ns * d * 4 // 256) * 256 + -(-rows * ns * 4 // 256) * 256)
+    assert B.fa_decode_workspace_size(p, n_q) == want
+
+
+@pytest.mark.parametrize("kw,n_q,status", [
+    ({}, 0, B.FA_ERR_ARG), ({"N": 16}, 17, B.FA_ERR_ARG),
+    ({"dtype": B.FA_F32}, 1, B.FA_ERR_UNSUPPORTED),
+    ({"block_mask": FAKE, "mask_block": 128}, 1, B.FA_ERR_UNSUPPORTED),
+    ({"dropout_p": 0.1}, 1, B.FA_ERR_UNSUPPORTED),
+    ({"d": 96}, 1, B.FA_ERR_UNSUPPORTED), ({"H_kv": 2}, 1, B.FA_ERR_ARG)])
+def test_decode_invalid_problems_rejected(kw, n_q, status):
+    p = _problem(**kw)
+    assert B.lib().fa_fwd_decode(ctypes.byref(p), n_q, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                 None) == status
+    assert B.fa_decode_workspace_size(p, n_q) == 0
+
+
+def test_decode_pointers_and_workspace_checked_before_launch():
+    L = B.lib()
+    p = _problem(N=4096, H=8, H_kv=2)
+    need = B.fa_decode_workspace_size(p, 1)
+    assert need > 0
+    assert L.fa_fwd_decode(ctypes.byref(p), 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, need,
+                           None) == B.FA_ERR_ARG
+    assert L.fa_fwd_decode(ctypes.byref(p), 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                           None) == B.FA_ERR_WORKSPACE
+    assert L.fa_fwd_decode(ctypes.byref(p), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4,
+                           None) == B.FA_ERR_WORKSPACE
