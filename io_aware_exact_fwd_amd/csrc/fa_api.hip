@@ -177,7 +177,7 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
 
 namespace {
 
-// Decode geometry: rows per K/V head, row blocks, key tiles and splits.  The
+// Decode geometry: rows per K/V head, row blocks, key tiles (of kDecKeys) and splits.  The
 // split count aims at >= 2048 workgroups (8 per CU) and depends only on the
 // problem, so the workspace size is known before any launch.
 struct DecodeShape {
@@ -192,8 +192,8 @@ DecodeShape decode_shape(const fa_problem* p, int n_q) {
   g.nkv = p->B * kv_heads(p);
   // keys some row sees: the rows sit at positions N - n_q .. N - 1
   const int lo = p->window > 0 ? (p->N - n_q - p->window + 1 > 0 ? p->N - n_q - p->window + 1 : 0) : 0;
-  g.tile0 = lo / 64;
-  g.ntiles = (p->N - 1) / 64 - g.tile0 + 1;
+  g.tile0 = lo / fa::kDecKeys;
+  g.ntiles = (p->N - 1) / fa::kDecKeys - g.tile0 + 1;
   const int64_t wgs = (int64_t)g.nkv * g.nrb;
   int want = (int)((2048 + wgs - 1) / wgs);
   if (want < 1) want = 1;

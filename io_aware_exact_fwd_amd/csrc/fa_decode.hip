@@ -28,20 +28,26 @@ constexpr float kDecTau = 8.0f;  // reference move threshold (base 2), as in the
 
 template <int D>
 struct DecGeom {
-  static constexpr int KT = 64;                // keys per tile
+  static constexpr int KT = kDecKeys;          // keys per tile
+  static constexpr int NST = 4;                // LDS stages: one computed, three in flight
   static constexpr int KBYTES = KT * D * 2;    // K tile, swizzled
   static constexpr int VBYTES = KT * D * 2;    // V tile, swizzled
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
+  static constexpr int COPIES = 2 * KT * D / 8 / 256;  // copies per thread per tile (K and V)
 };
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding and nothing else (expcnt and lgkmcnt at maximum).
+constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <typename T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecParams p) {
   using G = DecGeom<D>;
   using V8 = typename Vec8<T>::type;
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[G::NST * G::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -82,109 +88,108 @@ void decode_split_kernel(DecParams p) {
 #pragma unroll
   for (int t = 0; t < G::NKS; ++t)
     qf[t] = __builtin_bit_cast(V8, buf_load16(bq, (uint32_t)(r * D + t * 16 + g * 8) * sizeof(T)));
+  // Q has landed before any tile copy is issued, so no wait for Q remains
+  // inside the loop (where it would also drain the copies in flight)
+  wait_all_memory();
 
   f32x16 o[G::NDB];
 #pragma unroll
   for (int i = 0; i < G::NDB; ++i) o[i] = f32x16{0};
   float m_ref = kNegInf, ref = 0.f, l_run = 0.f;
 
-  auto gload = [&](int tile, int stage) {
-    char* ks = smem + stage * G::STAGE;
-    dma_tile<D, G::KT>(bk, tile * G::KT, ks, wave, lane);
-    dma_tile<D, G::KT>(bv, tile * G::KT, ks + G::KBYTES, wave, lane);
-  };
-
+  // Tile `it` of the split goes to stage it % NST.  Every iteration issues
+  // exactly one tile's copies (tiles past the split read beyond the buffer,
+  // which writes zeros without touching memory), so the number of copies in
+  // flight is a constant and the waits below are exact.
   const int ntl = t_end - t_begin;
-  if (ntl > 0) gload(t_begin, 0);
-  wait_all_memory();
-  __syncthreads();
+  auto issue = [&](int it) {
+    const int key0 = it < ntl ? (t_begin + it) * G::KT : N;
+    char* ks = smem + (it % G::NST) * G::STAGE;
+    dma_tile<D, G::KT>(bk, key0, ks, wave, lane);
+    dma_tile<D, G::KT>(bv, key0, ks + G::KBYTES, wave, lane);
+  };
+#pragma unroll
+  for (int it = 0; it < G::NST - 1; ++it) issue(it);
 
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
   for (int it = 0; it < ntl; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < ntl) gload(t_begin + it + 1, cur ^ 1);
+    // tile it has landed (the two younger tiles may still be in flight); after
+    // the barrier every wave's copies are visible and no wave still reads the
+    // stage of tile it - 1, which receives tile it + 3
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most((G::NST - 2) * G::COPIES));
+    __syncthreads();
+    issue(it + G::NST - 1);
     const int k0 = (t_begin + it) * G::KT;
-    const char* ks = smem + cur * G::STAGE;
+    const char* ks = smem + (it % G::NST) * G::STAGE;
     const char* vs = ks + G::KBYTES;
-    if (wave_rows && k0 <= w_hi && k0 + G::KT - 1 >= w_lo) {
-      f32x16 s[2];
+    if (!(wave_rows && k0 <= w_hi && k0 + G::KT - 1 >= w_lo)) continue;
+    f32x16 s = f32x16{0};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{0};
+    for (int t = 0; t < G::NKS; ++t)
+      s = mfma32(lds_read8<T>(ks + swz_off<D>(l32, t * 16 + g * 8)), qf[t], s);
+    // keys outside the row's band; key of register rr is k0 + g*4 + C,
+    // C = (rr/4)*8 + rr%4
+    if (k0 + G::KT - 1 > c_hi) {
+      const int ub = band.hi(pos) - k0 - g * 4;
 #pragma unroll
-        for (int t = 0; t < G::NKS; ++t)
-          s[kb] = mfma32(lds_read8<T>(ks + swz_off<D>(kb * 32 + l32, t * 16 + g * 8)), qf[t], s[kb]);
-      }
-      // keys outside the row's band; key of register rr of block kb is
-      // k0 + g*4 + C, C = kb*32 + (rr/4)*8 + rr%4
-      if (k0 + G::KT - 1 > c_hi) {
-        const int ub = band.hi(pos) - k0 - g * 4;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int C = kb * 32 + (rr >> 2) * 8 + (rr & 3);
-            s[kb][rr] = C > ub ? kNegInf : s[kb][rr];
-          }
-      }
-      if (k0 < c_lo) {
-        const int lb = band.lo(pos) - k0 - g * 4;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int C = kb * 32 + (rr >> 2) * 8 + (rr & 3);
-            s[kb][rr] = C < lb ? kNegInf : s[kb][rr];
-          }
-      }
-      // online softmax and O^T += V^T P^T, one 32-key half at a time
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float m4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m4[i] = vmax(s[kb][i], s[kb][i + 4]);
-#pragma unroll
-        for (int rr = 8; rr < 16; ++rr) m4[rr & 3] = vmax(m4[rr & 3], s[kb][rr]);
-        const float mx = vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3])) * p.c;
-        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kDecTau) != 0) {
-          FA_KEEP_BRANCH();
-          const float m_new = vmax(m_ref, pair_max(mx));
-          const float r_new = (m_new == kNegInf) ? 0.f : m_new;
-          const float alpha = fast_exp2(m_ref - r_new);  // 0 while m_ref = -inf
-          l_run *= alpha;
-#pragma unroll
-          for (int i = 0; i < G::NDB; ++i) o[i] *= alpha;
-          m_ref = m_new;
-          ref = r_new;
-        }
-#pragma unroll
-        for (int th = 0; th < 2; ++th) {
-          const int t = kb * 2 + th, r0 = th * 8;
-          u32x4 w;
-          float lp = 0.f;
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const float e0 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2 * h], p.c, -ref));
-            const float e1 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2 * h + 1], p.c, -ref));
-            w[h] = pack2<T>(e0, e1);
-            if constexpr (__is_same(T, _Float16)) {
-              lp = add_pair<T>(w[h], lp);  // fp16: the rounded weights P V uses
-            } else {
-              lp += e0 + e1;  // bf16 rounding is too coarse for the LSE: fp32 sum
-            }
-          }
-          l_run += lp;
-          const V8 bp = __builtin_bit_cast(V8, w);
-#pragma unroll
-          for (int db = 0; db < G::NDB; ++db)
-            o[db] = mfma32(swz_tr_operand<T, D>(vs, t * 16 + g * 4 + tr_row, db * 32 + tr_col), bp, o[db]);
-        }
+      for (int rr = 0; rr < 16; ++rr) {
+        const int C = (rr >> 2) * 8 + (rr & 3);
+        s[rr] = C > ub ? kNegInf : s[rr];
       }
     }
-    wait_all_memory();  // this thread's copies into the next stage have landed
-    __syncthreads();
+    if (k0 < c_lo) {
+      const int lb = band.lo(pos) - k0 - g * 4;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int C = (rr >> 2) * 8 + (rr & 3);
+        s[rr] = C < lb ? kNegInf : s[rr];
+      }
+    }
+    // online softmax and O^T += V^T P^T
+    float m4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m4[i] = vmax(s[i], s[i + 4]);
+#pragma unroll
+    for (int rr = 8; rr < 16; ++rr) m4[rr & 3] = vmax(m4[rr & 3], s[rr]);
+    const float mx = vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3])) * p.c;
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kDecTau) != 0) {
+      FA_KEEP_BRANCH();
+      const float m_new = vmax(m_ref, pair_max(mx));
+      const float r_new = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_ref - r_new);  // 0 while m_ref = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < G::NDB; ++i) o[i] *= alpha;
+      m_ref = m_new;
+      ref = r_new;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r0 = t * 8;
+      u32x4 w;
+      float lp = 0.f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float e0 = fast_exp2(__builtin_fmaf(s[r0 + 2 * h], p.c, -ref));
+        const float e1 = fast_exp2(__builtin_fmaf(s[r0 + 2 * h + 1], p.c, -ref));
+        w[h] = pack2<T>(e0, e1);
+        if constexpr (__is_same(T, _Float16)) {
+          lp = add_pair<T>(w[h], lp);  // fp16: the rounded weights P V uses
+        } else {
+          lp += e0 + e1;  // bf16 rounding is too coarse for the LSE: fp32 sum
+        }
+      }
+      l_run += lp;
+      const V8 bp = __builtin_bit_cast(V8, w);
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db)
+        o[db] = mfma32(swz_tr_operand<T, D>(vs, t * 16 + g * 4 + tr_row, db * 32 + tr_col), bp, o[db]);
+    }
   }
+  // the copies issued past the last tile must land before this workgroup's
+  // LDS can be handed to another one
+  wait_all_memory();
 
   // this split's part of the row: O / l and LSE (natural log), -inf if the
   // split holds no visible key of the row

@@ -13,6 +13,7 @@ constexpr int kFwdRows = 128;   // query rows per forward / dQ workgroup (4 wave
 constexpr int kKeyTile = 64;    // keys per inner step of the forward / dQ loop
 constexpr int kBwdKeys = 128;   // keys per dK/dV workgroup (4 waves x 32)
 constexpr int kThreads = 256;
+constexpr int kDecKeys = 32;   // keys per tile of the decode kernel
 
 // Block-sparse lists compiled from the dense block mask (see fa_mask_compile).
 struct MaskLists {

@@ -145,11 +145,11 @@ def test_mask_compile_argument_checks():
 
 def _decode_splits(B_, Hkv, N, n_q, group, window=0):
     """The split rule the library documents: >= 2048 workgroups of (K/V head,
-    128-row block, key split), never more splits than 64-key tiles."""
+    128-row block, key split), never more splits than 32-key tiles."""
     rows = group * n_q
     nrb = (rows + 127) // 128
     lo = max(0, N - n_q - window + 1) if window else 0
-    ntiles = (N - 1) // 64 - lo // 64 + 1
+    ntiles = (N - 1) // 32 - lo // 32 + 1
     wgs = B_ * Hkv * nrb
     want = min(max(1, -(-2048 // wgs)), ntiles)
     tps = -(-ntiles // want)

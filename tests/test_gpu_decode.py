@@ -79,7 +79,10 @@ def test_decode_zero_queries_lse_counts_visible_keys(N, nq, causal, window):
 
 
 def test_decode_square_equals_forward_kernel():
-    """n_q = N through the decode path agrees with fa_fwd on the same inputs."""
+    """n_q = N through the decode path agrees with fa_fwd on the same inputs,
+    to the stated O and LSE tolerances (the two paths tile the keys differently,
+    32 vs 64, so their running reference maxima -- and with them the fp16
+    rounding of the weights that the row sum adds up -- differ)."""
     B, H, N, d = 1, 4, 1000, 64
     q, k, v = make_decode_inputs(B, H, N, d, N, "f16", hkv=2)
     dev = torch.device("cuda:0")
@@ -87,8 +90,8 @@ def test_decode_square_equals_forward_kernel():
     o1, l1 = fa_fwd_decode(qd, kd, vd, causal=True)
     o2, l2 = fa_fwd(qd, kd, vd, causal=True)
     torch.cuda.synchronize()
-    assert float((o1.float() - o2.float()).abs().max()) <= 2e-3
-    assert float((l1 - l2).abs().max()) <= 1e-4
+    assert float((o1.float() - o2.float()).abs().max()) <= O_TOL["f16"]
+    assert float((l1 - l2).abs().max()) <= LSE_TOL
 
 
 def test_workload_decode_gqa_full_size():
