@@ -180,6 +180,46 @@ size_t fa_decode_workspace_size(const fa_problem* p, int32_t n_q);
 int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k, const void* v,
                   void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
+/* FP8 forward: block quantisation with a random Hadamard-style rotation
+ * ("Atencao Eficiente em Escala", section 10 on FlashAttention-3: Q, K, V are
+ * quantised to FP8 with one scale per tile after an orthogonal randomised
+ * Hadamard projection that spreads outlier coordinates; the rotation is undone
+ * after the product).  Two calls:
+ *
+ * fa_fp8_quantize rotates every row of q, k, v by M = diag(signs) H / sqrt(d)
+ * (H the d x d Sylvester Hadamard matrix; float32 butterflies with pair
+ * distances 1, 2, ..., d/2, then a multiply by float32(1 / sqrt(d))), and
+ * quantises each block of 64 rows of one head to E4M3 (bias 7, largest finite
+ * value 448, round to nearest even) with the scale 2^e, e the smallest integer
+ * with max |row value| <= 448 * 2^e.  Rows past N (up to N64 = N rounded up to
+ * a multiple of 64) are zero.  Results go to the workspace:
+ *   Q codes  uint8 (B H, N64, d) row-major;  K codes uint8 (B H_kv, N64, d);
+ *   V codes  uint8 (B H_kv, N64 / 64, d, 64): per 64-key tile, row c holds
+ *            column c of V, byte p holding key 32 (i / 16) + 8 ((i % 16) / 4)
+ *            + 4 h + i % 4 of the tile, h = p / 32, i = p % 32;
+ *   then int8 exponents e of Q (B H, N64 / 64), K and V (B H_kv, N64 / 64);
+ *   each of the six regions starts on a 256-byte boundary, in that order.
+ * fa_fwd_fp8 computes attention on those codes: S = scale Qr Kr^T on the FP8
+ * matrix cores with the block scales applied inside the product, the online
+ * softmax in float32, probabilities (at most 256) rounded to E4M3 for the P V
+ * product, float32 accumulation, and O = (P Vr / l) M^T written in the
+ * problem's dtype (B, H, N, d), with lse float32 (B, H, N) the natural-log
+ * LSE of the scores.  Masks: causal and window as for fa_fwd.
+ *
+ * signs: device float32[d], each +1 or -1 (the caller's random draw; the
+ * library reads, never writes it).  q, k, v as for fa_fwd.  Requirements:
+ * dtype FA_F16 or FA_BF16, block_mask == NULL and dropout_p == 0 (else
+ * FA_ERR_UNSUPPORTED); workspace at least fa_fp8_workspace_size(p) bytes,
+ * 16-byte aligned (else FA_ERR_WORKSPACE), owned by the caller and left
+ * unchanged by fa_fwd_fp8, which reads the codes fa_fp8_quantize left there
+ * for the same problem and signs.  fa_fp8_workspace_size returns 0 for a
+ * problem the FP8 path does not take. */
+size_t fa_fp8_workspace_size(const fa_problem* p);
+int fa_fp8_quantize(const fa_problem* p, const float* signs, const void* q, const void* k,
+                    const void* v, void* workspace, size_t ws_bytes, void* stream);
+int fa_fwd_fp8(const fa_problem* p, const float* signs, const void* workspace, size_t ws_bytes,
+               void* o, float* lse, void* stream);
+
 /* Static string for a status code. */
 const char* fa_status_string(int status);
 

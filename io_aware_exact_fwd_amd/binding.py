@@ -24,6 +24,7 @@ FA_OK, FA_ERR_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = 0, -1, 
 
 EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv",
            "fa_mask_compile", "fa_decode_workspace_size", "fa_fwd_decode",
+           "fa_fp8_workspace_size", "fa_fp8_quantize", "fa_fwd_fp8",
            "fa_status_string", "fa_version")
 
 
@@ -84,6 +85,12 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_workspace_size.restype = sz
     L.fa_fwd_decode.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.fa_fwd_decode.restype = ctypes.c_int
+    L.fa_fp8_workspace_size.argtypes = [pp]
+    L.fa_fp8_workspace_size.restype = sz
+    L.fa_fp8_quantize.argtypes = [pp, vp, vp, vp, vp, vp, sz, vp]
+    L.fa_fp8_quantize.restype = ctypes.c_int
+    L.fa_fwd_fp8.argtypes = [pp, vp, vp, sz, vp, vp, vp]
+    L.fa_fwd_fp8.restype = ctypes.c_int
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -226,6 +233,87 @@ def fa_fwd_decode(q, k, v, causal=True, scale=None, window=0, out=None, lse=None
                              o.data_ptr(), lse_t.data_ptr(), ws.data_ptr(), ws_n, _stream(q))
     if st != FA_OK:
         raise FaError("fa_fwd_decode", st)
+    return o, lse_t
+
+
+def fa_fp8_workspace_size(p: FaProblem) -> int:
+    return int(lib().fa_fp8_workspace_size(ctypes.byref(p)))
+
+
+def _check_signs(signs, q):
+    import torch
+
+    if (not isinstance(signs, torch.Tensor) or signs.dtype != torch.float32 or not signs.is_cuda
+            or not signs.is_contiguous() or signs.shape != (q.shape[3],)):
+        raise ValueError("signs must be a contiguous float32 GPU tensor of d values (+1 / -1)")
+
+
+def fp8_quantize(q, k, v, signs, causal=False, scale=None, window=0, workspace=None):
+    """Rotate and block-quantise q, k, v to E4M3 (``fa_fp8_quantize``).
+    Returns (problem, workspace uint8 tensor); ``fp8_workspace_views`` names
+    the regions of the workspace."""
+    import torch
+
+    _check_qkv(q, k, v)
+    _check_signs(signs, q)
+    p = make_problem(q, causal, scale, None, 128, k, window)
+    ws_n = fa_fp8_workspace_size(p)
+    if ws_n == 0:
+        raise FaError("fa_fp8_workspace_size", FA_ERR_UNSUPPORTED)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    if ws.dtype != torch.uint8 or not ws.is_cuda or not ws.is_contiguous() or ws.numel() < ws_n:
+        raise ValueError(f"workspace must be a contiguous uint8 GPU tensor of >= {ws_n} bytes")
+    st = lib().fa_fp8_quantize(ctypes.byref(p), signs.data_ptr(), q.data_ptr(), k.data_ptr(),
+                               v.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q))
+    if st != FA_OK:
+        raise FaError("fa_fp8_quantize", st)
+    return p, ws
+
+
+def fp8_workspace_views(ws, B, H, H_kv, N, d):
+    """Views of the six regions of an FP8 workspace (layout of include/fa.h):
+    q/k codes (heads, N64, d), v codes (H_kv heads, N64 / 64, d, 64), and the
+    int8 block exponents (heads, N64 / 64)."""
+    import torch
+
+    n64 = (N + 63) // 64 * 64
+    hq, hk = B * H, B * H_kv
+
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    sizes = [hq * n64 * d, hk * n64 * d, hk * n64 * d, hq * n64 // 64, hk * n64 // 64,
+             hk * n64 // 64]
+    offs, o = [], 0
+    for sz in sizes:
+        offs.append(o)
+        o += al(sz)
+    views = {
+        "qc": ws[offs[0]:offs[0] + sizes[0]].view(hq, n64, d),
+        "kc": ws[offs[1]:offs[1] + sizes[1]].view(hk, n64, d),
+        "vc": ws[offs[2]:offs[2] + sizes[2]].view(hk, n64 // 64, d, 64),
+    }
+    for name, i, h in (("qe", 3, hq), ("ke", 4, hk), ("ve", 5, hk)):
+        views[name] = ws[offs[i]:offs[i] + sizes[i]].view(torch.int8).view(h, n64 // 64)
+    return views
+
+
+def fa_fwd_fp8(q, k, v, signs, causal=False, scale=None, window=0, out=None, lse=None,
+               workspace=None):
+    """FP8 forward with block scales and the random Hadamard rotation given by
+    ``signs`` (float32 (d,), +1 / -1): quantises q, k, v into the workspace,
+    then runs attention on the codes.  Returns (O like q, LSE float32 (B, H, N))."""
+    import torch
+
+    p, ws = fp8_quantize(q, k, v, signs, causal, scale, window, workspace)
+    B, H, N, d = q.shape
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensors(q, o)
+    st = lib().fa_fwd_fp8(ctypes.byref(p), signs.data_ptr(), ws.data_ptr(), ws.numel(),
+                          o.data_ptr(), lse_t.data_ptr(), _stream(q))
+    if st != FA_OK:
+        raise FaError("fa_fwd_fp8", st)
     return o, lse_t
 
 

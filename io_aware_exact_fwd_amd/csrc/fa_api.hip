@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -257,6 +257,107 @@ int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k
   d.window = p->window;
   d.c = p->scale * fa::kLog2e;
   return fa::launch_decode(d, p->dtype, p->d, p->causal != 0, (hipStream_t)stream) == hipSuccess
+             ? FA_OK
+             : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+namespace {
+
+// FP8 workspace regions (see include/fa.h): codes of Q, K, V, then the block
+// exponents of Q, K, V, each region 256-byte aligned.
+struct Fp8Layout {
+  size_t n64, qc, kc, vc, qe, ke, ve, total;
+};
+
+Fp8Layout fp8_layout(const fa_problem* p) {
+  Fp8Layout l;
+  l.n64 = (size_t)(p->N + 63) / 64 * 64;
+  const size_t hq = (size_t)p->B * p->H, hk = (size_t)p->B * kv_heads(p);
+  l.qc = 0;
+  l.kc = l.qc + align_up(hq * l.n64 * p->d);
+  l.vc = l.kc + align_up(hk * l.n64 * p->d);
+  l.qe = l.vc + align_up(hk * l.n64 * p->d);
+  l.ke = l.qe + align_up(hq * (l.n64 / 64));
+  l.ve = l.ke + align_up(hk * (l.n64 / 64));
+  l.total = l.ve + align_up(hk * (l.n64 / 64));
+  return l;
+}
+
+int check_fp8(const fa_problem* p, const float* signs) {
+  int st = check_problem(p);
+  if (st != FA_OK) return st;
+  if (!signs || ((uintptr_t)signs & 3u)) return FA_ERR_ARG;
+  if (p->dtype == FA_F32 || p->block_mask != nullptr || p->dropout_p != 0.f) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_fp8_workspace_size(const fa_problem* p) {
+  if (check_problem(p) != FA_OK || p->dtype == FA_F32 || p->block_mask || p->dropout_p != 0.f) return 0;
+  return fp8_layout(p).total;
+}
+
+int fa_fp8_quantize(const fa_problem* p, const float* signs, const void* q, const void* k, const void* v,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_fp8(p, signs);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !aligned16(q) || !aligned16(k) || !aligned16(v)) return FA_ERR_ARG;
+  const Fp8Layout l = fp8_layout(p);
+  if (!workspace || ws_bytes < l.total || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const int hq = p->B * p->H, hk = p->B * kv_heads(p);
+  const struct {
+    const void* x;
+    size_t codes, exps;
+    int heads;
+    bool vlayout;
+  } parts[3] = {{q, l.qc, l.qe, hq, false}, {k, l.kc, l.ke, hk, false}, {v, l.vc, l.ve, hk, true}};
+  for (const auto& t : parts) {
+    fa::Fp8QuantParams qp;
+    qp.x = t.x;
+    qp.codes = (uint8_t*)(ws + t.codes);
+    qp.exps = (int8_t*)(ws + t.exps);
+    qp.signs = signs;
+    qp.N = p->N;
+    qp.N64 = (int)l.n64;
+    if (fa::launch_fp8_quantize(qp, p->dtype, p->d, t.vlayout, t.heads, s) != hipSuccess)
+      return FA_ERR_LAUNCH;
+  }
+  return FA_OK;
+}
+
+int fa_fwd_fp8(const fa_problem* p, const float* signs, const void* workspace, size_t ws_bytes, void* o,
+               float* lse, void* stream) {
+  int st = check_fp8(p, signs);
+  if (st != FA_OK) return st;
+  if (!o || !lse || !aligned16(o) || ((uintptr_t)lse & 3u)) return FA_ERR_ARG;
+  const Fp8Layout l = fp8_layout(p);
+  if (!workspace || ws_bytes < l.total || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  const char* ws = (const char*)workspace;
+  fa::Fp8FwdParams f;
+  f.qc = (const uint8_t*)(ws + l.qc);
+  f.kc = (const uint8_t*)(ws + l.kc);
+  f.vc = (const uint8_t*)(ws + l.vc);
+  f.qe = (const int8_t*)(ws + l.qe);
+  f.ke = (const int8_t*)(ws + l.ke);
+  f.ve = (const int8_t*)(ws + l.ve);
+  f.signs = signs;
+  f.o = o;
+  f.lse = lse;
+  f.N = p->N;
+  f.N64 = (int)l.n64;
+  f.nheads = p->B * p->H;
+  f.nqt = (p->N + 127) / 128;
+  f.window = p->window;
+  f.group = group_of(p);
+  f.c = p->scale * fa::kLog2e;
+  return fa::launch_fp8_fwd(f, p->dtype, p->d, p->causal != 0, (hipStream_t)stream) == hipSuccess
              ? FA_OK
              : FA_ERR_LAUNCH;
 }

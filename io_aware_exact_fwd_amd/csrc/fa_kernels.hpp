@@ -93,6 +93,36 @@ struct DecParams {
   float c;           // scale * log2(e)
 };
 
+// FP8 forward (fa_fp8.hip): rotation + block quantisation, then attention on
+// the codes.
+struct Fp8QuantParams {
+  const void* x;        // (heads, N, d) input in the problem dtype
+  uint8_t* codes;       // row-major (heads, N64, d) or V tiles (heads, N64/64, d, 64)
+  int8_t* exps;         // (heads, N64 / 64) block exponents
+  const float* signs;   // d random signs of the rotation
+  int N;
+  int N64;              // N rounded up to a multiple of 64
+};
+
+struct Fp8FwdParams {
+  const uint8_t* qc;    // Q codes (B*H, N64, d)
+  const uint8_t* kc;    // K codes (B*H_kv, N64, d)
+  const uint8_t* vc;    // V codes, tiles (B*H_kv, N64/64, d, 64)
+  const int8_t* qe;     // block exponents
+  const int8_t* ke;
+  const int8_t* ve;
+  const float* signs;
+  void* o;              // (B, H, N, d) in the problem dtype
+  float* lse;           // (B, H, N)
+  int N;
+  int N64;
+  int nheads;           // B * H
+  int nqt;              // 128-row query tiles per head
+  int window;
+  int group;            // query heads per K/V head
+  float c;              // scale * log2(e)
+};
+
 struct F32Params {
   const float* q;
   const float* k;
@@ -133,6 +163,9 @@ hipError_t launch_bwd_dq_drop(const BwdParams& p, int dtype, int d, bool causal,
 hipError_t launch_bwd_dkdv_drop(const BwdParams& p, int dtype, int d, bool causal, bool masked,
                                 hipStream_t s);
 hipError_t launch_decode(const DecParams& p, int dtype, int d, bool causal, hipStream_t s);
+hipError_t launch_fp8_quantize(const Fp8QuantParams& qp, int dtype, int d, bool vlayout, int heads,
+                               hipStream_t s);
+hipError_t launch_fp8_fwd(const Fp8FwdParams& p, int dtype, int d, bool causal, hipStream_t s);
 hipError_t launch_f32_fwd(const F32Params& p, hipStream_t s);
 hipError_t launch_f32_dq(const F32Params& p, hipStream_t s);
 hipError_t launch_f32_dkdv(const F32Params& p, hipStream_t s);

@@ -42,6 +42,15 @@ N(0, 1), then rounded to the workload dtype with round-to-nearest-even.  Both
 the GPU path and the oracle receive these same rounded values.  Decode
 workloads draw Q (B, H, n_q, d), K, V (B, H_kv, N, d) in that order from the
 same seed (``make_decode_inputs``).
+
+FP8 path (block-quantised forward with the random rotation): the same shapes
+in bf16 / fp16, and inputs with outlier channels (``make_outlier_inputs``:
+the N(0, 1) draw of ``make_inputs`` with a few head-dim coordinates of Q and
+K multiplied by large factors, the case the rotation exists for); the
+rotation's signs are drawn by ``make_signs``.
+
+  long_wide_fp8 long_wide's shape (B=2 H=16 N=8192 d=128 causal) through the
+                FP8 forward, bf16 in and out
 """
 
 from __future__ import annotations
@@ -56,6 +65,8 @@ __all__ = [
     "WORKLOADS",
     "make_inputs",
     "make_decode_inputs",
+    "make_outlier_inputs",
+    "make_signs",
     "butterfly_block_mask",
     "kept_pairs_per_head",
     "fwd_flops",
@@ -81,6 +92,7 @@ class Workload:
     hkv: int = 0             # K/V heads; 0 means H
     dropout: float = 0.0
     nq: int = 0              # decode: queries per head (the last nq positions); 0: N
+    fp8: bool = False        # forward through the FP8 path (block scales + rotation)
 
     @property
     def elem_bytes(self) -> int:
@@ -112,6 +124,8 @@ WORKLOADS = {
                                     1.0 / 8.0, dropout=0.1),
     "decode_gqa": Workload("decode_gqa", 16, 64, 8192, 128, "bf16", True, 1.0 / math.sqrt(128.0),
                            hkv=8, nq=1),
+    "long_wide_fp8": Workload("long_wide_fp8", 2, 16, 8192, 128, "bf16", True,
+                              1.0 / math.sqrt(128.0), fp8=True),
 }
 
 
@@ -153,6 +167,36 @@ def make_decode_inputs(B, H, N, d, nq, dtype="bf16", seed=None, hkv=None):
         x = torch.randn(shape, generator=g, dtype=torch.float32)
         out.append(x.to(_torch_dtype(dtype)).contiguous())
     return tuple(out)
+
+
+def make_outlier_inputs(B, H, N, d, dtype="bf16", seed=None, hkv=None,
+                        outliers=((3, 30.0), (17, 20.0))):
+    """``make_inputs`` with the head-dim coordinates c of Q and K multiplied by
+    f for each (c, f) in ``outliers`` (before the rounding to ``dtype``)."""
+    import torch
+
+    g = torch.Generator("cpu")
+    g.manual_seed(1000 + N if seed is None else seed)
+    out = []
+    for i, heads in enumerate((H, hkv or H, hkv or H, H)):
+        x = torch.randn((B, heads, N, d), generator=g, dtype=torch.float32)
+        if i < 2:
+            for c, f in outliers:
+                x[..., c] *= f
+        out.append(x.to(_torch_dtype(dtype)).contiguous())
+    return tuple(out)
+
+
+def make_signs(d, seed=7):
+    """d random signs (+1 / -1) as a float32 CPU tensor, from
+    torch.Generator('cpu').manual_seed(seed): sign = +1 where a uniform draw
+    is below 1/2."""
+    import torch
+
+    g = torch.Generator("cpu")
+    g.manual_seed(seed)
+    u = torch.rand(d, generator=g, dtype=torch.float32)
+    return torch.where(u < 0.5, 1.0, -1.0).to(torch.float32)
 
 
 def butterfly_block_mask(nblocks: int) -> np.ndarray:

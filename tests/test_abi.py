@@ -20,7 +20,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_exports():
@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.fa_version() == 10200
+    assert B.fa_version() == 10300
     assert B.fa_status_string(0) == "ok"
     assert "workspace" in B.fa_status_string(B.FA_ERR_WORKSPACE)
     assert B.fa_status_string(12345) == "unknown status"
@@ -191,3 +191,56 @@ def test_decode_pointers_and_workspace_checked_before_launch():
                            None) == B.FA_ERR_WORKSPACE
     assert L.fa_fwd_decode(ctypes.byref(p), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4,
                            None) == B.FA_ERR_WORKSPACE
+
+
+def _fp8_size(B_, H, Hkv, N, d):
+    """The FP8 workspace layout the header documents: Q, K, V codes, then the
+    int8 block exponents of Q, K, V, each region 256-byte aligned."""
+    n64 = -(-N // 64) * 64
+
+    def al(x):
+        return -(-x // 256) * 256
+
+    hq, hk = B_ * H, B_ * Hkv
+    return (al(hq * n64 * d) + 2 * al(hk * n64 * d) + al(hq * n64 // 64)
+            + 2 * al(hk * n64 // 64))
+
+
+@pytest.mark.parametrize("B_,H,Hkv,N,d", [(2, 3, 3, 256, 64), (1, 8, 2, 1000, 128),
+                                          (4, 16, 16, 1, 64)])
+def test_fp8_workspace_size(B_, H, Hkv, N, d):
+    p = _problem(B=B_, H=H, H_kv=Hkv, N=N, d=d)
+    assert B.fa_fp8_workspace_size(p) == _fp8_size(B_, H, Hkv, N, d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"dtype": B.FA_F32}, B.FA_ERR_UNSUPPORTED),
+    ({"block_mask": FAKE, "mask_block": 128}, B.FA_ERR_UNSUPPORTED),
+    ({"dropout_p": 0.1}, B.FA_ERR_UNSUPPORTED),
+    ({"d": 96}, B.FA_ERR_UNSUPPORTED), ({"H_kv": 2}, B.FA_ERR_ARG), ({"N": 0}, B.FA_ERR_ARG)])
+def test_fp8_invalid_problems_rejected(kw, status):
+    p = _problem(**kw)
+    L = B.lib()
+    assert B.fa_fp8_workspace_size(p) == 0
+    assert L.fa_fp8_quantize(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                             None) == status
+    assert L.fa_fwd_fp8(ctypes.byref(p), FAKE, FAKE, 1 << 30, FAKE, FAKE, None) == status
+
+
+def test_fp8_pointers_and_workspace_checked_before_launch():
+    L = B.lib()
+    p = _problem()
+    need = B.fa_fp8_workspace_size(p)
+    assert need > 0
+    q = ctypes.byref(p)
+    assert L.fa_fp8_quantize(q, None, FAKE, FAKE, FAKE, FAKE, need, None) == B.FA_ERR_ARG
+    assert L.fa_fp8_quantize(q, FAKE + 2, FAKE, FAKE, FAKE, FAKE, need, None) == B.FA_ERR_ARG
+    assert L.fa_fp8_quantize(q, FAKE, FAKE, None, FAKE, FAKE, need, None) == B.FA_ERR_ARG
+    assert L.fa_fp8_quantize(q, FAKE, FAKE, FAKE, FAKE + 8, FAKE, need, None) == B.FA_ERR_ARG
+    assert L.fa_fp8_quantize(q, FAKE, FAKE, FAKE, FAKE, None, need, None) == B.FA_ERR_WORKSPACE
+    assert L.fa_fp8_quantize(q, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                             None) == B.FA_ERR_WORKSPACE
+    assert L.fa_fwd_fp8(q, FAKE, FAKE, need, None, FAKE, None) == B.FA_ERR_ARG
+    assert L.fa_fwd_fp8(q, FAKE, FAKE, need, FAKE, FAKE + 2, None) == B.FA_ERR_ARG
+    assert L.fa_fwd_fp8(q, FAKE, FAKE, need - 1, FAKE, FAKE, None) == B.FA_ERR_WORKSPACE
+    assert L.fa_fwd_fp8(q, FAKE, FAKE + 8, need, FAKE, FAKE, None) == B.FA_ERR_WORKSPACE
