@@ -21,7 +21,11 @@ FP8 rounding.  Readings taken where the pages leave the details open:
   performs, so both sides reach identical quantised codes.
 * Block: 64 consecutive rows of one head (the kernels' tile height); scale
   2^e with e the smallest integer such that max |y| <= 448 * 2^e (an exact
-  power of two, so dequantisation is exact); codes = E4M3(y / 2^e).
+  power of two, so dequantisation is exact); codes = E4M3(y / 2^e).  The
+  scale is carried as an 8-bit power-of-two exponent (E8M0, 2^-127 ..
+  2^127), so e is raised to -127 for a block whose largest magnitude is below
+  448 * 2^-128 (values near the float32 underflow threshold); e = 0 for an
+  all-zero block.
 * Attention: the plain definition (``oracle.attention``) applied to the
   dequantised rotated tensors in float64, then O multiplied by M^T.  The
   kernel additionally rounds the probabilities to E4M3 before the P V
@@ -113,12 +117,17 @@ def rotate_rows_f32(x, signs):
     return (y * np.float32(1.0 / np.sqrt(d))).astype(np.float32)
 
 
+E8M0_MIN_EXP = -127
+
+
 def _block_exponent(amax):
-    """Smallest integer e with amax <= 448 * 2^e (0 for an all-zero block)."""
+    """Smallest integer e >= -127 with amax <= 448 * 2^e (0 for an all-zero
+    block)."""
     amax = np.asarray(amax, dtype=np.float64)
     f, e2 = np.frexp(np.where(amax > 0, amax, 1.0))  # amax = f * 2^e2, f in [0.5, 1)
     mant = 2.0 * f                                     # amax = mant * 2^(e2 - 1)
     e = (e2 - 1) - 8 + (mant > 1.75).astype(np.int64)
+    e = np.maximum(e, E8M0_MIN_EXP)
     return np.where(amax > 0, e, 0).astype(np.int64)
 
 

@@ -68,6 +68,26 @@ def test_float32_butterflies_equal_the_matrix_product(d):
                           (rotation_matrix(s) * np.sqrt(d)).astype(np.float32) * np.float32(1 / np.sqrt(d)))
 
 
+def test_block_exponent_stays_in_the_e8m0_range():
+    """A block whose largest magnitude is below 448 * 2^-128 keeps e = -127
+    (the smallest E8M0 scale); just above it the tight rule applies."""
+    y = np.zeros((128, 64), dtype=np.float32)
+    y[0, 0] = np.float32(2.0 ** -125)       # tight e would be -125 - 8 = -133
+    y[5, 3] = np.float32(-3.0 * 2.0 ** -130)
+    y[64, 0] = np.float32(448.0 * 2.0 ** -127)  # tight e = -127 exactly
+    codes, e = block_quantize(y)
+    assert list(e) == [-127, -127]
+    # 2^-125 / 2^-127 = 4 = 1.0 * 2^2: exponent field 9, mantissa 0 -> 0x48;
+    # -3 * 2^-130 / 2^-127 = -3/8 = -1.5 * 2^-2: field 5, mantissa 4 -> 0x80 | 0x2C
+    assert codes[0, 0] == 0x48 and codes[5, 3] == 0xAC and codes[64, 0] == 0x7E
+    assert np.all(block_dequantize(codes, e, 128)[[0, 5, 64], [0, 3, 0]]
+                  == [2.0 ** -125, -3.0 * 2.0 ** -130, 448.0 * 2.0 ** -127])
+    _, e2 = block_quantize(np.full((64, 64), 1.75 * 2.0 ** -119, dtype=np.float32))
+    assert e2[0] == -127                     # 1.75 * 2^-119 = 448 * 2^-127
+    _, e3 = block_quantize(np.full((64, 64), 2.0 ** -118, dtype=np.float32))
+    assert e3[0] == -126
+
+
 def test_block_scales_are_tight_powers_of_two():
     rng = np.random.default_rng(2)
     y = (rng.standard_normal((2, 200, 64)) * rng.uniform(1e-3, 1e3, (2, 1, 1))).astype(np.float32)
