@@ -310,26 +310,27 @@ int fa_fp8_quantize(const fa_problem* p, const float* signs, const void* q, cons
   const Fp8Layout l = fp8_layout(p);
   if (!workspace || ws_bytes < l.total || !aligned16(workspace)) return FA_ERR_WORKSPACE;
   char* ws = (char*)workspace;
-  hipStream_t s = (hipStream_t)stream;
-  const int hq = p->B * p->H, hk = p->B * kv_heads(p);
-  const struct {
-    const void* x;
-    size_t codes, exps;
-    int heads;
-    bool vlayout;
-  } parts[3] = {{q, l.qc, l.qe, hq, false}, {k, l.kc, l.ke, hk, false}, {v, l.vc, l.ve, hk, true}};
-  for (const auto& t : parts) {
-    fa::Fp8QuantParams qp;
-    qp.x = t.x;
-    qp.codes = (uint8_t*)(ws + t.codes);
-    qp.exps = (int8_t*)(ws + t.exps);
-    qp.signs = signs;
-    qp.N = p->N;
-    qp.N64 = (int)l.n64;
-    if (fa::launch_fp8_quantize(qp, p->dtype, p->d, t.vlayout, t.heads, s) != hipSuccess)
-      return FA_ERR_LAUNCH;
-  }
-  return FA_OK;
+  const int nblk = (int)(l.n64 / 64);
+  fa::Fp8QuantParams qp;
+  qp.x0 = q;
+  qp.x1 = k;
+  qp.x2 = v;
+  qp.c0 = (uint8_t*)(ws + l.qc);
+  qp.c1 = (uint8_t*)(ws + l.kc);
+  qp.c2 = (uint8_t*)(ws + l.vc);
+  qp.e0 = (int8_t*)(ws + l.qe);
+  qp.e1 = (int8_t*)(ws + l.ke);
+  qp.e2 = (int8_t*)(ws + l.ve);
+  qp.signs = signs;
+  qp.nq_wg = p->B * p->H * nblk;
+  qp.nk_wg = p->B * kv_heads(p) * nblk;
+  qp.N = p->N;
+  qp.N64 = (int)l.n64;
+  const int64_t wgs = (int64_t)qp.nq_wg + 2 * (int64_t)qp.nk_wg;
+  if (wgs > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
+  return fa::launch_fp8_quantize(qp, p->dtype, p->d, (int)wgs, (hipStream_t)stream) == hipSuccess
+             ? FA_OK
+             : FA_ERR_LAUNCH;
 }
 
 int fa_fwd_fp8(const fa_problem* p, const float* signs, const void* workspace, size_t ws_bytes, void* o,

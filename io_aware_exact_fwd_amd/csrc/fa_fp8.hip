@@ -86,33 +86,73 @@ __device__ __forceinline__ uint32_t fp8x2(float a, float b, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
 }
 
-// Smallest e with amax <= 448 * 2^e, from the float32 bits (0 for amax = 0).
+// Smallest e >= -127 (the E8M0 range) with amax <= 448 * 2^e, from the float32
+// bits; 0 for amax = 0.  A float32-subnormal amax reads as exponent -127 and
+// lands on the -127 floor like every amax below 448 * 2^-128.
 __device__ __forceinline__ int block_exponent(float amax) {
   if (!(amax > 0.f)) return 0;
   const uint32_t u = __builtin_bit_cast(uint32_t, amax);
   const int E = (int)((u >> 23) & 0xFF) - 127;
-  return E - 8 + ((u & 0x7FFFFF) > 0x600000 ? 1 : 0);  // mantissa above 1.75
+  return max(-127, E - 8 + ((u & 0x7FFFFF) > 0x600000 ? 1 : 0));  // mantissa above 1.75
+}
+
+__device__ __forceinline__ float exp2i(int k) {  // 2^k, -126 <= k <= 127
+  return __builtin_bit_cast(float, (uint32_t)(k + 127) << 23);
 }
 
 // ---------------------------------------------------------------------------
-// Quantisation: one wave per 64-row block of one head, one lane per row.
-template <typename T, int D, bool VLAYOUT>
+// Quantisation: one wave per 64-row block of one head, one lane per row; Q, K
+// and V blocks in one launch.  The block's rows are copied into LDS with
+// contiguous 1 KiB copies, each lane then reads its own row (XOR-swizzled
+// 16-byte chunks keep those reads free of bank conflicts), and the codes leave
+// through LDS again so that the global stores are contiguous too.
+template <int CPR>
+__device__ __forceinline__ int swzq(int r) {  // chunk swizzle of a CPR-chunk row
+  return CPR == 16 ? (r & 15) : CPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+
+template <typename T, int D>
 __global__ __launch_bounds__(64) void fp8_quant_kernel(Fp8QuantParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[VLAYOUT ? 64 * D : 16];
+  constexpr int RB = 2 * D;      // input row bytes
+  constexpr int CPR = RB / 16;   // input chunks per row
+  constexpr int OCPR = D / 16;   // code chunks per row
+  __shared__ __attribute__((aligned(16))) char tile[64 * RB];
   const int lane = threadIdx.x;
   const int nblk = p.N64 / 64;
-  const int head = blockIdx.x / nblk;
-  const int blk = blockIdx.x % nblk;
-  const int n = blk * 64 + lane;
+  // which tensor (uniform per workgroup): Q, then K, then V
+  int idx = blockIdx.x;
+  int t = 0;
+  if (idx >= p.nq_wg) {
+    idx -= p.nq_wg;
+    t = 1;
+    if (idx >= p.nk_wg) {
+      idx -= p.nk_wg;
+      t = 2;
+    }
+  }
+  const void* x = t == 0 ? p.x0 : t == 1 ? p.x1 : p.x2;
+  uint8_t* codes = t == 0 ? p.c0 : t == 1 ? p.c1 : p.c2;
+  int8_t* exps = t == 0 ? p.e0 : t == 1 ? p.e1 : p.e2;
+  const int head = idx / nblk;
+  const int blk = idx % nblk;
+
+  // rows blk*64 .. +63 of the head; rows past N read as zeros
+  const Buf bx = make_buf((const char*)x + (size_t)head * p.N * RB, (uint32_t)p.N * RB);
+#pragma unroll
+  for (int it = 0; it < CPR; ++it) {
+    const int P = it * 64 + lane, r = P / CPR, sl = P % CPR;
+    dma16(bx, (uint32_t)((blk * 64 + r) * RB + ((sl ^ swzq<CPR>(r)) << 4)), tile + it * 1024);
+  }
+  wait_all_memory();
+  __syncthreads();
 
   float y[D];
-  const T* xrow = (const T*)p.x + ((size_t)head * p.N + (n < p.N ? n : 0)) * D;
 #pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    u32x4 w = n < p.N ? *(const u32x4*)(xrow + c) : u32x4{0, 0, 0, 0};
+  for (int c = 0; c < CPR; ++c) {
+    const u32x4 w = *(const u32x4*)(tile + lane * RB + ((c ^ swzq<CPR>(lane)) << 4));
     const T* e = (const T*)&w;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[c + i] = to_f32(e[i]) * p.signs[c + i];
+    for (int i = 0; i < 8; ++i) y[8 * c + i] = to_f32(e[i]) * p.signs[8 * c + i];
   }
   // fast Walsh-Hadamard transform: pair distances 1, 2, ..., D/2
 #pragma unroll
@@ -124,38 +164,54 @@ __global__ __launch_bounds__(64) void fp8_quant_kernel(Fp8QuantParams p) {
         y[i] = a + b;
         y[i + h] = a - b;
       }
+  // The rotated row is fl(y * c), c = float32(1 / sqrt(d)), and its codes are
+  // E4M3(fl(y * c) * 2^-e).  Rounding is monotone, so the block maximum is
+  // fl(max|y| * c).  For e >= -100, every element that E4M3 does not round
+  // to zero has |y c| >= 2^-110 (normal), and c * 2^-e is an exact float32,
+  // so fl(y * (c * 2^-e)) = fl(y * c) * 2^-e: one multiply per element gives
+  // the same codes.  Smaller blocks (magnitudes near float32 underflow, where
+  // fl(y * c) may be subnormal) take both roundings in turn.
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
-    y[i] *= inv_sqrt_d<D>();
-    amax = fmaxf(amax, fabsf(y[i]));
-  }
+  for (int i = 0; i < D; ++i) amax = fmaxf(amax, fabsf(y[i]));
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-  const int e = block_exponent(amax);
-  const float inv = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);  // 2^-e, exact
+  const int e = block_exponent(amax * inv_sqrt_d<D>());
+  float mul = inv_sqrt_d<D>() * exp2i(-e);  // exact
+  if (e < -100) {  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < D; ++i) y[i] *= inv_sqrt_d<D>();
+    mul = exp2i(-e);
+  }
   uint32_t w[D / 4];
 #pragma unroll
   for (int j = 0; j < D / 4; ++j) {
-    w[j] = fp8x2<false>(y[4 * j] * inv, y[4 * j + 1] * inv, 0u);
-    w[j] = fp8x2<true>(y[4 * j + 2] * inv, y[4 * j + 3] * inv, w[j]);
+    w[j] = fp8x2<false>(y[4 * j] * mul, y[4 * j + 1] * mul, 0u);
+    w[j] = fp8x2<true>(y[4 * j + 2] * mul, y[4 * j + 3] * mul, w[j]);
   }
-  if (lane == 0) p.exps[(size_t)head * nblk + blk] = (int8_t)e;
-  if constexpr (!VLAYOUT) {
-    uint8_t* out = p.codes + ((size_t)head * p.N64 + n) * D;
+  if (lane == 0) exps[(size_t)head * nblk + blk] = (int8_t)e;
+
+  // codes of the block, row-major with swizzled chunks, at the start of tile
+  __syncthreads();  // every lane has read its input row
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) *(u32x4*)(out + 16 * j) = u32x4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+  for (int j = 0; j < OCPR; ++j)
+    *(u32x4*)(tile + lane * D + ((j ^ swzq<OCPR>(lane)) << 4)) = u32x4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+  __syncthreads();
+  if (t != 2) {
+    uint8_t* out = codes + ((size_t)head * p.N64 + blk * 64) * D;
+#pragma unroll
+    for (int it = 0; it < OCPR; ++it) {
+      const int P = it * 64 + lane, r = P / OCPR, pos = P % OCPR;
+      *(u32x4*)(out + r * D + ((pos ^ swzq<OCPR>(r)) << 4)) = *(const u32x4*)(tile + P * 16);
+    }
   } else {
-    // transpose through LDS: output row c of the tile = column c, bytes in
-    // the key order kappa
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j)
-      *(u32x4*)(tile + lane * D + 16 * j) = u32x4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
-    __syncthreads();
-    uint8_t* out = p.codes + ((size_t)head * nblk + blk) * D * 64;
+    // V: row c of the output tile = column c of the codes, byte p of it the
+    // code of key kappa(p); built in the second half of tile, then stored
+    // contiguously
+    char* otile = tile + 64 * D;
 #pragma unroll
     for (int rr = 0; rr < D / 64; ++rr) {
-      const int c = rr * 64 + lane;  // column of V = row of the tile
+      const int c = rr * 64 + lane;
       uint32_t ow[16];
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -164,13 +220,21 @@ __global__ __launch_bounds__(64) void fp8_quant_kernel(Fp8QuantParams p) {
         for (int bt = 0; bt < 4; ++bt) {
           const int pp = q * 4 + bt, h = pp >> 5, i = pp & 31;
           const int key = (i >> 4) * 32 + ((i & 15) >> 2) * 8 + 4 * h + (i & 3);
-          word |= (uint32_t)tile[key * D + c] << (8 * bt);
+          const int off = key * D + (((c >> 4) ^ swzq<OCPR>(key)) << 4) + (c & 15);
+          word |= (uint32_t)(uint8_t)tile[off] << (8 * bt);
         }
         ow[q] = word;
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *(u32x4*)(out + (size_t)c * 64 + 16 * q) = u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]};
+        *(u32x4*)(otile + c * 64 + 16 * q) = u32x4{ow[4 * q], ow[4 * q + 1], ow[4 * q + 2], ow[4 * q + 3]};
+    }
+    __syncthreads();
+    uint8_t* out = codes + ((size_t)head * nblk + blk) * D * 64;
+#pragma unroll
+    for (int it = 0; it < D / 16; ++it) {
+      const int P = it * 64 + lane;
+      *(u32x4*)(out + P * 16) = *(const u32x4*)(otile + P * 16);
     }
   }
 }
@@ -410,12 +474,8 @@ void fp8_fwd_kernel(Fp8FwdParams p) {
 }
 
 template <typename T, int D>
-hipError_t quant_t(Fp8QuantParams qp, bool vlayout, int heads, hipStream_t s) {
-  dim3 grid(heads * (qp.N64 / 64)), block(64);
-  if (vlayout)
-    hipLaunchKernelGGL((fp8_quant_kernel<T, D, true>), grid, block, 0, s, qp);
-  else
-    hipLaunchKernelGGL((fp8_quant_kernel<T, D, false>), grid, block, 0, s, qp);
+hipError_t quant_t(const Fp8QuantParams& qp, int wgs, hipStream_t s) {
+  hipLaunchKernelGGL((fp8_quant_kernel<T, D>), dim3(wgs), dim3(64), 0, s, qp);
   return hipGetLastError();
 }
 
@@ -432,10 +492,9 @@ hipError_t fwd8_t(const Fp8FwdParams& p, bool causal, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fp8_quantize(const Fp8QuantParams& qp, int dtype, int d, bool vlayout, int heads,
-                               hipStream_t s) {
-  if (dtype == 1) return d == 64 ? quant_t<_Float16, 64>(qp, vlayout, heads, s) : quant_t<_Float16, 128>(qp, vlayout, heads, s);
-  return d == 64 ? quant_t<__bf16, 64>(qp, vlayout, heads, s) : quant_t<__bf16, 128>(qp, vlayout, heads, s);
+hipError_t launch_fp8_quantize(const Fp8QuantParams& qp, int dtype, int d, int wgs, hipStream_t s) {
+  if (dtype == 1) return d == 64 ? quant_t<_Float16, 64>(qp, wgs, s) : quant_t<_Float16, 128>(qp, wgs, s);
+  return d == 64 ? quant_t<__bf16, 64>(qp, wgs, s) : quant_t<__bf16, 128>(qp, wgs, s);
 }
 
 hipError_t launch_fp8_fwd(const Fp8FwdParams& p, int dtype, int d, bool causal, hipStream_t s) {

@@ -96,10 +96,18 @@ struct DecParams {
 // FP8 forward (fa_fp8.hip): rotation + block quantisation, then attention on
 // the codes.
 struct Fp8QuantParams {
-  const void* x;        // (heads, N, d) input in the problem dtype
-  uint8_t* codes;       // row-major (heads, N64, d) or V tiles (heads, N64/64, d, 64)
-  int8_t* exps;         // (heads, N64 / 64) block exponents
+  const void* x0;       // Q (B*H, N, d) in the problem dtype
+  const void* x1;       // K (B*H_kv, N, d)
+  const void* x2;       // V (B*H_kv, N, d)
+  uint8_t* c0;          // Q codes, row-major (B*H, N64, d)
+  uint8_t* c1;          // K codes, row-major (B*H_kv, N64, d)
+  uint8_t* c2;          // V codes, tiles (B*H_kv, N64/64, d, 64)
+  int8_t* e0;           // block exponents (heads, N64 / 64) of Q, K, V
+  int8_t* e1;
+  int8_t* e2;
   const float* signs;   // d random signs of the rotation
+  int nq_wg;            // workgroups (64-row blocks) of Q
+  int nk_wg;            // of K (V has as many)
   int N;
   int N64;              // N rounded up to a multiple of 64
 };
@@ -163,8 +171,7 @@ hipError_t launch_bwd_dq_drop(const BwdParams& p, int dtype, int d, bool causal,
 hipError_t launch_bwd_dkdv_drop(const BwdParams& p, int dtype, int d, bool causal, bool masked,
                                 hipStream_t s);
 hipError_t launch_decode(const DecParams& p, int dtype, int d, bool causal, hipStream_t s);
-hipError_t launch_fp8_quantize(const Fp8QuantParams& qp, int dtype, int d, bool vlayout, int heads,
-                               hipStream_t s);
+hipError_t launch_fp8_quantize(const Fp8QuantParams& qp, int dtype, int d, int wgs, hipStream_t s);
 hipError_t launch_fp8_fwd(const Fp8FwdParams& p, int dtype, int d, bool causal, hipStream_t s);
 hipError_t launch_f32_fwd(const F32Params& p, hipStream_t s);
 hipError_t launch_f32_dq(const F32Params& p, hipStream_t s);

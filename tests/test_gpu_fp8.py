@@ -72,11 +72,16 @@ def _v_rowmajor(vc):
     return out.reshape(hk, nt * 64, d)
 
 
+TINY = {"tiny": 2.0 ** -120, "small": 2.0 ** -95}  # magnitudes near float32 underflow
+
+
 def _inputs(kind, B, H, hkv, N, d, dtype, qmul=1.0):
     gen = make_outlier_inputs if kind == "outlier" else make_inputs
     q, k, v, _ = gen(B, H, N, d, dtype, hkv=hkv)
     if qmul != 1.0:
         q = (q.float() * qmul).to(q.dtype)
+    if kind in TINY:
+        q, k, v = ((x.float() * TINY[kind]).to(x.dtype) for x in (q, k, v))
     return q, k, v
 
 
@@ -149,6 +154,8 @@ CASES = [
     ("normal", "f16", 128, 1, 2, 2, 700, False, 100, 1.0),    # two-sided window
     ("normal", "bf16", 64, 1, 2, 2, 1024, True, 0, 6.0),      # peaked rows: the lazy reference moves
     ("normal", "f16", 128, 2, 2, 1, 640, False, 0, 4.0),
+    ("tiny", "bf16", 128, 1, 2, 2, 200, True, 0, 1.0),      # block exponents at the -127 floor
+    ("small", "bf16", 64, 1, 2, 2, 200, False, 0, 1.0),     # exponents near -100
 ]
 
 
