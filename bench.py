@@ -12,12 +12,17 @@ Reported value: fwd+bwd TFLOP/s with matrix-core FLOPs counted over kept
 (Q K^T, P V; the score recompute, dV, dP, dK, dQ).  The backward's extra
 score/dP recompute in the dQ kernel is work done but not credited.
 
+Before the warm-up steps the step runs untimed for --settle-ms (300 ms by
+default) so that the timed region sees the GPU's sustained clocks rather than
+their ramp; the JSON line reports the value it used.
+
 Prints ONE JSON line (plus a few human-readable lines on stderr).
 """
 
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import platform
@@ -33,6 +38,7 @@ METRIC = "attention fwd+bwd TFLOP/s (B64·H16·N1024·d64 fp16 causal), % of MFM
 # FLOP/clk x 2.4 GHz), HBM3E 8 TB/s.
 PEAK_MFMA_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 2 * PEAK_MFMA_TFLOPS  # dense E4M3 matrix rate, twice the 16-bit one
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -87,6 +93,26 @@ def kernel_work(w):
     }
 
 
+def settle(step, ms):
+    """Run `step` untimed for at least `ms` milliseconds of wall time before
+    the warm-up steps: the GPU raises its clocks over the first tens of
+    milliseconds of sustained load, and a short timed region would otherwise
+    measure that ramp rather than the steady rate."""
+    import torch
+
+    if ms <= 0:
+        return 0
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        step()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def decode_bench(w, args, dev):
     """Decode workload: n_q queries per head against N keys.  Bound by HBM:
     its algorithmic bytes are K and V once plus Q, O and LSE.  Prints one
@@ -102,6 +128,8 @@ def decode_bench(w, args, dev):
     lse = torch.empty((w.B, w.H, w.nq), dtype=torch.float32, device=dev)
     log(f"[bench] workload {w.name}: B={w.B} H={w.H} H_kv={w.H_kv} N={w.N} n_q={w.nq} d={w.d} "
         f"{w.dtype} causal={w.causal}; warmup {args.warmup}, steps {args.steps}")
+    settle(lambda: fa_fwd_decode(q, k, v, causal=w.causal, scale=w.scale, window=w.window,
+                                 out=o, lse=lse), args.settle_ms)
     for _ in range(args.warmup):
         fa_fwd_decode(q, k, v, causal=w.causal, scale=w.scale, window=w.window, out=o, lse=lse)
     torch.cuda.synchronize()
@@ -122,7 +150,7 @@ def decode_bench(w, args, dev):
         f"{nbytes / 1e6:.1f} MB -> {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of HBM peak)")
     out = {
         "metric": f"decode attention forward HBM GB/s ({w.name})", "value": round(gbs, 1),
-        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "n_q": w.nq,
@@ -130,6 +158,77 @@ def decode_bench(w, args, dev):
         "roofline": {"kernel": "decode", "bound": "hbm", "achieved": round(ms_ev and nbytes / (ms_ev / 1e3) / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(nbytes / (ms_ev / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def fp8_bench(w, args, dev):
+    """FP8 workload: one step = quantise Q, K, V (rotation + block scales)
+    then attention on the codes.  value = forward FLOPs of the attention /
+    step time; the attention kernel is rated against the dense FP8 matrix
+    peak, the quantiser against HBM (bf16 in, one byte per element out)."""
+    import torch
+
+    from io_aware_exact_fwd_amd import fa_fwd_fp8, fp8_quantize
+    from io_aware_exact_fwd_amd.binding import lib, _stream
+    from io_aware_exact_fwd_amd.workloads import fwd_flops, make_inputs, make_signs
+
+    q, k, v, _ = (t.to(dev) for t in make_inputs(w.B, w.H, w.N, w.d, w.dtype, hkv=w.H_kv))
+    signs = make_signs(w.d).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    p, ws = fp8_quantize(q, k, v, signs, w.causal, w.scale, w.window)
+    L = lib()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        st = L.fa_fp8_quantize(ctypes.byref(p), signs.data_ptr(), q.data_ptr(), k.data_ptr(),
+                               v.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q))
+        if ev is not None:
+            ev[1].record()
+        st |= L.fa_fwd_fp8(ctypes.byref(p), signs.data_ptr(), ws.data_ptr(), ws.numel(),
+                           o.data_ptr(), lse.data_ptr(), _stream(q))
+        if ev is not None:
+            ev[2].record()
+        if st:
+            raise RuntimeError(f"FP8 path failed ({st})")
+
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} H_kv={w.H_kv} N={w.N} d={w.d} {w.dtype} "
+        f"causal={w.causal}, FP8 path; warmup {args.warmup}, steps {args.steps}")
+    settle(step, args.settle_ms)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_q = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    ms_a = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    flops = fwd_flops(w)
+    value = flops / (ms_step / 1e3) / 1e12
+    elems = (w.B * w.H + 2 * w.B * w.H_kv) * w.N * w.d
+    qbytes = elems * (2 + 1)
+    ach = flops / (ms_a / 1e3) / 1e12
+    log(f"[bench] quantise {ms_q * 1e3:.1f} us ({qbytes / (ms_q / 1e3) / 1e9:.0f} GB/s), "
+        f"attention {ms_a * 1e3:.1f} us ({ach:.1f} TFLOP/s, {100 * ach / PEAK_FP8_TFLOPS:.1f}% "
+        f"of the FP8 peak); step {ms_step * 1e3:.1f} us -> {value:.1f} TFLOP/s")
+    out = {
+        "metric": f"FP8 attention forward TFLOP/s ({w.name})", "value": round(value, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "d": w.d,
+                   "dtype": w.dtype, "causal": w.causal, "scale": w.scale},
+        "kernel_ms": {"fp8_quantize": round(ms_q, 5), "fp8_fwd": round(ms_a, 5)},
+        "roofline": {"kernel": "fp8_fwd", "bound": "mfma", "achieved": round(ach, 1),
+                     "peak": round(PEAK_FP8_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None},
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
@@ -275,6 +374,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed run of the step before the warm-up steps, in ms of wall "
+                         "time (clock ramp-up; 0 to skip)")
     ap.add_argument("--workload", default="gpt2_medium")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU budget of the oracle baseline (0 to skip)")
@@ -329,6 +431,9 @@ def main():
     if w.nq:
         decode_bench(w, args, dev)
         return
+    if w.fp8:
+        fp8_bench(w, args, dev)
+        return
     inputs = make_inputs(w.B, w.H, w.N, w.d, w.dtype)
     q, k, v, do = (t.to(dev) for t in inputs)
     bm = w.block_mask()
@@ -353,6 +458,7 @@ def main():
 
     log(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} "
         f"causal={w.causal} mask={w.mask}; warmup {args.warmup}, steps {args.steps}")
+    settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -398,7 +504,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup, "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -100,6 +100,10 @@ __device__ __forceinline__ float exp2i(int k) {  // 2^k, -126 <= k <= 127
   return __builtin_bit_cast(float, (uint32_t)(k + 127) << 23);
 }
 
+#ifndef FA_Q8_WPE
+#define FA_Q8_WPE 1  // waves per SIMD the d = 128 quantiser is compiled for (1: no limit)
+#endif
+
 // ---------------------------------------------------------------------------
 // Quantisation: one wave per 64-row block of one head, one lane per row; Q, K
 // and V blocks in one launch.  The block's rows are copied into LDS with
@@ -112,7 +116,8 @@ __device__ __forceinline__ int swzq(int r) {  // chunk swizzle of a CPR-chunk ro
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(64) void fp8_quant_kernel(Fp8QuantParams p) {
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_eu(D == 128 ? FA_Q8_WPE : 1)))
+void fp8_quant_kernel(Fp8QuantParams p) {
   constexpr int RB = 2 * D;      // input row bytes
   constexpr int CPR = RB / 16;   // input chunks per row
   constexpr int OCPR = D / 16;   // code chunks per row
