@@ -38,6 +38,9 @@ namespace fa {
 #ifndef FA_DKDV_QT
 #define FA_DKDV_QT 64
 #endif
+#ifndef FA_DKDV_NST
+#define FA_DKDV_NST 3  // LDS stages of the d = 64 dK/dV ring (2 or 3)
+#endif
 #ifndef FA_DKDV64_WPE
 #define FA_DKDV64_WPE 2
 #endif
@@ -243,7 +246,11 @@ template <int D>
 struct DkvGeom {
   static constexpr int QT = FA_DKDV_QT;     // queries per step
   static constexpr int TBYTES = QT * D * 2;  // Q / dO tile, swizzled (no padding)
-  static constexpr int STAGE = 2 * TBYTES + 2 * QT * 4;  // Q, dO, lse2, D
+  static constexpr int LBYTES = 256;         // LSE (or D) of the step's rows, one dword per lane
+  static constexpr int STAGE = 2 * TBYTES + 2 * LBYTES;  // Q, dO, LSE, D
+  static constexpr int NST = D == 64 ? FA_DKDV_NST : 2;   // stages in the LDS ring
+  static constexpr int COPIES = 2 * (QT * D / 8 / 256);    // Q and dO copies per thread per step
+  static_assert(QT <= 64, "LSE / D rows of a step fit one 64-lane copy");
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
   static constexpr int NQB = QT / 32;       // 32-query blocks per step
@@ -256,7 +263,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
 void bwd_dkdv_kernel(BwdParams p) {
   using G = DkvGeom<D>;
   using V8 = typename Vec8<T>::type;
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
+  __shared__ __attribute__((aligned(16))) char smem[G::NST * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -292,6 +299,11 @@ void bwd_dkdv_kernel(BwdParams p) {
     kf[t] = __builtin_bit_cast(V8, buf_load16(bk, off));
     vf[t] = __builtin_bit_cast(V8, buf_load16(bv, off));
   }
+  // Wait for these here: the copies below are invisible to the compiler's
+  // own wait counting, which would otherwise wait inside the loop for loads
+  // it still thinks pending -- and, counts being in issue order, for the
+  // prefetch copies issued after them.
+  wait_all_memory();
 
   f32x16 dka[G::NDB], dva[G::NDB];
 #pragma unroll
@@ -300,53 +312,69 @@ void bwd_dkdv_kernel(BwdParams p) {
     dva[i] = f32x16{0};
   }
 
-  // Q and dO tiles go straight from global memory to LDS (no registers, no
-  // store instructions); LSE and D through registers.
-  float plse = 0.f, pdv = 0.f;
-  int pqq = 0;
-  auto gload = [&](int it, int stage) {
+  // Q, dO, LSE and D of a step go straight from global memory to LDS (no
+  // registers, no store instructions): Q and dO by all waves, LSE and D by
+  // wave 0, one row per lane (lanes past QT and rows past N read as zeros;
+  // such rows are hidden by the masks).  With NST = 3 stages the copies of
+  // step it + 2 are issued at the start of step it, so a step waits only for
+  // copies issued a whole step earlier.
+  auto gload = [&](int it, char* st) {
     const int r = it / nqt;
     const int qs = tiles.pos0(it - r * nqt);
     const size_t qh = (size_t)kvh * p.group + r;  // query head
     const Buf bq = make_buf((const T*)p.q + qh * N * D, head_bytes);
     const Buf bdo = make_buf((const T*)p.dout + qh * N * D, head_bytes);
-    char* qs_ = smem + stage * G::STAGE;
-    dma_tile<D, G::QT>(bq, qs, qs_, wave, lane);
-    dma_tile<D, G::QT>(bdo, qs, qs_ + G::TBYTES, wave, lane);
-    // raw values now (rows clamped into the sequence), converted when stored,
-    // so that nothing waits for these loads before the tile's work
-    if (tid < G::QT) {
-      pqq = qs + tid;
-      const size_t row = qh * N + min(pqq, N - 1);
-      plse = p.lse[row];
-      pdv = p.dvec[row];
+    dma_tile<D, G::QT>(bq, qs, st, wave, lane);
+    dma_tile<D, G::QT>(bdo, qs, st + G::TBYTES, wave, lane);
+    if (wave == 0) {
+      const Buf bl = make_buf(p.lse + qh * N, (uint32_t)N * 4);
+      const Buf bd = make_buf(p.dvec + qh * N, (uint32_t)N * 4);
+      const uint32_t off = lane < G::QT ? (uint32_t)(qs + lane) * 4 : 0x80000000u;
+      dma4(bl, off, st + 2 * G::TBYTES);
+      dma4(bd, off, st + 2 * G::TBYTES + G::LBYTES);
     }
   };
-  auto lstore = [&](int stage) {
-    float* ls = (float*)(smem + stage * G::STAGE + 2 * G::TBYTES);
-    if (tid < G::QT) {
-      // rows past the end or with no visible key: P = 0 (LSE2 = +inf)
-      const bool live = pqq < N && plse != kNegInf;
-      ls[tid] = live ? plse * kLog2e : __builtin_huge_valf();
-      ls[G::QT + tid] = pqq < N ? (DROP ? pdv / p.drop.mult : pdv) : 0.f;  // D / mult: see the dS step
+  // Wait until this wave's copies of the next step have landed (those of the
+  // step after it may stay in flight), then wave 0 converts that step's rows
+  // in place: LSE -> LSE log2(e) (+inf for a row with no visible key, so P =
+  // 0), D -> D / mult under dropout (see the dS step).  The barrier that
+  // follows publishes the stage.
+  auto land_next = [&](bool younger_in_flight, char* st) {
+    if (G::NST > 2 && younger_in_flight) {
+      if (wave == 0)
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(G::COPIES + 2));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(G::COPIES));
+    } else {
+      wait_all_memory();
+    }
+    if (wave == 0) {
+      float* ls = (float*)(st + 2 * G::TBYTES);
+      float* ds = (float*)(st + 2 * G::TBYTES + G::LBYTES);
+#pragma unroll
+      for (int i = lane; i < G::QT; i += 64) {
+        const float l = ls[i];
+        ls[i] = l != kNegInf ? l * kLog2e : __builtin_huge_valf();
+        if constexpr (DROP) ds[i] = ds[i] / p.drop.mult;
+      }
     }
   };
 
   const int ntiles = nqt * p.group;
-  if (ntiles > 0) {
-    gload(0, 0);
-    lstore(0);
-  }
-  wait_all_memory();
+  if (ntiles > 0) gload(0, smem);
+  if (G::NST > 2 && ntiles > 1) gload(1, smem + G::STAGE);
+  land_next(ntiles > 1, smem);
   __syncthreads();
 
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
+  int cur = 0;
   for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
-    const bool more = it + 1 < ntiles;
-    if (more) gload(it + 1, cur ^ 1);
+    if (it + G::NST - 1 < ntiles) {
+      const int st = cur + G::NST - 1 >= G::NST ? cur - 1 : cur + G::NST - 1;
+      gload(it + G::NST - 1, smem + st * G::STAGE);
+    }
 
     const int qs0 = tiles.pos0(it % nqt);
     const int qh = kvh * p.group + it / nqt;  // query head of this step
@@ -404,11 +432,11 @@ void bwd_dkdv_kernel(BwdParams p) {
         u32x4 kw;
         if constexpr (DROP)
           kw = drop_bytes_key_lanes(p.drop, (uint32_t)qh, kw0, qs0 + qb * 32,
-                                    smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
+                                    smem + G::NST * G::STAGE + wave * kDropLdsPerWave, lane);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const f32x4 l4 = *(const f32x4*)(lsm + qb * 32 + rr * 8 + g * 4);
-          const f32x4 d4 = *(const f32x4*)(lsm + G::QT + qb * 32 + rr * 8 + g * 4);
+          const f32x4 d4 = *(const f32x4*)(lsm + G::LBYTES / 4 + qb * 32 + rr * 8 + g * 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = rr * 4 + e;
@@ -441,25 +469,40 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
       }
     }
-    if (more) lstore(cur ^ 1);
-    wait_all_memory();  // this thread's copies into the next stage have landed
+    if (it + 1 < ntiles) land_next(it + 2 < ntiles, smem + (cur + 1 == G::NST ? 0 : cur + 1) * G::STAGE);
     __syncthreads();
+    cur = cur + 1 == G::NST ? 0 : cur + 1;
   }
 
-  // C layout: lane -> head-dim column, register -> key row
+  // C layout: lane -> head-dim column, register -> key row.  Each wave turns
+  // its 32 x D blocks of dK and dV into row-major order in LDS (the stages
+  // are free once every wave has left the loop), then stores 16-byte pieces
+  // of whole rows.
+  static_assert(4 * 2 * 32 * D * (int)sizeof(T) <= G::NST * G::STAGE, "epilogue fits the stages");
   const float fk = DROP ? p.scale * p.drop.mult : p.scale;
   const float fv = DROP ? p.drop.mult : 1.f;
+  __syncthreads();
+  T* ek = (T*)(smem + wave * 2 * 32 * D * sizeof(T));
+  T* ev = ek + 32 * D;
 #pragma unroll
   for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kr = kw0 + (r >> 2) * 8 + g * 4 + (r & 3);
-      if (kr < N) {
-        const size_t idx = kv_off + (size_t)kr * D + db * 32 + l32;
-        ((T*)p.dk)[idx] = (T)(dka[db][r] * fk);
-        ((T*)p.dv)[idx] = (T)(dva[db][r] * fv);
-      }
+      const int row = (r >> 2) * 8 + g * 4 + (r & 3);
+      ek[row * D + db * 32 + l32] = (T)(dka[db][r] * fk);
+      ev[row * D + db * 32 + l32] = (T)(dva[db][r] * fv);
     }
+  __syncthreads();
+  constexpr int CPR = D / 8;  // 16-byte pieces per row
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / 64; ++i) {
+    const int c = i * 64 + lane, row = c / CPR, piece = c % CPR;
+    if (kw0 + row < N) {
+      const size_t idx = kv_off + (size_t)(kw0 + row) * D + piece * 8;
+      *(u32x4*)((T*)p.dk + idx) = *(const u32x4*)(ek + row * D + piece * 8);
+      *(u32x4*)((T*)p.dv + idx) = *(const u32x4*)(ev + row * D + piece * 8);
+    }
+  }
 }
 
 template <typename T, int D, bool DROP>

@@ -165,6 +165,15 @@ __device__ __forceinline__ void dma16(const Buf& b, uint32_t byte_off, char* blo
                : "s"(m0), "v"(byte_off), "s"(b.r)
                : "memory", "m0");
 }
+// The 4-byte form: lane i's dword lands at block + 4 i (256 bytes per wave);
+// each lane's dword is range-checked on its own.
+__device__ __forceinline__ void dma4(const Buf& b, uint32_t byte_off, char* block) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)block;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(byte_off), "s"(b.r)
+               : "memory", "m0");
+}
 
 // Copy rows [r0, r0 + ROWS) of a row-major (rows x D) 16-bit tensor held by
 // buffer b into the swizzled tile at `tile` (256 threads; each issues
@@ -247,6 +256,10 @@ struct IntC {
 // before the loop (operands kept in registers) into every iteration, where it
 // would also wait for the prefetch of the next tile.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// s_waitcnt operand: at most n vector-memory operations of this wave still
+// outstanding (they complete in issue order), no wait on the other counters.
+constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Wave index as a wave-uniform (scalar) value, so that branches on it stay
 // scalar branches instead of being if-converted.

@@ -38,10 +38,6 @@ struct DecGeom {
   static constexpr int COPIES = 2 * KT * D / 8 / 256;  // copies per thread per tile (K and V)
 };
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding and nothing else (expcnt and lgkmcnt at maximum).
-constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 template <typename T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(DecParams p) {
