@@ -100,29 +100,32 @@ __device__ __forceinline__ float exp2i(int k) {  // 2^k, -126 <= k <= 127
   return __builtin_bit_cast(float, (uint32_t)(k + 127) << 23);
 }
 
-#ifndef FA_Q8_WPE
-#define FA_Q8_WPE 1  // waves per SIMD the d = 128 quantiser is compiled for (1: no limit)
-#endif
-
 // ---------------------------------------------------------------------------
-// Quantisation: one wave per 64-row block of one head, one lane per row; Q, K
-// and V blocks in one launch.  The block's rows are copied into LDS with
-// contiguous 1 KiB copies, each lane then reads its own row (XOR-swizzled
-// 16-byte chunks keep those reads free of bank conflicts), and the codes leave
-// through LDS again so that the global stores are contiguous too.
+// Quantisation: one workgroup of two waves per 64-row block of one head; a
+// wave holds 32 rows, lane l the first half of its row and lane l + 32 the
+// second half, so a lane keeps d/2 values in registers.  Q, K and V blocks
+// share one launch.  The block's rows are copied into LDS with contiguous
+// 1 KiB copies, each lane reads its half row (XOR-swizzled 16-byte chunks keep
+// those reads free of bank conflicts), and the codes leave through LDS again
+// so that the global stores are contiguous too.
 template <int CPR>
 __device__ __forceinline__ int swzq(int r) {  // chunk swizzle of a CPR-chunk row
   return CPR == 16 ? (r & 15) : CPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
 template <typename T, int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_eu(D == 128 ? FA_Q8_WPE : 1)))
-void fp8_quant_kernel(Fp8QuantParams p) {
+__global__ __launch_bounds__(128) void fp8_quant_kernel(Fp8QuantParams p) {
   constexpr int RB = 2 * D;      // input row bytes
   constexpr int CPR = RB / 16;   // input chunks per row
   constexpr int OCPR = D / 16;   // code chunks per row
+  constexpr int H = D / 2;       // values per lane
   __shared__ __attribute__((aligned(16))) char tile[64 * RB];
-  const int lane = threadIdx.x;
+  __shared__ float wave_max[2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_id();
+  const int g = lane >> 5;                 // which half of the row
+  const int r = wave * 32 + (lane & 31);   // row within the block
   const int nblk = p.N64 / 64;
   // which tensor (uniform per workgroup): Q, then K, then V
   int idx = blockIdx.x;
@@ -141,34 +144,44 @@ void fp8_quant_kernel(Fp8QuantParams p) {
   const int head = idx / nblk;
   const int blk = idx % nblk;
 
-  // rows blk*64 .. +63 of the head; rows past N read as zeros
+  // rows blk*64 .. +63 of the head (rows past N read as zeros): CPR copies of
+  // 1 KiB, copy n of wave w filling block 2n + w
   const Buf bx = make_buf((const char*)x + (size_t)head * p.N * RB, (uint32_t)p.N * RB);
 #pragma unroll
-  for (int it = 0; it < CPR; ++it) {
-    const int P = it * 64 + lane, r = P / CPR, sl = P % CPR;
-    dma16(bx, (uint32_t)((blk * 64 + r) * RB + ((sl ^ swzq<CPR>(r)) << 4)), tile + it * 1024);
+  for (int n = 0; n < CPR / 2; ++n) {
+    const int P = (2 * n + wave) * 64 + lane, rr = P / CPR, sl = P % CPR;
+    dma16(bx, (uint32_t)((blk * 64 + rr) * RB + ((sl ^ swzq<CPR>(rr)) << 4)), tile + (2 * n + wave) * 1024);
   }
   wait_all_memory();
   __syncthreads();
 
-  float y[D];
+  float y[H];
 #pragma unroll
-  for (int c = 0; c < CPR; ++c) {
-    const u32x4 w = *(const u32x4*)(tile + lane * RB + ((c ^ swzq<CPR>(lane)) << 4));
+  for (int c = 0; c < CPR / 2; ++c) {
+    const int cc = g * (CPR / 2) + c;
+    const u32x4 w = *(const u32x4*)(tile + r * RB + ((cc ^ swzq<CPR>(r)) << 4));
     const T* e = (const T*)&w;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[8 * c + i] = to_f32(e[i]) * p.signs[8 * c + i];
+    for (int i = 0; i < 8; ++i) y[8 * c + i] = to_f32(e[i]) * p.signs[g * H + 8 * c + i];
   }
-  // fast Walsh-Hadamard transform: pair distances 1, 2, ..., D/2
+  // fast Walsh-Hadamard transform, pair distances 1, 2, ..., D/2: the stages
+  // below D/2 inside the half row, the last one between the two halves
+  // (element i with element i + D/2, held by lane l ^ 32)
 #pragma unroll
-  for (int h = 1; h < D; h <<= 1)
+  for (int h = 1; h < H; h <<= 1)
 #pragma unroll
-    for (int i = 0; i < D; ++i)
+    for (int i = 0; i < H; ++i)
       if (!(i & h)) {
         const float a = y[i], b = y[i + h];
         y[i] = a + b;
         y[i + h] = a - b;
       }
+  const float sgn = g == 0 ? 1.f : -1.f;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const LanePair pr = lane_pair(y[i]);
+    y[i] = __builtin_fmaf(pr.hi, sgn, pr.lo);  // a + b or a - b, one rounding
+  }
   // The rotated row is fl(y * c), c = float32(1 / sqrt(d)), and its codes are
   // E4M3(fl(y * c) * 2^-e).  Rounding is monotone, so the block maximum is
   // fl(max|y| * c).  For e >= -100, every element that E4M3 does not round
@@ -178,45 +191,47 @@ void fp8_quant_kernel(Fp8QuantParams p) {
   // fl(y * c) may be subnormal) take both roundings in turn.
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < D; ++i) amax = fmaxf(amax, fabsf(y[i]));
+  for (int i = 0; i < H; ++i) amax = fmaxf(amax, fabsf(y[i]));
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  if (lane == 0) wave_max[wave] = amax;
+  __syncthreads();  // also: every lane has read its input row
+  amax = fmaxf(wave_max[0], wave_max[1]);
   const int e = block_exponent(amax * inv_sqrt_d<D>());
   float mul = inv_sqrt_d<D>() * exp2i(-e);  // exact
-  if (e < -100) {  // wave-uniform
+  if (e < -100) {  // uniform over the workgroup
 #pragma unroll
-    for (int i = 0; i < D; ++i) y[i] *= inv_sqrt_d<D>();
+    for (int i = 0; i < H; ++i) y[i] *= inv_sqrt_d<D>();
     mul = exp2i(-e);
   }
-  uint32_t w[D / 4];
+  uint32_t w[H / 4];
 #pragma unroll
-  for (int j = 0; j < D / 4; ++j) {
+  for (int j = 0; j < H / 4; ++j) {
     w[j] = fp8x2<false>(y[4 * j] * mul, y[4 * j + 1] * mul, 0u);
     w[j] = fp8x2<true>(y[4 * j + 2] * mul, y[4 * j + 3] * mul, w[j]);
   }
-  if (lane == 0) exps[(size_t)head * nblk + blk] = (int8_t)e;
+  if (tid == 0) exps[(size_t)head * nblk + blk] = (int8_t)e;
 
   // codes of the block, row-major with swizzled chunks, at the start of tile
-  __syncthreads();  // every lane has read its input row
 #pragma unroll
-  for (int j = 0; j < OCPR; ++j)
-    *(u32x4*)(tile + lane * D + ((j ^ swzq<OCPR>(lane)) << 4)) = u32x4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+  for (int j = 0; j < OCPR / 2; ++j) {
+    const int cc = g * (OCPR / 2) + j;
+    *(u32x4*)(tile + r * D + ((cc ^ swzq<OCPR>(r)) << 4)) = u32x4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+  }
   __syncthreads();
   if (t != 2) {
     uint8_t* out = codes + ((size_t)head * p.N64 + blk * 64) * D;
 #pragma unroll
-    for (int it = 0; it < OCPR; ++it) {
-      const int P = it * 64 + lane, r = P / OCPR, pos = P % OCPR;
-      *(u32x4*)(out + r * D + ((pos ^ swzq<OCPR>(r)) << 4)) = *(const u32x4*)(tile + P * 16);
+    for (int it = 0; it < OCPR / 2; ++it) {
+      const int P = it * 128 + tid, rr = P / OCPR, pos = P % OCPR;
+      *(u32x4*)(out + rr * D + ((pos ^ swzq<OCPR>(rr)) << 4)) = *(const u32x4*)(tile + P * 16);
     }
   } else {
     // V: row c of the output tile = column c of the codes, byte p of it the
     // code of key kappa(p); built in the second half of tile, then stored
     // contiguously
     char* otile = tile + 64 * D;
-#pragma unroll
-    for (int rr = 0; rr < D / 64; ++rr) {
-      const int c = rr * 64 + lane;
+    for (int c = tid; c < D; c += 128) {
       uint32_t ow[16];
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -237,8 +252,8 @@ void fp8_quant_kernel(Fp8QuantParams p) {
     __syncthreads();
     uint8_t* out = codes + ((size_t)head * nblk + blk) * D * 64;
 #pragma unroll
-    for (int it = 0; it < D / 16; ++it) {
-      const int P = it * 64 + lane;
+    for (int it = 0; it < D / 32; ++it) {
+      const int P = it * 128 + tid;
       *(u32x4*)(out + P * 16) = *(const u32x4*)(otile + P * 16);
     }
   }
@@ -480,7 +495,7 @@ void fp8_fwd_kernel(Fp8FwdParams p) {
 
 template <typename T, int D>
 hipError_t quant_t(const Fp8QuantParams& qp, int wgs, hipStream_t s) {
-  hipLaunchKernelGGL((fp8_quant_kernel<T, D>), dim3(wgs), dim3(64), 0, s, qp);
+  hipLaunchKernelGGL((fp8_quant_kernel<T, D>), dim3(wgs), dim3(128), 0, s, qp);
   return hipGetLastError();
 }
 
