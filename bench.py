@@ -471,12 +471,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ms = {"fwd": 0.0, "dq": 0.0, "dkdv": 0.0}
+    per = {"fwd": [], "dq": [], "dkdv": []}
     for ev in events:
-        ms["fwd"] += ev[0].elapsed_time(ev[1])
-        ms["dq"] += ev[1].elapsed_time(ev[2])
-        ms["dkdv"] += ev[2].elapsed_time(ev[3])
-    ms = {kk: vv / args.steps for kk, vv in ms.items()}
+        per["fwd"].append(ev[0].elapsed_time(ev[1]))
+        per["dq"].append(ev[1].elapsed_time(ev[2]))
+        per["dkdv"].append(ev[2].elapsed_time(ev[3]))
+    ms = {kk: sum(vv) / args.steps for kk, vv in per.items()}
+    med = {kk: sorted(vv)[len(vv) // 2] for kk, vv in per.items()}
+
+    # one cold step (outside the timed region): a 512 MiB write first evicts
+    # the inputs from L2 and the last-level cache
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    flush.fill_(1)
+    cold = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    torch.cuda.synchronize()
+    step(cold)
+    torch.cuda.synchronize()
+    cold_ms = cold[0].elapsed_time(cold[3])
+    del flush
     ms_step = wall * 1e3 / args.steps
     f_fwd, f_bwd = fwd_flops(w), bwd_flops(w)
     value = (f_fwd + f_bwd) / (ms_step / 1e3) / 1e12
@@ -491,7 +503,8 @@ def main():
             f"({100 * r['frac']:.1f}% of {r['bound']} peak)")
     log(f"[bench] step {ms_step * 1e3:.1f} us -> {value:.1f} TFLOP/s "
         f"({100 * value / PEAK_MFMA_TFLOPS:.1f}% of {PEAK_MFMA_TFLOPS:.0f}); fwd alone "
-        f"{f_fwd / (ms['fwd'] / 1e3) / 1e12:.1f} TFLOP/s")
+        f"{f_fwd / (ms['fwd'] / 1e3) / 1e12:.1f} TFLOP/s; one cold step (caches flushed) "
+        f"{cold_ms * 1e3:.1f} us")
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -518,6 +531,8 @@ def main():
         "fwd_tflops": round(f_fwd / (ms["fwd"] / 1e3) / 1e12, 2),
         "bwd_tflops": round(f_bwd / ((ms["dq"] + ms["dkdv"]) / 1e3) / 1e12, 2),
         "kernel_ms": {kk: round(vv, 5) for kk, vv in ms.items()},
+        "kernel_ms_median": {kk: round(vv, 5) for kk, vv in med.items()},
+        "cold_step_ms": round(cold_ms, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
