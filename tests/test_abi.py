@@ -244,3 +244,27 @@ def test_fp8_pointers_and_workspace_checked_before_launch():
     assert L.fa_fwd_fp8(q, FAKE, FAKE, need, FAKE, FAKE + 2, None) == B.FA_ERR_ARG
     assert L.fa_fwd_fp8(q, FAKE, FAKE, need - 1, FAKE, FAKE, None) == B.FA_ERR_WORKSPACE
     assert L.fa_fwd_fp8(q, FAKE, FAKE + 8, need, FAKE, FAKE, None) == B.FA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("B_,H,Hkv,N,d", [(2, 3, 3, 256, 64), (1, 8, 2, 1000, 128), (1, 2, 1, 1, 64)])
+def test_fp8_workspace_views_match_the_documented_layout(B_, H, Hkv, N, d):
+    """The binding's views of an FP8 workspace (a CPU byte tensor here) tile
+    exactly the size the library reports, in the header's order, each region
+    on a 256-byte boundary and no two overlapping."""
+    import torch
+
+    need = B.fa_fp8_workspace_size(_problem(B=B_, H=H, H_kv=Hkv, N=N, d=d))
+    ws = torch.zeros(need, dtype=torch.uint8)
+    views = B.fp8_workspace_views(ws, B_, H, Hkv, N, d)
+    n64 = -(-N // 64) * 64
+    assert views["qc"].shape == (B_ * H, n64, d) and views["kc"].shape == (B_ * Hkv, n64, d)
+    assert views["vc"].shape == (B_ * Hkv, n64 // 64, d, 64)
+    assert views["qe"].shape == (B_ * H, n64 // 64) and views["ve"].dtype == torch.int8
+    base = ws.data_ptr()
+    spans = []
+    for name in ("qc", "kc", "vc", "qe", "ke", "ve"):
+        start = views[name].data_ptr() - base
+        assert start % 256 == 0, name
+        spans.append((start, start + views[name].numel()))
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    assert spans[-1][1] <= need < spans[-1][1] + 256
