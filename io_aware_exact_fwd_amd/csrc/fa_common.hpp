@@ -187,7 +187,8 @@ __device__ __forceinline__ void dma_tile(const Buf& b, int r0, char* tile, int w
   for (int n = 0; n < NI; ++n) {
     const int P = (n * 4 + wave) * 64 + lane;
     const int r = P / CPR, pc = P % CPR;
-    const uint32_t off = (uint32_t)(((r0 + r) * D + ((pc ^ swz<D>(r)) << 3)) * 2);
+    // in 32-bit unsigned arithmetic: rows past N of the largest head reach 2^31 bytes
+    const uint32_t off = (uint32_t)((r0 + r) * D + ((pc ^ swz<D>(r)) << 3)) * 2u;
     dma16(b, off, tile + (n * 4 + wave) * 1024);
   }
 }

@@ -150,7 +150,7 @@ __global__ __launch_bounds__(128) void fp8_quant_kernel(Fp8QuantParams p) {
 #pragma unroll
   for (int n = 0; n < CPR / 2; ++n) {
     const int P = (2 * n + wave) * 64 + lane, rr = P / CPR, sl = P % CPR;
-    dma16(bx, (uint32_t)((blk * 64 + rr) * RB + ((sl ^ swzq<CPR>(rr)) << 4)), tile + (2 * n + wave) * 1024);
+    dma16(bx, (uint32_t)(blk * 64 + rr) * RB + (uint32_t)((sl ^ swzq<CPR>(rr)) << 4), tile + (2 * n + wave) * 1024);
   }
   wait_all_memory();
   __syncthreads();
