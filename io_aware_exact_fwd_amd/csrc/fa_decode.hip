@@ -221,28 +221,42 @@ void decode_split_kernel(DecParams p) {
   }
 }
 
-// One thread per (row, column): LSE = log sum_s exp(LSE_s),
-// O = sum_s exp(LSE_s - LSE) O_s.  A row no split sees gets O = 0, LSE = -inf.
-// The split LSEs of a row are read by all D threads of the row (cached).
+// Merge: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.  A row no
+// split sees gets O = 0, LSE = -inf.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p, int total_rows) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int row = idx / D;
+  // one wave per output row: the wave reduces the splits' LSE (max, then sum
+  // of exponentials), then each lane accumulates D / 64 columns
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave_id();
   if (row >= total_rows) return;
-  const int c = idx % D;
-  const float* pl = p.part_lse + (size_t)row * p.nsplit;
+  const int ns = p.nsplit;
+  const float* pl = p.part_lse + (size_t)row * ns;
   float m = kNegInf;
-  for (int s = 0; s < p.nsplit; ++s) m = fmaxf(m, pl[s]);
-  float acc = 0.f, lse = kNegInf;
+  for (int s = lane; s < ns; s += 64) m = vmax(m, pl[s]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = vmax(m, __shfl_xor(m, o, 64));
+  float lse = kNegInf;
+  float acc[D / 64];
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) acc[j] = 0.f;
   if (m != kNegInf) {
     float sum = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) sum += expf(pl[s] - m);
-    lse = m + logf(sum);
-    const float* po = p.part_o + (size_t)row * p.nsplit * D + c;
-    for (int s = 0; s < p.nsplit; ++s) acc += expf(pl[s] - lse) * po[(size_t)s * D];  // 0 for LSE_s = -inf
+    for (int s = lane; s < ns; s += 64) sum += fast_exp2((pl[s] - m) * kLog2e);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    lse = m + fast_log2(sum) * kLn2;
+    const float* po = p.part_o + (size_t)row * ns * D + lane;
+    for (int s = 0; s < ns; ++s) {
+      const float w = fast_exp2((pl[s] - lse) * kLog2e);  // 0 for LSE_s = -inf
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) acc[j] += w * po[(size_t)s * D + j * 64];
+    }
   }
-  ((T*)p.o)[(size_t)row * D + c] = (T)acc;
-  if (c == 0) p.lse[row] = lse;
+  T* orow = (T*)p.o + (size_t)row * D + lane;
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) orow[j * 64] = (T)acc[j];
+  if (lane == 0) p.lse[row] = lse;
 }
 
 template <typename T, int D>
@@ -255,8 +269,7 @@ hipError_t launch_decode_t(const DecParams& p, bool causal, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   const int total_rows = p.nkv * p.rows;
-  const int threads = total_rows * D;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((threads + 255) / 256), dim3(256), 0, s, p,
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((total_rows + 3) / 4), dim3(256), 0, s, p,
                      total_rows);
   return hipGetLastError();
 }
