@@ -93,6 +93,49 @@ def kernel_work(w):
     }
 
 
+class ClockSampler:
+    """Samples the GPU shader clock (the current level of the kernel's
+    pp_dpm_sclk table, marked '*') every few milliseconds on a host thread
+    while the timed steps run; mean() is None where the file is absent."""
+
+    def __init__(self, period_s=0.004):
+        import glob
+        import threading
+
+        files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = files[0] if files else None
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                with open(self.path) as f:
+                    for line in f:
+                        if line.rstrip().endswith("*"):
+                            mhz = float(line.split(":")[1].strip().split("Mhz")[0])
+                            if mhz > 400:  # skip the idle / deep-sleep level
+                                self.samples.append(mhz)
+            except (OSError, ValueError, IndexError):
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._thread.join()
+
+    def mean(self):
+        return round(sum(self.samples) / len(self.samples), 1) if self.samples else None
+
+
 def settle(step, ms):
     """Run `step` untimed for at least `ms` milliseconds of wall time before
     the warm-up steps: the GPU raises its clocks over the first tens of
@@ -202,11 +245,12 @@ def fp8_bench(w, args, dev):
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_q = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     ms_a = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     ms_step = wall * 1e3 / args.steps
@@ -226,6 +270,7 @@ def fp8_bench(w, args, dev):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "d": w.d,
                    "dtype": w.dtype, "causal": w.causal, "scale": w.scale},
         "kernel_ms": {"fp8_quantize": round(ms_q, 5), "fp8_fwd": round(ms_a, 5)},
+        "sclk_mhz": clock.mean(),
         "roofline": {"kernel": "fp8_fwd", "bound": "mfma", "achieved": round(ach, 1),
                      "peak": round(PEAK_FP8_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None},
@@ -465,11 +510,13 @@ def main():
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    sclk = clock.mean()
 
     per = {"fwd": [], "dq": [], "dkdv": []}
     for ev in events:
@@ -501,6 +548,10 @@ def main():
         r = roofline(kk, work[kk], ms[kk])
         log(f"[bench] {kk:5s} {ms[kk] * 1e3:9.1f} us  {r['achieved']:8.1f} {r['unit']} "
             f"({100 * r['frac']:.1f}% of {r['bound']} peak)")
+    peak_at_sclk = PEAK_MFMA_TFLOPS * sclk / 2400.0 if sclk else None
+    if sclk:
+        log(f"[bench] shader clock during the timed steps {sclk:.0f} MHz: peak there "
+            f"{peak_at_sclk:.0f} TFLOP/s, {100 * value / peak_at_sclk:.1f}% of it")
     log(f"[bench] step {ms_step * 1e3:.1f} us -> {value:.1f} TFLOP/s "
         f"({100 * value / PEAK_MFMA_TFLOPS:.1f}% of {PEAK_MFMA_TFLOPS:.0f}); fwd alone "
         f"{f_fwd / (ms['fwd'] / 1e3) / 1e12:.1f} TFLOP/s; one cold step (caches flushed) "
@@ -528,6 +579,8 @@ def main():
                    "dtype": w.dtype, "causal": w.causal, "scale": w.scale,
                    "block_mask": w.mask},
         "pct_of_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
+        "sclk_mhz": sclk,
+        "pct_of_mfma_peak_at_sclk": round(100 * value / peak_at_sclk, 2) if sclk else None,
         "fwd_tflops": round(f_fwd / (ms["fwd"] / 1e3) / 1e12, 2),
         "bwd_tflops": round(f_bwd / ((ms["dq"] + ms["dkdv"]) / 1e3) / 1e12, 2),
         "kernel_ms": {kk: round(vv, 5) for kk, vv in ms.items()},
