@@ -41,6 +41,12 @@ namespace fa {
 #ifndef FA_DKDV_NST
 #define FA_DKDV_NST 3  // LDS stages of the d = 64 dK/dV ring (2 or 3)
 #endif
+#ifndef FA_DKDV_AHEAD
+#define FA_DKDV_AHEAD 4  // LDS reads issued ahead of the score products (0: compiler's order)
+#endif
+#ifndef FA_DQ_AHEAD
+#define FA_DQ_AHEAD 0
+#endif
 #ifndef FA_DKDV64_WPE
 #define FA_DKDV64_WPE 2
 #endif
@@ -164,6 +170,7 @@ void bwd_dq_kernel(BwdParams p) {
           dp[kb] = mfma32(b, dof[t], dp[kb]);
         }
       }
+      sched_reads_ahead<4 * G::NKS, FA_DQ_AHEAD>();
       // hide keys outside the row's band (future, outside the window, past
       // the end): key of register r is k0 + g*4 + C(kb, r) with
       // C = kb*32 + (r/4)*8 + r%4; hidden iff C < lb or C > ub
@@ -400,6 +407,7 @@ void bwd_dkdv_kernel(BwdParams p) {
           dp[qb] = mfma32(b, vf[t], dp[qb]);
         }
       }
+      sched_reads_ahead<2 * G::NQB * G::NKS, FA_DKDV_AHEAD>();
       // hide queries outside this lane's key band (before the key under
       // causal, outside the window, past the end).  Query of register r in
       // block qb is qs0 + g*4 + C(qb, r), C = qb*32 + (r/4)*8 + r%4; hidden

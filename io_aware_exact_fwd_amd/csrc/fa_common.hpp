@@ -258,6 +258,24 @@ struct IntC {
 // would also wait for the prefetch of the next tile.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Scheduling hint for a block of N LDS operand reads feeding N matrix products
+// (read i feeding product i): `ahead` reads first, then one product and one
+// read alternately, then the last `ahead` products, so each read is issued
+// `ahead` products before its use.  AHEAD = 0 leaves the block to the
+// compiler.  Place it after the block's code (it orders that basic block).
+template <int N, int AHEAD>
+__device__ __forceinline__ void sched_reads_ahead() {
+  if constexpr (AHEAD > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < N - AHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // matrix products
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+  }
+}
+
 // s_waitcnt operand: at most n vector-memory operations of this wave still
 // outstanding (they complete in issue order), no wait on the other counters.
 constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }

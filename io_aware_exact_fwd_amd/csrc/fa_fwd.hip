@@ -53,6 +53,9 @@ constexpr float kRescaleTau = 8.0f;
 #ifndef FA_FWD64_QB
 #define FA_FWD64_QB 1
 #endif
+#ifndef FA_FWD_AHEAD
+#define FA_FWD_AHEAD 0  // LDS reads issued ahead of the score products (0: compiler's order)
+#endif
 #ifndef FA_FWD64_WPE
 #define FA_FWD64_WPE 4
 #endif
@@ -163,6 +166,7 @@ void fwd_kernel(FwdParams p) {
           for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][t], s[qb][kb]);
         }
       }
+      if constexpr (QB == 1) sched_reads_ahead<2 * G::NKS, FA_FWD_AHEAD>();
       // 2. mask keys outside the row's band (future keys, keys outside the
       // window, keys past the end).  Key of register r is k0 + g*4 + C(kb, r),
       // C = kb*32 + (r/4)*8 + r%4; it is hidden iff C < lb or C > ub.
