@@ -20,6 +20,8 @@
 //                    dV += P^T dO and dK += dS^T Q.
 // The price is computing S and dP in both kernels: 14 d multiply-add FLOPs
 // per visible pair instead of 10 d.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_dropout.hpp"
 #include "fa_kernels.hpp"
@@ -142,11 +144,11 @@ void bwd_dq_kernel(BwdParams p) {
   wait_all_memory();
   __syncthreads();
 
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
+  const TileOffsets<D> toff(lane);
+  // one key tile; the LDS stage is a compile-time constant (two steps per
+  // iteration of the loop below), so it joins the reads' immediate offsets
+  auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
+    constexpr int cur = decltype(stage)::value;
     const bool more = it + 1 < ntiles;
     if (more) gload(it + 1, cur ^ 1);
 
@@ -163,10 +165,9 @@ void bwd_dq_kernel(BwdParams p) {
         dp[kb] = f32x16{0};
 #pragma unroll
         for (int t = 0; t < G::NKS; ++t) {
-          const int ro = swz_off<D>(kb * 32 + l32, t * 16 + g * 8);
-          const V8 a = lds_read8<T>(ks + ro);
+          const V8 a = toff.template row_operand<T>(ks, kb * 32, t);
           s[kb] = mfma32(a, qf[t], s[kb]);
-          const V8 b = lds_read8<T>(vs + ro);
+          const V8 b = toff.template row_operand<T>(vs, kb * 32, t);
           dp[kb] = mfma32(b, dof[t], dp[kb]);
         }
       }
@@ -223,12 +224,16 @@ void bwd_dq_kernel(BwdParams p) {
       for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const V8 a = swz_tr_operand<T, D>(ks, t * 16 + g * 4 + tr_row, db * 32 + tr_col);
+          const V8 a = toff.template tr_operand<T>(ks, t * 16, db);
           acc[db] = mfma32(a, bs[t], acc[db]);
         }
     }
     wait_all_memory();  // this thread's copies into the next stage have landed
     __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
   }
 
   if (q < N) {
@@ -256,6 +261,7 @@ struct DkvGeom {
   static constexpr int LBYTES = 256;         // LSE (or D) of the step's rows, one dword per lane
   static constexpr int STAGE = 2 * TBYTES + 2 * LBYTES;  // Q, dO, LSE, D
   static constexpr int NST = D == 64 ? FA_DKDV_NST : 2;   // stages in the LDS ring
+  static_assert(NST == 2 || NST == 3, "the step loop unrolls two or three stages");
   static constexpr int COPIES = 2 * (QT * D / 8 / 256);    // Q and dO copies per thread per step
   static_assert(QT <= 64, "LSE / D rows of a step fit one 64-lane copy");
   static constexpr int NDB = D / 32;
@@ -373,15 +379,15 @@ void bwd_dkdv_kernel(BwdParams p) {
   land_next(ntiles > 1, smem);
   __syncthreads();
 
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-
-  int cur = 0;
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + G::NST - 1 < ntiles) {
-      const int st = cur + G::NST - 1 >= G::NST ? cur - 1 : cur + G::NST - 1;
-      gload(it + G::NST - 1, smem + st * G::STAGE);
-    }
+  const TileOffsets<D> toff(lane);
+  // one query step; its LDS stage (it mod NST) is a compile-time constant
+  // (NST steps per iteration of the loop below), so stage addresses join the
+  // reads' immediate offsets
+  auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
+    constexpr int cur = decltype(stage)::value;
+    constexpr int nxt = cur + 1 == G::NST ? 0 : cur + 1;  // stage of step it + 1
+    constexpr int pre = (cur + G::NST - 1) % G::NST;      // stage of step it + NST - 1
+    if (it + G::NST - 1 < ntiles) gload(it + G::NST - 1, smem + pre * G::STAGE);
 
     const int qs0 = tiles.pos0(it % nqt);
     const int qh = kvh * p.group + it / nqt;  // query head of this step
@@ -400,10 +406,9 @@ void bwd_dkdv_kernel(BwdParams p) {
         dp[qb] = f32x16{0};
 #pragma unroll
         for (int t = 0; t < G::NKS; ++t) {
-          const int ro = swz_off<D>(qb * 32 + l32, t * 16 + g * 8);
-          const V8 a = lds_read8<T>(qsm + ro);
+          const V8 a = toff.template row_operand<T>(qsm, qb * 32, t);
           s[qb] = mfma32(a, kf[t], s[qb]);
-          const V8 b = lds_read8<T>(dsm + ro);
+          const V8 b = toff.template row_operand<T>(dsm, qb * 32, t);
           dp[qb] = mfma32(b, vf[t], dp[qb]);
         }
       }
@@ -470,16 +475,22 @@ void bwd_dkdv_kernel(BwdParams p) {
                                dp[qb][r0 + 4], dp[qb][r0 + 5], dp[qb][r0 + 6], dp[qb][r0 + 7]);
 #pragma unroll
         for (int db = 0; db < G::NDB; ++db) {
-          const V8 bdo_ = swz_tr_operand<T, D>(dsm, t * 16 + g * 4 + tr_row, db * 32 + tr_col);
+          const V8 bdo_ = toff.template tr_operand<T>(dsm, t * 16, db);
           dva[db] = mfma32(ap, bdo_, dva[db]);
-          const V8 bq_ = swz_tr_operand<T, D>(qsm, t * 16 + g * 4 + tr_row, db * 32 + tr_col);
+          const V8 bq_ = toff.template tr_operand<T>(qsm, t * 16, db);
           dka[db] = mfma32(ad, bq_, dka[db]);
         }
       }
     }
-    if (it + 1 < ntiles) land_next(it + 2 < ntiles, smem + (cur + 1 == G::NST ? 0 : cur + 1) * G::STAGE);
+    if (it + 1 < ntiles) land_next(it + 2 < ntiles, smem + nxt * G::STAGE);
     __syncthreads();
-    cur = cur + 1 == G::NST ? 0 : cur + 1;
+  };
+  for (int it = 0; it < ntiles; it += G::NST) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
+    if constexpr (G::NST > 2) {
+      if (it + 2 < ntiles) step(it + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   // C layout: lane -> head-dim column, register -> key row.  Each wave turns

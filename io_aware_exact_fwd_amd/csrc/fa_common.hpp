@@ -200,6 +200,46 @@ __device__ __forceinline__ typename Vec8<T>::type swz_tr_operand(const char* til
   return lds_tr_operand<T>(tile + swz_off<D>(r, col), tile + swz_off<D>(r + 8, col));
 }
 
+// Per-lane byte offsets of the two operand reads of a swizzled tile, taken
+// once before the tile loop.  The swizzle depends on the four low row bits
+// only, so the same read 16 rows further down (the next k-step or 32-row
+// block) or in another LDS stage is this offset plus a constant, which the
+// read instruction carries as its immediate: no address arithmetic per read
+// once the stage is known at compile time.
+//   rows[t]:  lds_read8 at row l32, element columns 16 t + 8 g
+//   tr[db][h]: the transpose reads of rows 4 g + (lane % 16) / 4 + 8 h,
+//             element columns 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4)
+template <int D>
+struct TileOffsets {
+  int rows[D / 16];
+  int tr[D / 32][2];
+  __device__ __forceinline__ explicit TileOffsets(int lane) {
+    const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) rows[t] = swz_off<D>(l32, t * 16 + g * 8);
+    const int r0 = g * 4 + ((lane & 15) >> 2);
+    const int c0 = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      tr[db][0] = swz_off<D>(r0, db * 32 + c0);
+      tr[db][1] = swz_off<D>(r0 + 8, db * 32 + c0);
+    }
+  }
+  // lds_read8 operand of rows row0 + l32 (row0 a multiple of 16), k-step t
+  template <typename T>
+  __device__ __forceinline__ typename Vec8<T>::type row_operand(const char* tile, int row0,
+                                                                int t) const {
+    return lds_read8<T>(tile + row0 * D * 2 + rows[t]);
+  }
+  // transpose-read operand of rows row0 .. row0 + 15 (row0 a multiple of 16),
+  // column block db; equal to swz_tr_operand at row row0 + 4 g + (lane % 16) / 4
+  template <typename T>
+  __device__ __forceinline__ typename Vec8<T>::type tr_operand(const char* tile, int row0,
+                                                               int db) const {
+    return lds_tr_operand<T>(tile + row0 * D * 2 + tr[db][0], tile + row0 * D * 2 + tr[db][1]);
+  }
+};
+
 // ---- workgroup -> work-item mapping -----------------------------------------
 // Workgroups are handed to the 8 XCDs round-robin by linear id.  Remap so that
 // each XCD receives one contiguous range of the logical order (head-major):

@@ -33,6 +33,8 @@
 // per lane (lanes l and l+32 share it), so row reductions are in-lane plus one
 // exchange with lane l^32, and the probabilities are already laid out as the
 // B operand of the P V product (see fa_common.hpp for the MFMA layouts).
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_dropout.hpp"
 #include "fa_kernels.hpp"
@@ -44,7 +46,7 @@ constexpr float kRescaleTau = 8.0f;
 
 // Tuning knobs of the dense head-dim-64 forward: waves per workgroup, 32-row
 // query blocks per wave, waves per SIMD the register budget targets.  Measured
-// on MI355X: 32 rows per wave at 4 waves per SIMD (127 VGPRs) beats 64 rows per
+// on MI355X: 32 rows per wave at 4 waves per SIMD (112 VGPRs) beats 64 rows per
 // wave at 2 waves per SIMD; latency hiding across waves matters more there than
 // reusing each LDS fragment twice.
 #ifndef FA_FWD64_NW
@@ -135,13 +137,16 @@ void fwd_kernel(FwdParams p) {
     dma_tile<D, G::KT>(bv, k0, ks + G::KBYTES, wave, lane);
   };
 
+  const TileOffsets<D> toff(lane);
   const int ntiles = tiles.count;
   if (ntiles > 0) gload(0, 0);
   wait_all_memory();
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
+  // one key tile; the LDS stage is a compile-time constant (the loop below
+  // runs two steps per iteration), so it joins the reads' immediate offsets
+  auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
+    constexpr int cur = decltype(stage)::value;
     const bool more = it + 1 < ntiles;
     if (more) gload(it + 1, cur ^ 1);
 
@@ -161,7 +166,7 @@ void fwd_kernel(FwdParams p) {
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{0};
 #pragma unroll
         for (int t = 0; t < G::NKS; ++t) {
-          const V8 a = lds_read8<T>(ks + swz_off<D>(kb * 32 + l32, t * 16 + g * 8));
+          const V8 a = toff.template row_operand<T>(ks, kb * 32, t);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][t], s[qb][kb]);
         }
@@ -204,8 +209,6 @@ void fwd_kernel(FwdParams p) {
       // overlap the score products of half 1 still in flight, and those of
       // half 1 the P V products of half 0.  The reference may move between
       // the halves; O and l are rescaled with it, so the result is the same.
-      const int tr_row = (lane & 15) >> 2;
-      const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // dropout: generator bytes of this half's keys (byte e of kw[qb][rr]
@@ -269,7 +272,7 @@ void fwd_kernel(FwdParams p) {
           }
 #pragma unroll
           for (int db = 0; db < G::NDB; ++db) {
-            const V8 a = swz_tr_operand<T, D>(vs, t * 16 + g * 4 + tr_row, db * 32 + tr_col);
+            const V8 a = toff.template tr_operand<T>(vs, t * 16, db);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(a, bp[qb], o[qb][db]);
           }
@@ -278,6 +281,10 @@ void fwd_kernel(FwdParams p) {
     }
     wait_all_memory();  // this thread's copies into the next stage have landed
     __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
   }
 
   // epilogue: deferred normalisation (and the scale of kept weights under
