@@ -30,7 +30,10 @@
 namespace fa {
 
 // Tuning knobs: waves per SIMD of the dQ kernel, query rows per step and waves
-// per SIMD of the head-dim-64 dK/dV kernel.
+// per SIMD of the dK/dV kernel.  Measured on MI355X at head dim 128: dQ under
+// dropout fits two waves per SIMD (234-240 VGPRs) and runs 19 % faster than
+// with one; dK/dV needs about 350 registers (VGPRs and AGPRs) and spills at
+// two waves per SIMD, running at half the speed.
 #ifndef FA_DQ_WPE
 #define FA_DQ_WPE 3
 #endif
@@ -52,6 +55,12 @@ namespace fa {
 #ifndef FA_DKDV64_WPE
 #define FA_DKDV64_WPE 2
 #endif
+#ifndef FA_DKDV128_WPE
+#define FA_DKDV128_WPE 1
+#endif
+#ifndef FA_DQ128_DROP_WPE
+#define FA_DQ128_DROP_WPE 2
+#endif
 
 // ============================================================================
 // dQ kernel
@@ -65,7 +74,7 @@ struct DqGeom {
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
   // waves per SIMD the registers allow
-  static constexpr int wpe(bool drop) { return D == 128 ? (drop ? 1 : FA_DQ128_WPE) : FA_DQ_WPE; }
+  static constexpr int wpe(bool drop) { return D == 128 ? (drop ? FA_DQ128_DROP_WPE : FA_DQ128_WPE) : FA_DQ_WPE; }
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
@@ -267,7 +276,7 @@ struct DkvGeom {
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
   static constexpr int NQB = QT / 32;       // 32-query blocks per step
-  static constexpr int WPE = D == 64 ? FA_DKDV64_WPE : 1;  // waves per SIMD the registers allow
+  static constexpr int WPE = D == 64 ? FA_DKDV64_WPE : FA_DKDV128_WPE;  // waves per SIMD the registers allow
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
