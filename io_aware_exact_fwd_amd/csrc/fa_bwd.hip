@@ -30,12 +30,18 @@
 namespace fa {
 
 // Tuning knobs: waves per SIMD of the dQ kernel, query rows per step and waves
-// per SIMD of the dK/dV kernel.  Measured on MI355X at head dim 128: dQ under
+// per SIMD of the dK/dV kernel.  At head dim 64, running the two 32-key halves
+// of a tile one after the other (scores to dQ) keeps dQ within 124 VGPRs, so
+// it runs at four waves per SIMD: 3-4 % faster on MI355X than both halves at
+// once at three waves (150 VGPRs), with bitwise the same dQ.  Measured on MI355X at head dim 128: dQ under
 // dropout fits two waves per SIMD (234-240 VGPRs) and runs 19 % faster than
 // with one; dK/dV needs about 350 registers (VGPRs and AGPRs) and spills at
 // two waves per SIMD, running at half the speed.
 #ifndef FA_DQ_WPE
-#define FA_DQ_WPE 3
+#define FA_DQ_WPE 4
+#endif
+#ifndef FA_DQ64_DROP_WPE
+#define FA_DQ64_DROP_WPE 3  // the dropout generator's registers: four waves would spill
 #endif
 #ifndef FA_DQ128_WPE
 #define FA_DQ128_WPE 2
@@ -48,6 +54,9 @@ namespace fa {
 #endif
 #ifndef FA_DKDV_AHEAD
 #define FA_DKDV_AHEAD 4  // LDS reads issued ahead of the score products (0: compiler's order)
+#endif
+#ifndef FA_DQ_HALVES
+#define FA_DQ_HALVES 1  // 1: each 32-key half of a tile runs scores to dQ before the next
 #endif
 #ifndef FA_DQ_AHEAD
 #define FA_DQ_AHEAD 0
@@ -74,7 +83,10 @@ struct DqGeom {
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
   // waves per SIMD the registers allow
-  static constexpr int wpe(bool drop) { return D == 128 ? (drop ? FA_DQ128_DROP_WPE : FA_DQ128_WPE) : FA_DQ_WPE; }
+  static constexpr int wpe(bool drop) {
+    if (D == 128) return drop ? FA_DQ128_DROP_WPE : FA_DQ128_WPE;
+    return drop ? FA_DQ64_DROP_WPE : FA_DQ_WPE;
+  }
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
@@ -166,76 +178,89 @@ void bwd_dq_kernel(BwdParams p) {
     const char* vs = ks + G::KBYTES;
     const int qw_last = qw0 + 31;
     const bool active = k0 <= band.hi(qw_last) && k0 + G::KT - 1 >= band.lo(qw0);
-    if (active) {
-      f32x16 s[2], dp[2];
+    // key halves KB0 .. KB0 + NKB - 1 of the tile: scores, dP, dS, then dQ
+    auto halves = [&](auto kb0_c, auto nkb_c) __attribute__((always_inline)) {
+      constexpr int KB0 = decltype(kb0_c)::value, NKB = decltype(nkb_c)::value;
+      // a half no row of the wave sees adds nothing (the later half of a
+      // causal diagonal tile)
+      if (NKB == 1 && (k0 + KB0 * 32 > band.hi(qw_last) || k0 + KB0 * 32 + 31 < band.lo(qw0))) return;
+      f32x16 s[NKB], dp[NKB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{0};
-        dp[kb] = f32x16{0};
+      for (int i = 0; i < NKB; ++i) {
+        s[i] = f32x16{0};
+        dp[i] = f32x16{0};
 #pragma unroll
         for (int t = 0; t < G::NKS; ++t) {
-          const V8 a = toff.template row_operand<T>(ks, kb * 32, t);
-          s[kb] = mfma32(a, qf[t], s[kb]);
-          const V8 b = toff.template row_operand<T>(vs, kb * 32, t);
-          dp[kb] = mfma32(b, dof[t], dp[kb]);
+          const V8 a = toff.template row_operand<T>(ks, (KB0 + i) * 32, t);
+          s[i] = mfma32(a, qf[t], s[i]);
+          const V8 b = toff.template row_operand<T>(vs, (KB0 + i) * 32, t);
+          dp[i] = mfma32(b, dof[t], dp[i]);
         }
       }
-      sched_reads_ahead<4 * G::NKS, FA_DQ_AHEAD>();
+      sched_reads_ahead<2 * NKB * G::NKS, FA_DQ_AHEAD>();
       // hide keys outside the row's band (future, outside the window, past
       // the end): key of register r is k0 + g*4 + C(kb, r) with
       // C = kb*32 + (r/4)*8 + r%4; hidden iff C < lb or C > ub
       // one compare-and-select per bound, each only where some row needs it
       // (an OR of the two compares would route every element through the
       // scalar unit)
-      if (k0 + G::KT - 1 > band.hi(qw0)) {
+      if (k0 + KB0 * 32 + NKB * 32 - 1 > band.hi(qw0)) {
         const int ub = band.hi(q) - k0 - g * 4;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < NKB; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
-            s[kb][r] = C > ub ? kNegInf : s[kb][r];
+            const int C = (KB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
+            s[i][r] = C > ub ? kNegInf : s[i][r];
           }
       }
-      if (k0 < band.lo(qw_last)) {
+      if (k0 + KB0 * 32 < band.lo(qw_last)) {
         const int lb = band.lo(q) - k0 - g * 4;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < NKB; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
-            s[kb][r] = C < lb ? kNegInf : s[kb][r];
+            const int C = (KB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
+            s[i][r] = C < lb ? kNegInf : s[i][r];
           }
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int i = 0; i < NKB; ++i) {
         u32x4 kw;
         if constexpr (DROP)
-          kw = drop_bytes_query_lanes(p.drop, (uint32_t)head, k0 + kb * 32, qw0,
+          kw = drop_bytes_query_lanes(p.drop, (uint32_t)head, k0 + (KB0 + i) * 32, qw0,
                                       smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(__builtin_fmaf(s[kb][r], p.c, -lse2));
-          float dpr = dp[kb][r];
+          const float pr = fast_exp2(__builtin_fmaf(s[i][r], p.c, -lse2));
+          float dpr = dp[i][r];
           if constexpr (DROP) dpr = keep_byte(kw[r >> 2], r & 3, p.drop.t8) ? dpr : 0.f;
-          s[kb][r] = pr * (dpr - d_sub);  // dS^T (scale applied to dQ at the end)
+          s[i][r] = pr * (dpr - d_sub);  // dS^T (scale applied to dQ at the end)
         }
       }
       // dQ^T += K^T dS^T : A = K^T via transpose reads of the K tile
-      V8 bs[4];
+      V8 bs[2 * NKB];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int kb = t >> 1, r0 = (t & 1) * 8;
-        bs[t] = pack8<T>(s[kb][r0 + 0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3],
-                         s[kb][r0 + 4], s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
+      for (int t = 0; t < 2 * NKB; ++t) {
+        const int i = t >> 1, r0 = (t & 1) * 8;
+        bs[t] = pack8<T>(s[i][r0 + 0], s[i][r0 + 1], s[i][r0 + 2], s[i][r0 + 3],
+                         s[i][r0 + 4], s[i][r0 + 5], s[i][r0 + 6], s[i][r0 + 7]);
       }
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const V8 a = toff.template tr_operand<T>(ks, t * 16, db);
+        for (int t = 0; t < 2 * NKB; ++t) {
+          const V8 a = toff.template tr_operand<T>(ks, (2 * KB0 + t) * 16, db);
           acc[db] = mfma32(a, bs[t], acc[db]);
         }
+    };
+    if (active) {
+      if constexpr (FA_DQ_HALVES) {
+        halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+        halves(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+      } else {
+        halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
+      }
     }
     wait_all_memory();  // this thread's copies into the next stage have landed
     __syncthreads();
