@@ -33,7 +33,11 @@ namespace fa {
 // per SIMD of the dK/dV kernel.  At head dim 64, running the two 32-key halves
 // of a tile one after the other (scores to dQ) keeps dQ within 124 VGPRs, so
 // it runs at four waves per SIMD: 3-4 % faster on MI355X than both halves at
-// once at three waves (150 VGPRs), with bitwise the same dQ.  Measured on MI355X at head dim 128: dQ under
+// once at three waves (150 VGPRs), with bitwise the same dQ.  Likewise dK/dV
+// handles the 32-query blocks of a step one after the other: at head dim 64
+// it fits 168 VGPRs, three waves per SIMD instead of two (dK/dV 5 % faster),
+// and at head dim 128 it runs 10 % faster at the same occupancy; 128-query
+// steps (half the barriers, two LDS stages) measured slower.  Measured on MI355X at head dim 128: dQ under
 // dropout fits two waves per SIMD (234-240 VGPRs) and runs 19 % faster than
 // with one; dK/dV needs about 350 registers (VGPRs and AGPRs) and spills at
 // two waves per SIMD, running at half the speed.
@@ -49,6 +53,9 @@ namespace fa {
 #ifndef FA_DKDV_QT
 #define FA_DKDV_QT 64
 #endif
+#ifndef FA_DKDV_QBLK
+#define FA_DKDV_QBLK 1  // 32-query blocks of a step handled together (scores to products)
+#endif
 #ifndef FA_DKDV_NST
 #define FA_DKDV_NST 3  // LDS stages of the d = 64 dK/dV ring (2 or 3)
 #endif
@@ -62,7 +69,7 @@ namespace fa {
 #define FA_DQ_AHEAD 0
 #endif
 #ifndef FA_DKDV64_WPE
-#define FA_DKDV64_WPE 2
+#define FA_DKDV64_WPE 3
 #endif
 #ifndef FA_DKDV128_WPE
 #define FA_DKDV128_WPE 1
@@ -292,15 +299,19 @@ template <int D>
 struct DkvGeom {
   static constexpr int QT = FA_DKDV_QT;     // queries per step
   static constexpr int TBYTES = QT * D * 2;  // Q / dO tile, swizzled (no padding)
-  static constexpr int LBYTES = 256;         // LSE (or D) of the step's rows, one dword per lane
+  static constexpr int NL = (QT + 63) / 64;  // 64-row copies of LSE (and of D) per step
+  static constexpr int LBYTES = NL * 256;    // LSE (or D) of the step's rows, one dword per lane
   static constexpr int STAGE = 2 * TBYTES + 2 * LBYTES;  // Q, dO, LSE, D
   static constexpr int NST = D == 64 ? FA_DKDV_NST : 2;   // stages in the LDS ring
   static_assert(NST == 2 || NST == 3, "the step loop unrolls two or three stages");
   static constexpr int COPIES = 2 * (QT * D / 8 / 256);    // Q and dO copies per thread per step
-  static_assert(QT <= 64, "LSE / D rows of a step fit one 64-lane copy");
+  static constexpr int LCOPIES = 2 * NL;    // LSE and D copies per step (wave 0)
+  static_assert(QT % 32 == 0 && QT <= 128, "whole 32-query blocks, within a 128-row mask block");
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
   static constexpr int NQB = QT / 32;       // 32-query blocks per step
+  static constexpr int QBLK = FA_DKDV_QBLK < NQB ? FA_DKDV_QBLK : NQB;  // blocks handled together
+  static_assert(NQB % QBLK == 0, "the step splits into whole groups of blocks");
   static constexpr int WPE = D == 64 ? FA_DKDV64_WPE : FA_DKDV128_WPE;  // waves per SIMD the registers allow
 };
 
@@ -376,9 +387,13 @@ void bwd_dkdv_kernel(BwdParams p) {
     if (wave == 0) {
       const Buf bl = make_buf(p.lse + qh * N, (uint32_t)N * 4);
       const Buf bd = make_buf(p.dvec + qh * N, (uint32_t)N * 4);
-      const uint32_t off = lane < G::QT ? (uint32_t)(qs + lane) * 4 : 0x80000000u;
-      dma4(bl, off, st + 2 * G::TBYTES);
-      dma4(bd, off, st + 2 * G::TBYTES + G::LBYTES);
+#pragma unroll
+      for (int c = 0; c < G::NL; ++c) {
+        const int r = c * 64 + lane;
+        const uint32_t off = r < G::QT ? (uint32_t)(qs + r) * 4 : 0x80000000u;
+        dma4(bl, off, st + 2 * G::TBYTES + c * 256);
+        dma4(bd, off, st + 2 * G::TBYTES + G::LBYTES + c * 256);
+      }
     }
   };
   // Wait until this wave's copies of the next step have landed (those of the
@@ -389,7 +404,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   auto land_next = [&](bool younger_in_flight, char* st) {
     if (G::NST > 2 && younger_in_flight) {
       if (wave == 0)
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(G::COPIES + 2));
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(G::COPIES + G::LCOPIES));
       else
         __builtin_amdgcn_s_waitcnt(vmcnt_at_most(G::COPIES));
     } else {
@@ -432,50 +447,57 @@ void bwd_dkdv_kernel(BwdParams p) {
     // between them, and by all of them in [qlo(kw_last), qhi(kw0)]
     const int kw_last = kw0 + 31;
     const bool active = qs0 <= band.qhi(kw_last) && qs0 + G::QT - 1 >= band.qlo(kw0);
-    if (active) {
-      f32x16 s[G::NQB], dp[G::NQB];
+    // 32-query blocks QB0 .. QB0 + NQ - 1 of the step: scores, dP, softmax,
+    // dS, then their dV and dK products
+    auto qblocks = [&](auto qb0_c, auto nq_c) __attribute__((always_inline)) {
+      constexpr int QB0 = decltype(qb0_c)::value, NQ = decltype(nq_c)::value;
+      const int qa = qs0 + QB0 * 32, qz = qa + NQ * 32 - 1;  // the blocks' queries
+      // blocks that see none of the wave's keys add nothing
+      if (NQ < G::NQB && (qa > band.qhi(kw_last) || qz < band.qlo(kw0))) return;
+      f32x16 s[NQ], dp[NQ];
 #pragma unroll
-      for (int qb = 0; qb < G::NQB; ++qb) {
-        s[qb] = f32x16{0};
-        dp[qb] = f32x16{0};
+      for (int i = 0; i < NQ; ++i) {
+        s[i] = f32x16{0};
+        dp[i] = f32x16{0};
 #pragma unroll
         for (int t = 0; t < G::NKS; ++t) {
-          const V8 a = toff.template row_operand<T>(qsm, qb * 32, t);
-          s[qb] = mfma32(a, kf[t], s[qb]);
-          const V8 b = toff.template row_operand<T>(dsm, qb * 32, t);
-          dp[qb] = mfma32(b, vf[t], dp[qb]);
+          const V8 a = toff.template row_operand<T>(qsm, (QB0 + i) * 32, t);
+          s[i] = mfma32(a, kf[t], s[i]);
+          const V8 b = toff.template row_operand<T>(dsm, (QB0 + i) * 32, t);
+          dp[i] = mfma32(b, vf[t], dp[i]);
         }
       }
-      sched_reads_ahead<2 * G::NQB * G::NKS, FA_DKDV_AHEAD>();
+      sched_reads_ahead<2 * NQ * G::NKS, FA_DKDV_AHEAD>();
       // hide queries outside this lane's key band (before the key under
       // causal, outside the window, past the end).  Query of register r in
       // block qb is qs0 + g*4 + C(qb, r), C = qb*32 + (r/4)*8 + r%4; hidden
       // iff C < lb or C > ub
-      if (qs0 < band.qlo(kw_last)) {
+      if (qa < band.qlo(kw_last)) {
         const int lb = band.qlo(key) - qs0 - g * 4;
 #pragma unroll
-        for (int qb = 0; qb < G::NQB; ++qb)
+        for (int i = 0; i < NQ; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int C = qb * 32 + (r >> 2) * 8 + (r & 3);
-            s[qb][r] = C < lb ? kNegInf : s[qb][r];
+            const int C = (QB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
+            s[i][r] = C < lb ? kNegInf : s[i][r];
           }
       }
-      if (qs0 + G::QT - 1 > band.qhi(kw0)) {
+      if (qz > band.qhi(kw0)) {
         const int ub = band.qhi(key) - qs0 - g * 4;
 #pragma unroll
-        for (int qb = 0; qb < G::NQB; ++qb)
+        for (int i = 0; i < NQ; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int C = qb * 32 + (r >> 2) * 8 + (r & 3);
-            s[qb][r] = C > ub ? kNegInf : s[qb][r];
+            const int C = (QB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
+            s[i][r] = C > ub ? kNegInf : s[i][r];
           }
       }
       // Under dropout (keep mask Z01, scale mult): dV = mult (Z01 o P)^T dO and
       // dS = mult * P o (Z01 o dP' - D / mult); both mult factors join the
       // finished dV and dK, and the D loaded with the tile is already / mult.
 #pragma unroll
-      for (int qb = 0; qb < G::NQB; ++qb) {
+      for (int i = 0; i < NQ; ++i) {
+        const int qb = QB0 + i;
         u32x4 kw;
         if constexpr (DROP)
           kw = drop_bytes_key_lanes(p.drop, (uint32_t)qh, kw0, qs0 + qb * 32,
@@ -487,33 +509,43 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = rr * 4 + e;
-            const float pr = fast_exp2(__builtin_fmaf(s[qb][r], p.c, -l4[e]));
+            const float pr = fast_exp2(__builtin_fmaf(s[i][r], p.c, -l4[e]));
             if constexpr (DROP) {
               const bool keep = keep_byte(kw[rr], e, p.drop.t8);
-              s[qb][r] = keep ? pr : 0.f;                              // Z01 o P
-              dp[qb][r] = pr * ((keep ? dp[qb][r] : 0.f) - d4[e]);  // dS / mult
+              s[i][r] = keep ? pr : 0.f;                             // Z01 o P
+              dp[i][r] = pr * ((keep ? dp[i][r] : 0.f) - d4[e]);  // dS / mult
             } else {
-              s[qb][r] = pr;                                   // P
-              dp[qb][r] = pr * (dp[qb][r] - d4[e]);  // dS (scale applied to dK at the end)
+              s[i][r] = pr;                                  // P
+              dp[i][r] = pr * (dp[i][r] - d4[e]);  // dS (scale applied to dK at the end)
             }
           }
         }
       }
       // dV += P^T dO,  dK += dS^T Q ; k-step t covers queries 16t .. 16t+15
 #pragma unroll
-      for (int t = 0; t < G::QT / 16; ++t) {
-        const int qb = t >> 1, r0 = (t & 1) * 8;
-        const V8 ap = pack8<T>(s[qb][r0 + 0], s[qb][r0 + 1], s[qb][r0 + 2], s[qb][r0 + 3],
-                               s[qb][r0 + 4], s[qb][r0 + 5], s[qb][r0 + 6], s[qb][r0 + 7]);
-        const V8 ad = pack8<T>(dp[qb][r0 + 0], dp[qb][r0 + 1], dp[qb][r0 + 2], dp[qb][r0 + 3],
-                               dp[qb][r0 + 4], dp[qb][r0 + 5], dp[qb][r0 + 6], dp[qb][r0 + 7]);
+      for (int t = 0; t < 2 * NQ; ++t) {
+        const int i = t >> 1, r0 = (t & 1) * 8;
+        const V8 ap = pack8<T>(s[i][r0 + 0], s[i][r0 + 1], s[i][r0 + 2], s[i][r0 + 3],
+                               s[i][r0 + 4], s[i][r0 + 5], s[i][r0 + 6], s[i][r0 + 7]);
+        const V8 ad = pack8<T>(dp[i][r0 + 0], dp[i][r0 + 1], dp[i][r0 + 2], dp[i][r0 + 3],
+                               dp[i][r0 + 4], dp[i][r0 + 5], dp[i][r0 + 6], dp[i][r0 + 7]);
 #pragma unroll
         for (int db = 0; db < G::NDB; ++db) {
-          const V8 bdo_ = toff.template tr_operand<T>(dsm, t * 16, db);
+          const V8 bdo_ = toff.template tr_operand<T>(dsm, (2 * QB0 + t) * 16, db);
           dva[db] = mfma32(ap, bdo_, dva[db]);
-          const V8 bq_ = toff.template tr_operand<T>(qsm, t * 16, db);
+          const V8 bq_ = toff.template tr_operand<T>(qsm, (2 * QB0 + t) * 16, db);
           dka[db] = mfma32(ad, bq_, dka[db]);
         }
+      }
+    };
+    if (active) {
+      if constexpr (G::QBLK >= G::NQB) {
+        qblocks(std::integral_constant<int, 0>{}, std::integral_constant<int, G::NQB>{});
+      } else {
+        static_for<G::NQB / G::QBLK>([&](auto b) __attribute__((always_inline)) {
+          qblocks(std::integral_constant<int, decltype(b)::value * G::QBLK>{},
+                  std::integral_constant<int, G::QBLK>{});
+        });
       }
     }
     if (it + 1 < ntiles) land_next(it + 2 < ntiles, smem + nxt * G::STAGE);

@@ -21,6 +21,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -239,6 +242,16 @@ struct TileOffsets {
     return lds_tr_operand<T>(tile + row0 * D * 2 + tr[db][0], tile + row0 * D * 2 + tr[db][1]);
   }
 };
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // ---- workgroup -> work-item mapping -----------------------------------------
 // Workgroups are handed to the 8 XCDs round-robin by linear id.  Remap so that
