@@ -58,6 +58,9 @@ constexpr float kRescaleTau = 8.0f;
 #ifndef FA_FWD_AHEAD
 #define FA_FWD_AHEAD 0  // LDS reads issued ahead of the score products (0: compiler's order)
 #endif
+#ifndef FA_FWD_HALVES
+#define FA_FWD_HALVES 0  // 1: each 32-key half of a tile runs scores to P V before the next
+#endif
 #ifndef FA_FWD64_WPE
 #define FA_FWD64_WPE 4
 #endif
@@ -157,25 +160,30 @@ void fwd_kernel(FwdParams p) {
     // them, and every row sees [lo(qw_last), hi(qw0)]
     const int qw_last = qw0 + WQ - 1;
     const bool active = k0 <= band.hi(qw_last) && k0 + G::KT - 1 >= band.lo(qw0);
-    if (active) {
+    // key halves KB0 .. KB0 + NKB - 1 (32 keys each) of the tile
+    auto key_halves = [&](auto kb0_c, auto nkb_c) __attribute__((always_inline)) {
+      constexpr int KB0 = decltype(kb0_c)::value, NKB = decltype(nkb_c)::value;
+      const int ka = k0 + KB0 * 32, kz = ka + NKB * 32 - 1;  // the halves' keys
+      // halves no row of the wave sees add nothing
+      if (NKB < 2 && (ka > band.hi(qw_last) || kz < band.lo(qw0))) return;
       // 1. S^T = K Q^T for each (key block kb, query block qb)
-      f32x16 s[QB][2];
+      f32x16 s[QB][NKB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int j = 0; j < NKB; ++j) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{0};
+        for (int qb = 0; qb < QB; ++qb) s[qb][j] = f32x16{0};
 #pragma unroll
         for (int t = 0; t < G::NKS; ++t) {
-          const V8 a = toff.template row_operand<T>(ks, kb * 32, t);
+          const V8 a = toff.template row_operand<T>(ks, (KB0 + j) * 32, t);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][t], s[qb][kb]);
+          for (int qb = 0; qb < QB; ++qb) s[qb][j] = mfma32(a, qf[qb][t], s[qb][j]);
         }
       }
-      if constexpr (QB == 1) sched_reads_ahead<2 * G::NKS, FA_FWD_AHEAD>();
+      if constexpr (QB == 1) sched_reads_ahead<NKB * G::NKS, FA_FWD_AHEAD>();
       // 2. mask keys outside the row's band (future keys, keys outside the
       // window, keys past the end).  Key of register r is k0 + g*4 + C(kb, r),
       // C = kb*32 + (r/4)*8 + r%4; it is hidden iff C < lb or C > ub.
-      const bool need_mask = k0 < band.lo(qw_last) || k0 + G::KT - 1 > band.hi(qw0);
+      const bool need_mask = ka < band.lo(qw_last) || kz > band.hi(qw0);
       if (need_mask) {
         FA_KEEP_BRANCH();
         // one compare-and-select per bound on the VALU (an OR of the two
@@ -185,32 +193,34 @@ void fwd_kernel(FwdParams p) {
           const int i = qw0 + qb * 32 + l32;
           const int ub = band.hi(i) - k0 - g * 4;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int j = 0; j < NKB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
-              s[qb][kb][r] = C > ub ? kNegInf : s[qb][kb][r];
+              const int C = (KB0 + j) * 32 + (r >> 2) * 8 + (r & 3);
+              s[qb][j][r] = C > ub ? kNegInf : s[qb][j][r];
             }
           if (p.window > 0) {
             const int lb = band.lo(i) - k0 - g * 4;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int j = 0; j < NKB; ++j)
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
-                const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
-                s[qb][kb][r] = C < lb ? kNegInf : s[qb][kb][r];
+                const int C = (KB0 + j) * 32 + (r >> 2) * 8 + (r & 3);
+                s[qb][j][r] = C < lb ? kNegInf : s[qb][j][r];
               }
           }
         }
       }
       // 3-4. per 32-key half kb: row maxima of the half, reference move if
       // needed, P = 2^(S c - ref) packed to the input type, row sums, then
-      // O^T += V^T P^T for its two key steps.  The exponentials of half 0
-      // overlap the score products of half 1 still in flight, and those of
-      // half 1 the P V products of half 0.  The reference may move between
-      // the halves; O and l are rescaled with it, so the result is the same.
+      // O^T += V^T P^T for its two key steps.  With both halves' scores
+      // computed first, the exponentials of half 0 overlap the score products
+      // of half 1 still in flight, and those of half 1 the P V products of
+      // half 0.  The reference may move between the halves; O and l are
+      // rescaled with it, so the result is the same.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int j = 0; j < NKB; ++j) {
+        const int kb = KB0 + j;
         // dropout: generator bytes of this half's keys (byte e of kw[qb][rr]
         // decides the key of register rr * 4 + e)
         u32x4 kw[QB];
@@ -226,9 +236,9 @@ void fwd_kernel(FwdParams p) {
         for (int qb = 0; qb < QB; ++qb) {
           float m4[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) m4[i] = vmax(s[qb][kb][i], s[qb][kb][i + 4]);
+          for (int i = 0; i < 4; ++i) m4[i] = vmax(s[qb][j][i], s[qb][j][i + 4]);
 #pragma unroll
-          for (int r = 8; r < 16; ++r) m4[r & 3] = vmax(m4[r & 3], s[qb][kb][r]);
+          for (int r = 8; r < 16; ++r) m4[r & 3] = vmax(m4[r & 3], s[qb][j][r]);
           mxs[qb] = vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3])) * p.c;
           move |= mxs[qb] > m_ref[qb] + kRescaleTau;
         }
@@ -256,8 +266,8 @@ void fwd_kernel(FwdParams p) {
             float lp = 0.f;
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-              const float e0 = fast_exp2(__builtin_fmaf(s[qb][kb][r0 + 2 * h], p.c, -ref[qb]));
-              const float e1 = fast_exp2(__builtin_fmaf(s[qb][kb][r0 + 2 * h + 1], p.c, -ref[qb]));
+              const float e0 = fast_exp2(__builtin_fmaf(s[qb][j][r0 + 2 * h], p.c, -ref[qb]));
+              const float e1 = fast_exp2(__builtin_fmaf(s[qb][j][r0 + 2 * h + 1], p.c, -ref[qb]));
               w[h] = pack2<T>(e0, e1);
               if constexpr (__is_same(T, _Float16)) {
                 lp = add_pair<T>(w[h], lp);  // fp16: the rounded weights P V uses
@@ -277,6 +287,14 @@ void fwd_kernel(FwdParams p) {
             for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(a, bp[qb], o[qb][db]);
           }
         }
+      }
+    };
+    if (active) {
+      if constexpr (FA_FWD_HALVES) {
+        key_halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+        key_halves(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+      } else {
+        key_halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
       }
     }
     wait_all_memory();  // this thread's copies into the next stage have landed
