@@ -159,8 +159,8 @@ int fa_bwd_dkdv(const fa_problem* p, const void* q, const void* k, const void* v
 int fa_mask_compile(const uint8_t* mask, int32_t nb, int32_t* row_ptr, int32_t* col_idx,
                     int32_t* col_ptr, int32_t* row_idx, void* stream);
 
-/* Decode-shaped forward (a few queries against many keys, the survey's
- * decode workload next to grouped heads).  q and o are (B, H, n_q, d) in the
+/* Decode-shaped forward (a few queries against many keys, with grouped K/V
+ * heads).  q and o are (B, H, n_q, d) in the
  * problem's dtype, lse is float32 (B, H, n_q); k and v are (B, H_kv, N, d) with
  * N = p->N.  Query i of each head sits at position N - n_q + i of the key
  * sequence, and causal / window visibility use that position (with causal and

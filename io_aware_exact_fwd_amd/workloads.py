@@ -29,8 +29,8 @@ Extensions of the method (sliding window, grouped K/V heads, dropout):
                 70B (64 query heads sharing 8 K/V heads, head dim 128)
   gpt2_medium_dropout  gpt2_medium with attention dropout p = 0.1
 
-Decode shape (a few new queries against a long key sequence, the survey's
-workload next to grouped heads; forward only):
+Decode shape (a few new queries against a long key sequence, with grouped
+K/V heads; forward only):
 
   decode_gqa    B=16 H=64 H_kv=8 N=8192 d=128 bf16, n_q=1 (the last position),
                 causal: one token of a batch of 16 sequences with the

@@ -58,8 +58,8 @@ Z = Z01 / (1 - p'),
 Fully masked rows (possible only with a general block mask): O_i = 0,
 LSE_i = -inf, and the row contributes nothing to any gradient.
 
-Queries at an offset (the decode shape of the survey's next rows: a few
-queries against a long key sequence, as in incremental decoding after the
+Queries at an offset (the decode shape: a few queries against a long key
+sequence, as in incremental decoding after the
 [ldl] sections 4-6 discussion of grouped heads): query row r sits at position
 q_offset + r of the key sequence, and every visibility rule above uses that
 position (causal: key j <= q_offset + r; window: |q_offset + r - j| < W).
