@@ -42,6 +42,7 @@ PEAK_FP8_TFLOPS = 2 * PEAK_MFMA_TFLOPS  # dense E4M3 matrix rate, twice the 16-b
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+DROPOUT_SEED = 2024  # generator seed of the dropout workload's keep mask
 KERNEL_SOURCES = os.path.join(ROOT, "io_aware_exact_fwd_amd", "csrc")
 
 
@@ -83,13 +84,14 @@ def kernel_work(w):
     write, once."""
     from io_aware_exact_fwd_amd.workloads import kept_pairs_per_head
 
-    pairs = kept_pairs_per_head(w.N, w.causal, w.block_mask(), w.mask_block) * w.B * w.H
-    x = w.B * w.H * w.N * w.d * w.elem_bytes  # one (B, H, N, d) tensor
-    n4 = w.B * w.H * w.N * 4                  # one float32 (B, H, N) vector
+    pairs = kept_pairs_per_head(w.N, w.causal, w.block_mask(), w.mask_block, w.window) * w.B * w.H
+    x = w.B * w.H * w.N * w.d * w.elem_bytes      # one (B, H, N, d) tensor
+    xkv = w.B * w.H_kv * w.N * w.d * w.elem_bytes  # one K/V-shaped tensor
+    n4 = w.B * w.H * w.N * 4                      # one float32 (B, H, N) vector
     return {
-        "fwd": {"flops": 4.0 * w.d * pairs, "bytes": 4 * x + n4},            # Q K V -> O, LSE
-        "dq": {"flops": 6.0 * w.d * pairs, "bytes": 6 * x + 2 * n4},         # Q K V O dO LSE -> dQ D
-        "dkdv": {"flops": 8.0 * w.d * pairs, "bytes": 6 * x + 2 * n4},       # Q K V dO LSE D -> dK dV
+        "fwd": {"flops": 4.0 * w.d * pairs, "bytes": 2 * x + 2 * xkv + n4},       # Q K V -> O, LSE
+        "dq": {"flops": 6.0 * w.d * pairs, "bytes": 4 * x + 2 * xkv + 2 * n4},    # Q K V O dO LSE -> dQ D
+        "dkdv": {"flops": 8.0 * w.d * pairs, "bytes": 2 * x + 4 * xkv + 2 * n4},  # Q K V dO LSE D -> dK dV
     }
 
 
@@ -307,17 +309,22 @@ def cpu_baseline(w, inputs, seconds):
     q, k, v, do = inputs
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     bm = w.block_mask()
+    grp = w.H // w.H_kv
+    ext = dict(window=w.window)
+    if w.dropout:
+        ext.update(dropout_p=w.dropout, seed=DROPOUT_SEED, offset=0)
     done = 0
     t0 = time.perf_counter()
     for b, h in heads:
-        qn, kn, vn, don = (t[b, h].float().numpy() for t in (q, k, v, do))
-        attention_forward(qn, kn, vn, w.scale, w.causal, bm, w.mask_block)
-        attention_backward(qn, kn, vn, don, w.scale, w.causal, bm, w.mask_block)
+        qn, don = (t[b, h].float().numpy() for t in (q, do))
+        kn, vn = (t[b, h // grp].float().numpy() for t in (k, v))
+        attention_forward(qn, kn, vn, w.scale, w.causal, bm, w.mask_block, **ext)
+        attention_backward(qn, kn, vn, don, w.scale, w.causal, bm, w.mask_block, **ext)
         done += 1
         if time.perf_counter() - t0 >= seconds:
             break
     el = time.perf_counter() - t0
-    flops = 14.0 * w.d * kept_pairs_per_head(w.N, w.causal, bm, w.mask_block) * done
+    flops = 14.0 * w.d * kept_pairs_per_head(w.N, w.causal, bm, w.mask_block, w.window) * done
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
@@ -479,19 +486,23 @@ def main():
     if w.fp8:
         fp8_bench(w, args, dev)
         return
-    inputs = make_inputs(w.B, w.H, w.N, w.d, w.dtype)
+    inputs = make_inputs(w.B, w.H, w.N, w.d, w.dtype, hkv=w.H_kv)
     q, k, v, do = (t.to(dev) for t in inputs)
     bm = w.block_mask()
     bmd = None if bm is None else torch.as_tensor(bm, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    p, ws, ws_n, bmt = bwd_workspace(q, w.causal, w.scale, bmd, w.mask_block)
+    # the workload's window, grouped K/V heads (through k's shape) and dropout
+    ext = dict(window=w.window)
+    if w.dropout:
+        ext.update(dropout_p=w.dropout, seed=DROPOUT_SEED, offset=0)
+    p, ws, ws_n, bmt = bwd_workspace(q, w.causal, w.scale, bmd, w.mask_block, k=k, **ext)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        fa_fwd(q, k, v, w.causal, w.scale, bmt, w.mask_block, out=o, lse=lse)
+        fa_fwd(q, k, v, w.causal, w.scale, bmt, w.mask_block, out=o, lse=lse, **ext)
         if ev is not None:
             ev[1].record()
         fa_bwd_dq(p, q, k, v, o, do, lse, dq, ws, ws_n)
@@ -501,8 +512,9 @@ def main():
         if ev is not None:
             ev[3].record()
 
-    log(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} "
-        f"causal={w.causal} mask={w.mask}; warmup {args.warmup}, steps {args.steps}")
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} H_kv={w.H_kv} N={w.N} d={w.d} {w.dtype} "
+        f"causal={w.causal} mask={w.mask} window={w.window} dropout={w.dropout}; "
+        f"warmup {args.warmup}, steps {args.steps}")
     settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
@@ -577,7 +589,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "dtype": w.dtype, "causal": w.causal, "scale": w.scale,
-                   "block_mask": w.mask},
+                   "block_mask": w.mask,
+                   **({"H_kv": w.H_kv} if w.H_kv != w.H else {}),
+                   **({"window": w.window} if w.window else {}),
+                   **({"dropout": w.dropout} if w.dropout else {})},
         "pct_of_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
         "sclk_mhz": sclk,
         "pct_of_mfma_peak_at_sclk": round(100 * value / peak_at_sclk, 2) if sclk else None,
