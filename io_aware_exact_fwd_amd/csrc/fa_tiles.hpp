@@ -39,6 +39,15 @@ struct Band {
 // Tiles of size TS that meet positions [lo, hi] (inclusive).  Dense: tiles
 // first .. first + count - 1.  MASKED: entries first .. first + count - 1 of the
 // flattened list "each kept block of `list`, split into mask_block / TS tiles".
+// One entry of a compiled mask list.  Read through the constant address space
+// so that it becomes a scalar load (the index is uniform across the wave): its
+// wait counts scalar and LDS operations only, while a vector load's wait would
+// also count the LDS copies of the next tile issued just before, and every
+// step would then stall until its prefetch had landed.
+__device__ __forceinline__ int32_t list_at(const int32_t* list, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)list)[i];
+}
+
 template <int TS, bool MASKED>
 struct TileRun {
   int count;
@@ -62,7 +71,7 @@ struct TileRun {
     } else {
       int skip = 0, c = 0;
       for (int i = 0; i < nblocks; ++i) {
-        const int t0 = blocks[base + i] * mb;
+        const int t0 = list_at(blocks, base + i) * mb;
         if (t0 + mb - 1 < lo) {
           skip += per;
           continue;
@@ -83,7 +92,7 @@ struct TileRun {
     if constexpr (!MASKED) {
       return j * TS;
     } else {
-      return blocks[base + j / per] * mb + (j % per) * TS;
+      return list_at(blocks, base + j / per) * mb + (j % per) * TS;
     }
   }
 };
@@ -95,8 +104,8 @@ __device__ __forceinline__ TileRun<KT, MASKED> key_tiles(const MaskLists& m, con
   TileRun<KT, MASKED> t;
   if constexpr (MASKED) {
     const int qb = q_lo / m.mask_block;
-    const int base = m.row_ptr[qb];
-    t.init(b.lo(q_lo), b.hi(q_hi), m.col_idx, base, m.row_ptr[qb + 1] - base, m.mask_block);
+    const int base = list_at(m.row_ptr, qb);
+    t.init(b.lo(q_lo), b.hi(q_hi), m.col_idx, base, list_at(m.row_ptr, qb + 1) - base, m.mask_block);
   } else {
     t.init(b.lo(q_lo), b.hi(q_hi), nullptr, 0, 0, 0);
   }
@@ -111,8 +120,8 @@ __device__ __forceinline__ TileRun<QT, MASKED> query_tiles(const MaskLists& m, c
   k_hi = min(k_hi, b.N - 1);
   if constexpr (MASKED) {
     const int kb = k_lo / m.mask_block;
-    const int base = m.col_ptr[kb];
-    t.init(b.qlo(k_lo), b.qhi(k_hi), m.row_idx, base, m.col_ptr[kb + 1] - base, m.mask_block);
+    const int base = list_at(m.col_ptr, kb);
+    t.init(b.qlo(k_lo), b.qhi(k_hi), m.row_idx, base, list_at(m.col_ptr, kb + 1) - base, m.mask_block);
   } else {
     t.init(b.qlo(k_lo), b.qhi(k_hi), nullptr, 0, 0, 0);
   }
