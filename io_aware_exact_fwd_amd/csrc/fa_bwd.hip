@@ -44,6 +44,9 @@ namespace fa {
 #ifndef FA_DQ_WPE
 #define FA_DQ_WPE 4
 #endif
+#ifndef FA_DQ64_MASKED_NST
+#define FA_DQ64_MASKED_NST 2  // 3 measured 4 % slower on the N = 65536 butterfly workload
+#endif
 #ifndef FA_DQ64_DROP_WPE
 #define FA_DQ64_DROP_WPE 3  // the dropout generator's registers: four waves would spill
 #endif
@@ -93,19 +96,25 @@ struct DqGeom {
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
   // waves per SIMD the registers allow
-  static constexpr int wpe(bool drop) {
+  static constexpr int wpe(bool drop, bool masked) {
     if (D == 128) return drop ? FA_DQ128_DROP_WPE : FA_DQ128_WPE;
+    if (masked && nst(masked) > 2) return 3;  // LDS: three 48 KiB workgroups per CU
     return drop ? FA_DQ64_DROP_WPE : FA_DQ_WPE;
   }
+  // LDS stages: block-sparse at head dim 64 may keep the copies of two key
+  // tiles in flight (its kept tiles are scattered over the sequence)
+  static constexpr int nst(bool masked) { return masked && D == 64 ? FA_DQ64_MASKED_NST : 2; }
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(DqGeom<D>::wpe(DROP), DqGeom<D>::wpe(DROP))))
+                          amdgpu_waves_per_eu(DqGeom<D>::wpe(DROP, MASKED),
+                                              DqGeom<D>::wpe(DROP, MASKED))))
 void bwd_dq_kernel(BwdParams p) {
   using G = DqGeom<D>;
   using V8 = typename Vec8<T>::type;
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
+  constexpr int NST = G::nst(MASKED);
+  __shared__ __attribute__((aligned(16))) char smem[NST * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,16 +181,22 @@ void bwd_dq_kernel(BwdParams p) {
 
   const int ntiles = tiles.count;
   if (ntiles > 0) gload(0, 0);
+  if (NST > 2 && ntiles > 1) gload(1, 1);
   wait_all_memory();
   __syncthreads();
 
   const TileOffsets<D> toff(lane);
-  // one key tile; the LDS stage is a compile-time constant (two steps per
+  // With NST stages the copies of tile it + NST - 1 are issued at the start of
+  // step it, and a step ends once this thread's copies of the next tile have
+  // landed (those of the tile after it may stay in flight: the loop issues no
+  // other vector-memory operations, and they complete in issue order).
+  constexpr int COPIES = 2 * (G::KT * D / 8 / 256);  // K and V copies per thread per tile
+  // one key tile; the LDS stage is a compile-time constant (NST steps per
   // iteration of the loop below), so it joins the reads' immediate offsets
   auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
     constexpr int cur = decltype(stage)::value;
-    const bool more = it + 1 < ntiles;
-    if (more) gload(it + 1, cur ^ 1);
+    constexpr int pre = (cur + NST - 1) % NST;  // stage of tile it + NST - 1
+    if (it + NST - 1 < ntiles) gload(it + NST - 1, pre);
 
     const int k0 = tiles.pos0(it);
     const char* ks = smem + cur * G::STAGE;
@@ -239,7 +254,7 @@ void bwd_dq_kernel(BwdParams p) {
         u32x4 kw;
         if constexpr (DROP)
           kw = drop_bytes_query_lanes(p.drop, (uint32_t)head, k0 + (KB0 + i) * 32, qw0,
-                                      smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
+                                      smem + NST * G::STAGE + wave * kDropLdsPerWave, lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pr = fast_exp2(__builtin_fmaf(s[i][r], p.c, -lse2));
@@ -272,12 +287,19 @@ void bwd_dq_kernel(BwdParams p) {
         halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
       }
     }
-    wait_all_memory();  // this thread's copies into the next stage have landed
+    // this thread's copies of tile it + 1 have landed
+    if (NST > 2 && it + 2 < ntiles)
+      __builtin_amdgcn_s_waitcnt(vmcnt_at_most(COPIES));
+    else
+      wait_all_memory();
     __syncthreads();
   };
-  for (int it = 0; it < ntiles; it += 2) {
+  for (int it = 0; it < ntiles; it += NST) {
     step(it, std::integral_constant<int, 0>{});
     if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
+    if constexpr (NST > 2) {
+      if (it + 2 < ntiles) step(it + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   if (q < N) {

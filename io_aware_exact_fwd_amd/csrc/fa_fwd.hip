@@ -64,6 +64,16 @@ constexpr float kRescaleTau = 8.0f;
 #ifndef FA_FWD64_WPE
 #define FA_FWD64_WPE 4
 #endif
+// Block-sparse, head dim 64: LDS stages and waves per SIMD.  Three stages keep
+// the copies of two scattered key tiles in flight (48 KiB per workgroup, so
+// three waves per SIMD); on the N = 65536 butterfly workload two stages at four
+// waves measured 7 % faster.
+#ifndef FA_FWD64_MASKED_NST
+#define FA_FWD64_MASKED_NST 2
+#endif
+#ifndef FA_FWD64_MASKED_WPE
+#define FA_FWD64_MASKED_WPE 4
+#endif
 
 template <int D, int NW>
 struct FwdGeom {
@@ -76,7 +86,7 @@ struct FwdGeom {
   static_assert(NW == 4, "the tile copies assume 4 waves");
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP, int NW, int QB, int WPE>
+template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP, int NW, int QB, int WPE, int NST>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(FwdParams p) {
@@ -84,7 +94,8 @@ void fwd_kernel(FwdParams p) {
   using V8 = typename Vec8<T>::type;
   constexpr int BR = NW * QB * 32;  // query rows per workgroup
   constexpr int WQ = QB * 32;       // query rows per wave
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? NW * kDropLdsPerWave : 0)];
+  static_assert(NST == 2 || NST == 3, "two or three LDS stages");
+  __shared__ __attribute__((aligned(16))) char smem[NST * G::STAGE + (DROP ? NW * kDropLdsPerWave : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -142,16 +153,28 @@ void fwd_kernel(FwdParams p) {
 
   const TileOffsets<D> toff(lane);
   const int ntiles = tiles.count;
+  // With NST stages the copies of tile it + NST - 1 are issued at the start of
+  // step it; a step ends once this thread's copies of the next tile have
+  // landed (those of the tile after it may stay in flight: vector-memory
+  // operations complete in issue order), and the barrier publishes them.
+  constexpr int COPIES = 2 * (G::KT * D / 8 / 256);  // K and V copies per thread per tile
+  auto land_next = [&](bool younger_in_flight) {
+    if (NST > 2 && younger_in_flight)
+      __builtin_amdgcn_s_waitcnt(vmcnt_at_most(COPIES));
+    else
+      wait_all_memory();
+  };
   if (ntiles > 0) gload(0, 0);
-  wait_all_memory();
+  if (NST > 2 && ntiles > 1) gload(1, 1);
+  land_next(ntiles > 1);
   __syncthreads();
 
   // one key tile; the LDS stage is a compile-time constant (the loop below
-  // runs two steps per iteration), so it joins the reads' immediate offsets
+  // runs NST steps per iteration), so it joins the reads' immediate offsets
   auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
     constexpr int cur = decltype(stage)::value;
-    const bool more = it + 1 < ntiles;
-    if (more) gload(it + 1, cur ^ 1);
+    constexpr int pre = (cur + NST - 1) % NST;  // stage of tile it + NST - 1
+    if (it + NST - 1 < ntiles) gload(it + NST - 1, pre);
 
     const int k0 = tiles.pos0(it);
     const char* ks = smem + cur * G::STAGE;
@@ -228,7 +251,7 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             kw[qb] = drop_bytes_query_lanes(p.drop, (uint32_t)head, k0 + kb * 32, qw0 + qb * 32,
-                                            smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
+                                            smem + NST * G::STAGE + wave * kDropLdsPerWave, lane);
         }
         float mxs[QB];
         bool move = false;
@@ -297,12 +320,15 @@ void fwd_kernel(FwdParams p) {
         key_halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
       }
     }
-    wait_all_memory();  // this thread's copies into the next stage have landed
+    land_next(it + 2 < ntiles);  // this thread's copies of tile it + 1 have landed
     __syncthreads();
   };
-  for (int it = 0; it < ntiles; it += 2) {
+  for (int it = 0; it < ntiles; it += NST) {
     step(it, std::integral_constant<int, 0>{});
     if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
+    if constexpr (NST > 2) {
+      if (it + 2 < ntiles) step(it + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   // epilogue: deferred normalisation (and the scale of kept weights under
@@ -329,15 +355,15 @@ void fwd_kernel(FwdParams p) {
   }
 }
 
-template <typename T, int D, bool MASKED, bool DROP, int NW, int QB, int WPE>
+template <typename T, int D, bool MASKED, bool DROP, int NW, int QB, int WPE, int NST = 2>
 static hipError_t launch_fwd_t(FwdParams p, bool causal, hipStream_t s) {
   constexpr int BR = NW * QB * 32;
   p.nqt = (p.N + BR - 1) / BR;
   dim3 grid(p.nheads * p.nqt), block(NW * 64);
   if (causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, true, MASKED, DROP, NW, QB, WPE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<T, D, true, MASKED, DROP, NW, QB, WPE, NST>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, false, MASKED, DROP, NW, QB, WPE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<T, D, false, MASKED, DROP, NW, QB, WPE, NST>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -348,7 +374,6 @@ static hipError_t launch_fwd_t(FwdParams p, bool causal, hipStream_t s) {
 template <typename T>
 static hipError_t launch_fwd_dtype(const FwdParams& p, int d, bool causal, bool masked, bool drop,
                                    hipStream_t s) {
-  constexpr int BR64 = FA_FWD64_NW * FA_FWD64_QB * 32;
   if (drop) {
     if (d == 64)
       return masked ? launch_fwd_t<T, 64, true, true, 4, 1, 2>(p, causal, s)
@@ -357,9 +382,9 @@ static hipError_t launch_fwd_dtype(const FwdParams& p, int d, bool causal, bool 
                   : launch_fwd_t<T, 128, false, true, 4, 1, 2>(p, causal, s);
   }
   if (d == 64) {
-    if (masked && BR64 != 128) return launch_fwd_t<T, 64, true, false, 4, 1, 4>(p, causal, s);
-    if (masked)
-      return launch_fwd_t<T, 64, true, false, FA_FWD64_NW, FA_FWD64_QB, FA_FWD64_WPE>(p, causal, s);
+    if (masked)  // 128-row workgroups; copies two tiles ahead (see FA_FWD64_MASKED_NST)
+      return launch_fwd_t<T, 64, true, false, 4, 1, FA_FWD64_MASKED_WPE, FA_FWD64_MASKED_NST>(
+          p, causal, s);
     return launch_fwd_t<T, 64, false, false, FA_FWD64_NW, FA_FWD64_QB, FA_FWD64_WPE>(p, causal, s);
   }
   if (masked) return launch_fwd_t<T, 128, true, false, 4, 1, 2>(p, causal, s);

@@ -5,55 +5,119 @@
 // or computed, which is how block-sparse attention scales its IO by the
 // non-zero fraction (block-sparse paragraph of the agihunt.info summary).
 //
-// One workgroup; the mask is small (N/128 blocks on a side).  Counts, then a
-// serial prefix sum by one thread, then each thread fills whole rows/columns,
-// so the lists come out in increasing order and identical on every run.
+// Three launches, each reading the nb x nb mask bytes at most twice:
+//   count: workgroup g counts the kept blocks of row g and of column g;
+//   scan:  one workgroup turns the counts into the offsets row_ptr, col_ptr;
+//   fill:  workgroup g writes the lists of row g and column g, each thread a
+//          contiguous chunk at the offset given by a scan of the chunk counts.
+// The lists come out in increasing order and identical on every run.
 #include "fa_kernels.hpp"
 
 namespace fa {
+namespace {
 
-__global__ __launch_bounds__(256) void mask_compile_kernel(const uint8_t* mask, int nb,
-                                                           int32_t* row_ptr, int32_t* col_idx,
-                                                           int32_t* col_ptr, int32_t* row_idx) {
-  const int tid = threadIdx.x;
-  for (int r = tid; r < nb; r += blockDim.x) {
-    int c_row = 0;
-    for (int c = 0; c < nb; ++c) c_row += mask[(size_t)r * nb + c] != 0;
-    row_ptr[r + 1] = c_row;
-  }
-  for (int c = tid; c < nb; c += blockDim.x) {
-    int c_col = 0;
-    for (int r = 0; r < nb; ++r) c_col += mask[(size_t)r * nb + c] != 0;
-    col_ptr[c + 1] = c_col;
-  }
-  __threadfence();
+constexpr int kMaskThreads = 256;
+
+// Sum over the workgroup (256 threads); every thread gets the total.
+__device__ int block_sum(int v, int* lds) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int wave = threadIdx.x >> 6;
   __syncthreads();
-  if (tid == 0) {
-    row_ptr[0] = 0;
-    col_ptr[0] = 0;
-    for (int i = 0; i < nb; ++i) {
-      row_ptr[i + 1] += row_ptr[i];
-      col_ptr[i + 1] += col_ptr[i];
+  if ((threadIdx.x & 63) == 0) lds[wave] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < kMaskThreads / 64; ++w) t += lds[w];
+  return t;
+}
+
+// Exclusive prefix sum over the workgroup's threads in thread order.
+__device__ int block_exclusive_scan(int v, int* lds) {
+  __syncthreads();
+  lds[threadIdx.x] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < kMaskThreads; ++i) {
+      const int x = lds[i];
+      lds[i] = run;
+      run += x;
     }
   }
-  __threadfence();
   __syncthreads();
-  for (int r = tid; r < nb; r += blockDim.x) {
-    int pos = row_ptr[r];
-    for (int c = 0; c < nb; ++c)
-      if (mask[(size_t)r * nb + c] != 0) col_idx[pos++] = c;
-  }
-  for (int c = tid; c < nb; c += blockDim.x) {
-    int pos = col_ptr[c];
-    for (int r = 0; r < nb; ++r)
-      if (mask[(size_t)r * nb + c] != 0) row_idx[pos++] = r;
+  return lds[threadIdx.x];
+}
+
+__global__ __launch_bounds__(kMaskThreads) void mask_count_kernel(const uint8_t* mask, int nb,
+                                                                  int32_t* row_ptr,
+                                                                  int32_t* col_ptr) {
+  __shared__ int lds[kMaskThreads / 64];
+  const int g = blockIdx.x;
+  int rc = 0, cc = 0;
+  for (int c = threadIdx.x; c < nb; c += kMaskThreads) rc += mask[(size_t)g * nb + c] != 0;
+  for (int r = threadIdx.x; r < nb; r += kMaskThreads) cc += mask[(size_t)r * nb + g] != 0;
+  rc = block_sum(rc, lds);
+  cc = block_sum(cc, lds);
+  if (threadIdx.x == 0) {
+    row_ptr[g + 1] = rc;
+    col_ptr[g + 1] = cc;
   }
 }
 
+// a[1 .. nb] holds counts; afterwards a[i] = sum of the first i counts.
+__device__ void offsets_in_place(int32_t* a, int nb, int* lds) {
+  const int per = (nb + kMaskThreads - 1) / kMaskThreads;
+  const int lo = min(nb, (int)threadIdx.x * per), hi = min(nb, lo + per);
+  int local = 0;
+  for (int i = lo; i < hi; ++i) local += a[i + 1];
+  int run = block_exclusive_scan(local, lds);
+  for (int i = lo; i < hi; ++i) {
+    run += a[i + 1];
+    a[i + 1] = run;
+  }
+  if (threadIdx.x == 0) a[0] = 0;
+}
+
+__global__ __launch_bounds__(kMaskThreads) void mask_scan_kernel(int nb, int32_t* row_ptr,
+                                                                 int32_t* col_ptr) {
+  __shared__ int lds[kMaskThreads];
+  offsets_in_place(row_ptr, nb, lds);
+  offsets_in_place(col_ptr, nb, lds);
+}
+
+__global__ __launch_bounds__(kMaskThreads) void mask_fill_kernel(const uint8_t* mask, int nb,
+                                                                 const int32_t* row_ptr,
+                                                                 int32_t* col_idx,
+                                                                 const int32_t* col_ptr,
+                                                                 int32_t* row_idx) {
+  __shared__ int lds[kMaskThreads];
+  const int g = blockIdx.x;
+  const int per = (nb + kMaskThreads - 1) / kMaskThreads;
+  const int lo = min(nb, (int)threadIdx.x * per), hi = min(nb, lo + per);
+  // row g: its kept columns, in increasing order
+  int n = 0;
+  for (int c = lo; c < hi; ++c) n += mask[(size_t)g * nb + c] != 0;
+  int pos = row_ptr[g] + block_exclusive_scan(n, lds);
+  for (int c = lo; c < hi; ++c)
+    if (mask[(size_t)g * nb + c] != 0) col_idx[pos++] = c;
+  // column g: the rows that keep it, in increasing order
+  n = 0;
+  for (int r = lo; r < hi; ++r) n += mask[(size_t)r * nb + g] != 0;
+  pos = col_ptr[g] + block_exclusive_scan(n, lds);
+  for (int r = lo; r < hi; ++r)
+    if (mask[(size_t)r * nb + g] != 0) row_idx[pos++] = r;
+}
+
+}  // namespace
+
 hipError_t launch_mask_compile(const uint8_t* mask, int nb, int32_t* row_ptr, int32_t* col_idx,
                                int32_t* col_ptr, int32_t* row_idx, hipStream_t s) {
-  hipLaunchKernelGGL(mask_compile_kernel, dim3(1), dim3(256), 0, s, mask, nb, row_ptr, col_idx,
-                     col_ptr, row_idx);
+  hipLaunchKernelGGL(mask_count_kernel, dim3(nb), dim3(kMaskThreads), 0, s, mask, nb, row_ptr,
+                     col_ptr);
+  hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(kMaskThreads), 0, s, nb, row_ptr, col_ptr);
+  hipLaunchKernelGGL(mask_fill_kernel, dim3(nb), dim3(kMaskThreads), 0, s, mask, nb, row_ptr,
+                     col_idx, col_ptr, row_idx);
   return hipGetLastError();
 }
 
