@@ -63,7 +63,7 @@ namespace fa {
 #define FA_DKDV_QBLK 1  // 32-query blocks of a step handled together (scores to products)
 #endif
 #ifndef FA_DKDV_NST
-#define FA_DKDV_NST 3  // LDS stages of the d = 64 dK/dV ring (2 or 3)
+#define FA_DKDV_NST 2  // LDS stages of the d = 64 dK/dV ring (2 or 3)
 #endif
 #ifndef FA_DKDV_AHEAD
 #define FA_DKDV_AHEAD 4  // LDS reads issued ahead of the score products (0: compiler's order)

@@ -68,6 +68,9 @@ constexpr float kRescaleTau = 8.0f;
 // the copies of two scattered key tiles in flight (48 KiB per workgroup, so
 // three waves per SIMD); on the N = 65536 butterfly workload two stages at four
 // waves measured 7 % faster.
+#ifndef FA_FWD64_DROP_WPE
+#define FA_FWD64_DROP_WPE 4  // dropout forward, head dim 64 (126 VGPRs; 10 % faster than 2)
+#endif
 #ifndef FA_FWD64_MASKED_NST
 #define FA_FWD64_MASKED_NST 2
 #endif
@@ -376,8 +379,8 @@ static hipError_t launch_fwd_dtype(const FwdParams& p, int d, bool causal, bool 
                                    hipStream_t s) {
   if (drop) {
     if (d == 64)
-      return masked ? launch_fwd_t<T, 64, true, true, 4, 1, 2>(p, causal, s)
-                    : launch_fwd_t<T, 64, false, true, 4, 1, 2>(p, causal, s);
+      return masked ? launch_fwd_t<T, 64, true, true, 4, 1, FA_FWD64_DROP_WPE>(p, causal, s)
+                    : launch_fwd_t<T, 64, false, true, 4, 1, FA_FWD64_DROP_WPE>(p, causal, s);
     return masked ? launch_fwd_t<T, 128, true, true, 4, 1, 2>(p, causal, s)
                   : launch_fwd_t<T, 128, false, true, 4, 1, 2>(p, causal, s);
   }
