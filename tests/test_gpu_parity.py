@@ -120,10 +120,23 @@ def test_zero_queries_lse_counts_visible_keys(case):
         assert np.abs(got[0, h][live] - want[live]).max() <= 1e-5
 
 
+def _sparse_mask_with_empty_lines(nb, density, seed):
+    bm = (np.random.default_rng(seed).random((nb, nb)) < density).astype(np.uint8)
+    bm[[0, 5, nb - 1], :] = 0   # query blocks that keep nothing
+    bm[:, [3, nb // 2]] = 0     # key blocks nobody keeps
+    return bm
+
+
 def test_mask_compile_lists_exact():
+    """Row and column lists against numpy, bit for bit: sizes below and above
+    one row or column per thread of the compile kernels (256), a size that
+    leaves the last thread a partial chunk, empty rows and columns, a dense
+    mask and the one-block masks."""
     dev = torch.device("cuda:0")
     for bm in (butterfly_block_mask(512), _mask_with_holes(16),
-               (np.random.default_rng(0).random((37, 37)) < 0.3).astype(np.uint8)):
+               (np.random.default_rng(0).random((37, 37)) < 0.3).astype(np.uint8),
+               _sparse_mask_with_empty_lines(777, 0.05, 1), np.ones((300, 300), np.uint8),
+               np.ones((1, 1), np.uint8), np.zeros((1, 1), np.uint8)):
         say(f"[case] mask compile nb={bm.shape[0]}")
         row_ptr, col_idx, col_ptr, row_idx = fa_mask_compile(torch.as_tensor(bm, device=dev))
         b = bm != 0
