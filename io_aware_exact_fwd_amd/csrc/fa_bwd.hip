@@ -77,6 +77,9 @@ namespace fa {
 #ifndef FA_DKDV64_WPE
 #define FA_DKDV64_WPE 3
 #endif
+#ifndef FA_DKDV64_DROP_WPE
+#define FA_DKDV64_DROP_WPE 2  // dropout's generator registers: three waves would spill
+#endif
 #ifndef FA_DKDV128_WPE
 #define FA_DKDV128_WPE 1
 #endif
@@ -337,12 +340,15 @@ struct DkvGeom {
   static constexpr int NQB = QT / 32;       // 32-query blocks per step
   static constexpr int QBLK = FA_DKDV_QBLK < NQB ? FA_DKDV_QBLK : NQB;  // blocks handled together
   static_assert(NQB % QBLK == 0, "the step splits into whole groups of blocks");
-  static constexpr int WPE = D == 64 ? FA_DKDV64_WPE : FA_DKDV128_WPE;  // waves per SIMD the registers allow
+  // waves per SIMD the registers allow
+  static constexpr int wpe(bool drop) {
+    return D == 64 ? (drop ? FA_DKDV64_DROP_WPE : FA_DKDV64_WPE) : FA_DKDV128_WPE;
+  }
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(DkvGeom<D>::WPE, DkvGeom<D>::WPE)))
+                          amdgpu_waves_per_eu(DkvGeom<D>::wpe(DROP), DkvGeom<D>::wpe(DROP))))
 void bwd_dkdv_kernel(BwdParams p) {
   using G = DkvGeom<D>;
   using V8 = typename Vec8<T>::type;
