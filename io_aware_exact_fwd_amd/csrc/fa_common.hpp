@@ -267,6 +267,13 @@ __device__ __forceinline__ int xcd_remap(int linear, int total) {
 // IEEE maximum (NaN-propagating): v_maximum3_f32 on gfx950, no input
 // canonicalisation as fmaxf needs.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// maximum of the 16 values of an accumulator block: eight 3-input maxima, depth 3
+__device__ __forceinline__ float max16(const f32x16& x) {
+  float m5[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) m5[i] = vmax(vmax(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
+  return vmax(vmax(vmax(m5[0], m5[1]), m5[2]), vmax(vmax(m5[3], m5[4]), x[15]));
+}
 
 __device__ __forceinline__ float wave_max_pair(float v) {
   // lanes l and l ^ 32 hold the two halves of one query's row

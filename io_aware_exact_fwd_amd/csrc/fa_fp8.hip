@@ -383,12 +383,7 @@ void fp8_fwd_kernel(Fp8FwdParams p) {
       }
       // online softmax over the whole tile, then one P V product per
       // 32-column block of O
-      float m4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m4[i] = vmax(vmax(s[0][i], s[0][i + 4]), vmax(s[1][i], s[1][i + 4]));
-#pragma unroll
-      for (int r = 8; r < 16; ++r) m4[r & 3] = vmax(m4[r & 3], vmax(s[0][r], s[1][r]));
-      const float mx = vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3])) * p.c;
+      const float mx = vmax(max16(s[0]), max16(s[1])) * p.c;
       if (__builtin_amdgcn_ballot_w64(mx > m_ref + kFp8Tau) != 0) {
         FA_KEEP_BRANCH();
         const float m_new = vmax(m_ref, pair_max(mx));

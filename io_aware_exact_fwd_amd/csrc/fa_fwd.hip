@@ -260,13 +260,7 @@ void fwd_kernel(FwdParams p) {
         bool move = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          // 16 values in eight 3-input maxima, depth 3
-          const f32x16& x = s[qb][j];
-          float m5[5];
-#pragma unroll
-          for (int i = 0; i < 5; ++i) m5[i] = vmax(vmax(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
-          const float mx = vmax(vmax(vmax(m5[0], m5[1]), m5[2]), vmax(vmax(m5[3], m5[4]), x[15]));
-          mxs[qb] = mx * p.c;
+          mxs[qb] = max16(s[qb][j]) * p.c;
           move |= mxs[qb] > m_ref[qb] + kRescaleTau;
         }
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
