@@ -136,12 +136,13 @@ void fwd_kernel(FwdParams p) {
           V8, buf_load16(bq, (uint32_t)((qw0 + qb * 32 + l32) * D + t * 16 + g * 8) * sizeof(T)));
 
   f32x16 o[QB][G::NDB];
-  float m_ref[QB], ref[QB], l_run[QB];
+  float m_ref[QB], ref[QB], l_run[QB], thr[QB];  // thr = m_ref + kRescaleTau
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
     for (int i = 0; i < G::NDB; ++i) o[qb][i] = f32x16{0};
     m_ref[qb] = kNegInf;
+    thr[qb] = kNegInf;
     ref[qb] = 0.f;
     l_run[qb] = 0.f;
   }
@@ -261,7 +262,7 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           mxs[qb] = max16(s[qb][j]) * p.c;
-          move |= mxs[qb] > m_ref[qb] + kRescaleTau;
+          move |= mxs[qb] > thr[qb];
         }
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
           FA_KEEP_BRANCH();
@@ -274,6 +275,7 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int i = 0; i < G::NDB; ++i) o[qb][i] *= alpha;
             m_ref[qb] = m_new;
+            thr[qb] = m_new + kRescaleTau;
             ref[qb] = r_new;
           }
         }
@@ -284,21 +286,21 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             u32x4 w;
-            float lp = 0.f;
+            float lp = 0.f;  // bf16: this 16-key step's fp32 sum
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
               const float e0 = fast_exp2(__builtin_fmaf(s[qb][j][r0 + 2 * h], p.c, -ref[qb]));
               const float e1 = fast_exp2(__builtin_fmaf(s[qb][j][r0 + 2 * h + 1], p.c, -ref[qb]));
               w[h] = pack2<T>(e0, e1);
               if constexpr (__is_same(T, _Float16)) {
-                lp = add_pair<T>(w[h], lp);  // fp16: the rounded weights P V uses
+                l_run[qb] = add_pair<T>(w[h], l_run[qb]);  // fp16: the rounded weights P V uses
               } else {
                 lp += e0 + e1;  // bf16 rounding is too coarse for the LSE: fp32 sum
               }
               // dropout zeroes weights after the row sum: LSE normalises P itself
               if constexpr (DROP) w[h] &= keep_pair_mask(kw[qb][th * 2 + (h >> 1)], h & 1, bias);
             }
-            l_run[qb] += lp;
+            if constexpr (!__is_same(T, _Float16)) l_run[qb] += lp;
             bp[qb] = __builtin_bit_cast(V8, w);
           }
 #pragma unroll
