@@ -12,12 +12,16 @@
 // Two kernels, so that every output is reduced inside one workgroup and
 // written once (no atomics, no float32 dQ accumulator in memory, bitwise
 // repeatable):
-//   bwd_dq_kernel    query-outer (128 query rows per workgroup, 64-key steps):
-//                    computes D for its rows first, then S^T, dP^T, dS^T and
-//                    dQ^T += K^T dS^T.  It writes D for the second kernel.
+//   bwd_dq_kernel    query-outer (128 query rows per workgroup, 64-key steps,
+//                    each run as two 32-key halves): computes D for its rows
+//                    first, then per half S^T, dP^T, dS^T and dQ^T += K^T dS^T.
+//                    It writes D for the second kernel.
 //   bwd_dkdv_kernel  key-outer (128 keys per workgroup, 4 waves x 32 keys;
-//                    64-query steps): S, dP, dS with one key per lane, then
-//                    dV += P^T dO and dK += dS^T Q.
+//                    64-query steps, each run as two 32-query blocks): per
+//                    block S, dP, dS with one key per lane, then dV += P^T dO
+//                    and dK += dS^T Q.  In fp16 at head dim 64 the scale is
+//                    folded into K and -LSE, -D into the accumulators (see the
+//                    kernel).
 // The price is computing S and dP in both kernels: 14 d multiply-add FLOPs
 // per visible pair instead of 10 d.
 #include <type_traits>
