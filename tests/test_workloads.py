@@ -69,3 +69,27 @@ def test_inputs_seeded_and_rounded():
     ref = torch.randn((1, 2, 16, 8), generator=g)
     assert torch.equal(q, ref.to(torch.bfloat16))
     assert not torch.equal(q, k)
+
+
+def test_bench_units_follow_window_and_grouped_heads():
+    """bench.py's per-kernel units: the window's pairs (not the full causal
+    triangle) and K/V tensors with H_kv heads; the headline is unchanged."""
+    import bench
+
+    lw, full = wl.WORKLOADS["long_window"], wl.WORKLOADS["long_wide"]
+    u_lw, u_full = bench.kernel_work(lw), bench.kernel_work(full)
+    pairs = wl.kept_pairs_per_head(lw.N, lw.causal, None, 128, lw.window) * lw.B * lw.H
+    assert u_lw["fwd"]["flops"] == 4.0 * lw.d * pairs
+    assert u_lw["fwd"]["flops"] < u_full["fwd"]["flops"] / 8  # W = 512 of N = 8192
+    assert u_lw["dkdv"]["bytes"] == u_full["dkdv"]["bytes"]     # bytes do not depend on W
+
+    g = wl.WORKLOADS["gqa_h64_kv8"]
+    x = g.B * g.H * g.N * g.d * g.elem_bytes
+    xkv = g.B * g.H_kv * g.N * g.d * g.elem_bytes
+    n4 = g.B * g.H * g.N * 4
+    u = bench.kernel_work(g)
+    assert u["fwd"]["bytes"] == 2 * x + 2 * xkv + n4
+    assert u["dkdv"]["bytes"] == 2 * x + 4 * xkv + 2 * n4
+
+    h = wl.WORKLOADS["gpt2_medium"]
+    assert bench.kernel_work(h)["fwd"]["bytes"] == 541_065_216  # Q, K, V, O and LSE once
