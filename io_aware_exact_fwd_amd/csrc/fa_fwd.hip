@@ -68,6 +68,17 @@ constexpr float kRescaleTau = 8.0f;
 // the copies of two scattered key tiles in flight (48 KiB per workgroup, so
 // three waves per SIMD); on the N = 65536 butterfly workload two stages at four
 // waves measured 7 % faster.
+// Head dim 128: keys per tile and waves per SIMD.  A 64-key tile pair of
+// stages takes 64 KiB of LDS (two workgroups per CU); 32-key tiles take
+// 32 KiB, so three fit, and the kernel fits the 168 VGPRs of three waves.
+// Measured on MI355X: equal on the N = 8192 causal shape, 4 % faster with a
+// 512-key window, 1.4 % faster with 64 query heads on 8 K/V heads.
+#ifndef FA_FWD128_KT
+#define FA_FWD128_KT 32
+#endif
+#ifndef FA_FWD128_WPE
+#define FA_FWD128_WPE 3
+#endif
 #ifndef FA_FWD64_DROP_WPE
 #define FA_FWD64_DROP_WPE 4  // dropout forward, head dim 64 (126 VGPRs; 10 % faster than 2)
 #endif
@@ -78,9 +89,10 @@ constexpr float kRescaleTau = 8.0f;
 #define FA_FWD64_MASKED_WPE 4
 #endif
 
-template <int D, int NW>
+template <int D, int NW, int KT_ = kKeyTile>
 struct FwdGeom {
-  static constexpr int KT = kKeyTile;           // keys per tile
+  static constexpr int KT = KT_;                // keys per tile (64, or 32)
+  static_assert(KT == 32 || KT == 64, "one or two 32-key halves per tile");
   static constexpr int KBYTES = KT * D * 2;    // K tile (read by rows), swizzled
   static constexpr int VBYTES = KT * D * 2;    // V tile (read by transpose), swizzled
   static constexpr int STAGE = KBYTES + VBYTES;
@@ -89,11 +101,12 @@ struct FwdGeom {
   static_assert(NW == 4, "the tile copies assume 4 waves");
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP, int NW, int QB, int WPE, int NST>
+template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP, int NW, int QB, int WPE, int NST,
+          int KT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(FwdParams p) {
-  using G = FwdGeom<D, NW>;
+  using G = FwdGeom<D, NW, KT>;
   using V8 = typename Vec8<T>::type;
   constexpr int BR = NW * QB * 32;  // query rows per workgroup
   constexpr int WQ = QB * 32;       // query rows per wave
@@ -313,7 +326,9 @@ void fwd_kernel(FwdParams p) {
       }
     };
     if (active) {
-      if constexpr (FA_FWD_HALVES) {
+      if constexpr (G::KT == 32) {
+        key_halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+      } else if constexpr (FA_FWD_HALVES) {
         key_halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
         key_halves(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
       } else {
@@ -355,15 +370,18 @@ void fwd_kernel(FwdParams p) {
   }
 }
 
-template <typename T, int D, bool MASKED, bool DROP, int NW, int QB, int WPE, int NST = 2>
+template <typename T, int D, bool MASKED, bool DROP, int NW, int QB, int WPE, int NST = 2,
+          int KT = kKeyTile>
 static hipError_t launch_fwd_t(FwdParams p, bool causal, hipStream_t s) {
   constexpr int BR = NW * QB * 32;
   p.nqt = (p.N + BR - 1) / BR;
   dim3 grid(p.nheads * p.nqt), block(NW * 64);
   if (causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, true, MASKED, DROP, NW, QB, WPE, NST>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<T, D, true, MASKED, DROP, NW, QB, WPE, NST, KT>), grid, block, 0,
+                       s, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, false, MASKED, DROP, NW, QB, WPE, NST>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<T, D, false, MASKED, DROP, NW, QB, WPE, NST, KT>), grid, block, 0,
+                       s, p);
   return hipGetLastError();
 }
 
@@ -387,8 +405,9 @@ static hipError_t launch_fwd_dtype(const FwdParams& p, int d, bool causal, bool 
           p, causal, s);
     return launch_fwd_t<T, 64, false, false, FA_FWD64_NW, FA_FWD64_QB, FA_FWD64_WPE>(p, causal, s);
   }
-  if (masked) return launch_fwd_t<T, 128, true, false, 4, 1, 2>(p, causal, s);
-  return launch_fwd_t<T, 128, false, false, 4, 1, 2>(p, causal, s);
+  if (masked)
+    return launch_fwd_t<T, 128, true, false, 4, 1, FA_FWD128_WPE, 2, FA_FWD128_KT>(p, causal, s);
+  return launch_fwd_t<T, 128, false, false, 4, 1, FA_FWD128_WPE, 2, FA_FWD128_KT>(p, causal, s);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, bool causal, bool masked,
