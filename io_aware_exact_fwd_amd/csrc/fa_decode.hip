@@ -26,10 +26,22 @@ namespace {
 
 constexpr float kDecTau = 8.0f;  // reference move threshold (base 2), as in the forward
 
+#ifndef FA_DEC_NST
+#define FA_DEC_NST 4  // LDS stages of the split kernel: one computed, the others in flight
+#endif
+#ifndef FA_DEC_WPE64
+#define FA_DEC_WPE64 2
+#endif
+#ifndef FA_DEC_WPE128
+#define FA_DEC_WPE128 2
+#endif
+
 template <int D>
 struct DecGeom {
   static constexpr int KT = kDecKeys;          // keys per tile
-  static constexpr int NST = 4;                // LDS stages: one computed, three in flight
+  static constexpr int NST = FA_DEC_NST;       // LDS stages: one computed, NST - 1 in flight
+  static_assert(NST >= 2, "at least one tile in flight");
+  static constexpr int WPE = D == 64 ? FA_DEC_WPE64 : FA_DEC_WPE128;  // waves per SIMD
   static constexpr int KBYTES = KT * D * 2;    // K tile, swizzled
   static constexpr int VBYTES = KT * D * 2;    // V tile, swizzled
   static constexpr int STAGE = KBYTES + VBYTES;
@@ -39,7 +51,8 @@ struct DecGeom {
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(DecGeom<D>::WPE, DecGeom<D>::WPE)))
 void decode_split_kernel(DecParams p) {
   using G = DecGeom<D>;
   using V8 = typename Vec8<T>::type;
@@ -110,9 +123,9 @@ void decode_split_kernel(DecParams p) {
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
   for (int it = 0; it < ntl; ++it) {
-    // tile it has landed (the two younger tiles may still be in flight); after
-    // the barrier every wave's copies are visible and no wave still reads the
-    // stage of tile it - 1, which receives tile it + 3
+    // tile it has landed (the NST - 2 younger tiles may still be in flight);
+    // after the barrier every wave's copies are visible and no wave still
+    // reads the stage of tile it - 1, which receives tile it + NST - 1
     __builtin_amdgcn_s_waitcnt(vmcnt_at_most((G::NST - 2) * G::COPIES));
     __syncthreads();
     issue(it + G::NST - 1);
