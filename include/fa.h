@@ -58,8 +58,9 @@
  * (b, h).  Every tensor pointer is a DEVICE pointer (hipMalloc'd or equivalent)
  * unless stated otherwise; device pointers must be 16-byte aligned.
  *
- * Streams.  `stream` is a hipStream_t passed as void* (NULL = default stream).
- * All work is enqueued asynchronously on it; no call synchronises the host.
+ * Streams.  `stream` is the HIP stream to enqueue on (NULL = the default
+ * stream).  All work is enqueued asynchronously on it; no call synchronises
+ * the host.
  *
  * Ownership.  The caller allocates and owns every buffer, including the
  * workspace, and keeps them alive until the enqueued work has completed.  The
@@ -72,6 +73,7 @@
 #ifndef FA_MI355X_H
 #define FA_MI355X_H
 
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -94,7 +96,9 @@ enum fa_status {
   FA_ERR_UNSUPPORTED = -2,  /* d not in {64, 128}; unknown dtype; a block mask
                                whose block is not a positive multiple of 128 or
                                does not divide N                               */
-  FA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required     */
+  FA_ERR_WORKSPACE = -3,    /* workspace missing, smaller than required, or not
+                               16-byte aligned (every entry point that takes
+                               one)                                            */
   FA_ERR_LAUNCH = -4        /* the HIP runtime rejected a kernel launch       */
 };
 
@@ -123,7 +127,7 @@ size_t fa_workspace_size(const fa_problem* p, int pass);
  * float32, natural log).  workspace: device buffer of at least
  * fa_workspace_size(p, 0) bytes (may be NULL when that is 0). */
 int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, void* o,
-           float* lse, void* workspace, size_t ws_bytes, void* stream);
+           float* lse, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Backward of f = <O, dO>.  Reads q, k, v, o, dout and lse, which must be the
  * O and LSE that fa_fwd produced for the same q, k, v and problem (with
@@ -133,7 +137,7 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
  * and, with a block mask, the compiled block lists. */
 int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
-           size_t ws_bytes, void* stream);
+           size_t ws_bytes, hipStream_t stream);
 
 /* The two stages of fa_bwd, for callers that schedule or time them apart.
  * fa_bwd_dq: computes D_i = dO_i . O_i into the workspace (and, with a block
@@ -144,10 +148,10 @@ int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, con
  * Arguments, layouts and errors are those of fa_bwd. */
 int fa_bwd_dq(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
               const void* dout, const float* lse, void* dq, void* workspace, size_t ws_bytes,
-              void* stream);
+              hipStream_t stream);
 int fa_bwd_dkdv(const fa_problem* p, const void* q, const void* k, const void* v,
                 const void* dout, const float* lse, void* dk, void* dv, void* workspace,
-                size_t ws_bytes, void* stream);
+                size_t ws_bytes, hipStream_t stream);
 
 /* Block-mask compilation (the step both passes run first when a block mask is
  * given).  mask: device uint8 [nb][nb]; writes, all int32 device arrays:
@@ -157,7 +161,7 @@ int fa_bwd_dkdv(const fa_problem* p, const void* q, const void* k, const void* v
  *     it, row_idx[col_ptr[c] .. col_ptr[c+1]) in increasing order.
  * col_idx and row_idx must hold nb*nb entries (the worst case). */
 int fa_mask_compile(const uint8_t* mask, int32_t nb, int32_t* row_ptr, int32_t* col_idx,
-                    int32_t* col_ptr, int32_t* row_idx, void* stream);
+                    int32_t* col_ptr, int32_t* row_idx, hipStream_t stream);
 
 /* Decode-shaped forward (a few queries against many keys, with grouped K/V
  * heads).  q and o are (B, H, n_q, d) in the
@@ -178,7 +182,7 @@ int fa_mask_compile(const uint8_t* mask, int32_t nb, int32_t* row_ptr, int32_t* 
  * when that is 0).  The split count depends only on the problem. */
 size_t fa_decode_workspace_size(const fa_problem* p, int32_t n_q);
 int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k, const void* v,
-                  void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
+                  void* o, float* lse, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* FP8 forward: block quantisation with a random Hadamard-style rotation
  * ("Atencao Eficiente em Escala", section 10 on FlashAttention-3: Q, K, V are
@@ -216,9 +220,9 @@ int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k
  * problem the FP8 path does not take. */
 size_t fa_fp8_workspace_size(const fa_problem* p);
 int fa_fp8_quantize(const fa_problem* p, const float* signs, const void* q, const void* k,
-                    const void* v, void* workspace, size_t ws_bytes, void* stream);
+                    const void* v, void* workspace, size_t ws_bytes, hipStream_t stream);
 int fa_fwd_fp8(const fa_problem* p, const float* signs, const void* workspace, size_t ws_bytes,
-               void* o, float* lse, void* stream);
+               void* o, float* lse, hipStream_t stream);
 
 /* Static string for a status code. */
 const char* fa_status_string(int status);

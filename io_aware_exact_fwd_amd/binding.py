@@ -164,13 +164,23 @@ def _check_qkv(q, k, v):
         raise ValueError("the K/V head count must divide the query head count")
 
 
-def _mask_arg(block_mask, ref):
+def _mask_arg(block_mask, ref, mask_block):
+    """The block mask as a contiguous uint8 tensor on ref's device.  The C ABI
+    receives only a pointer, so its shape is checked here: 2-D, square, with
+    side N / mask_block (N = ref.shape[2])."""
     import torch
 
     if block_mask is None:
         return None
     if not isinstance(block_mask, torch.Tensor):
         block_mask = torch.as_tensor(block_mask)
+    N = ref.shape[2]
+    if mask_block <= 0 or N % mask_block:
+        raise ValueError(f"mask_block {mask_block} must be positive and divide N = {N}")
+    nb = N // mask_block
+    if block_mask.dim() != 2 or tuple(block_mask.shape) != (nb, nb):
+        raise ValueError(f"block mask must be ({nb}, {nb}) for N = {N} and mask_block = "
+                         f"{mask_block}, got {tuple(block_mask.shape)}")
     return block_mask.to(device=ref.device, dtype=torch.uint8).contiguous()
 
 
@@ -187,7 +197,7 @@ def fa_fwd(q, k, v, causal=False, scale=None, block_mask=None, mask_block=128, o
     import torch
 
     _check_qkv(q, k, v)
-    bm = _mask_arg(block_mask, q)
+    bm = _mask_arg(block_mask, q, mask_block)
     p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset)
     B, H, N, d = q.shape
     o = torch.empty_like(q) if out is None else out
@@ -326,7 +336,7 @@ def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, block_mask=None, mas
     _check_tensors(q, o, dout)
     if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
         raise ValueError("lse must be a contiguous float32 GPU tensor")
-    bm = _mask_arg(block_mask, q)
+    bm = _mask_arg(block_mask, q, mask_block)
     p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_n = fa_workspace_size(p, 1)
@@ -344,7 +354,7 @@ def bwd_workspace(q, causal=False, scale=None, block_mask=None, mask_block=128, 
     """(problem, workspace tensor, workspace bytes, mask) for the two backward stages."""
     import torch
 
-    bm = _mask_arg(block_mask, q)
+    bm = _mask_arg(block_mask, q, mask_block)
     p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset)
     ws_n = fa_workspace_size(p, 1)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)

@@ -113,15 +113,15 @@ size_t fa_workspace_size(const fa_problem* p, int pass) {
 }
 
 int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, void* o, float* lse,
-           void* workspace, size_t ws_bytes, void* stream) {
+           void* workspace, size_t ws_bytes, hipStream_t stream) {
   int st = check_problem(p);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o || !lse) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
     return FA_ERR_ARG;
   const size_t need = fa_workspace_size(p, 0);
-  if (need > 0 && (!workspace || ws_bytes < need)) return FA_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
+  hipStream_t s = stream;
   const float c = p->scale * fa::kLog2e;
   const int nheads = p->B * p->H;
 
@@ -226,7 +226,7 @@ size_t fa_decode_workspace_size(const fa_problem* p, int32_t n_q) {
 }
 
 int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k, const void* v,
-                  void* o, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+                  void* o, float* lse, void* workspace, size_t ws_bytes, hipStream_t stream) {
   int st = check_decode(p, n_q);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o || !lse) return FA_ERR_ARG;
@@ -256,7 +256,7 @@ int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k
   d.ntiles = g.ntiles;
   d.window = p->window;
   d.c = p->scale * fa::kLog2e;
-  return fa::launch_decode(d, p->dtype, p->d, p->causal != 0, (hipStream_t)stream) == hipSuccess
+  return fa::launch_decode(d, p->dtype, p->d, p->causal != 0, stream) == hipSuccess
              ? FA_OK
              : FA_ERR_LAUNCH;
 }
@@ -303,7 +303,7 @@ size_t fa_fp8_workspace_size(const fa_problem* p) {
 }
 
 int fa_fp8_quantize(const fa_problem* p, const float* signs, const void* q, const void* k, const void* v,
-                    void* workspace, size_t ws_bytes, void* stream) {
+                    void* workspace, size_t ws_bytes, hipStream_t stream) {
   int st = check_fp8(p, signs);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !aligned16(q) || !aligned16(k) || !aligned16(v)) return FA_ERR_ARG;
@@ -328,13 +328,13 @@ int fa_fp8_quantize(const fa_problem* p, const float* signs, const void* q, cons
   qp.N64 = (int)l.n64;
   const int64_t wgs = (int64_t)qp.nq_wg + 2 * (int64_t)qp.nk_wg;
   if (wgs > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
-  return fa::launch_fp8_quantize(qp, p->dtype, p->d, (int)wgs, (hipStream_t)stream) == hipSuccess
+  return fa::launch_fp8_quantize(qp, p->dtype, p->d, (int)wgs, stream) == hipSuccess
              ? FA_OK
              : FA_ERR_LAUNCH;
 }
 
 int fa_fwd_fp8(const fa_problem* p, const float* signs, const void* workspace, size_t ws_bytes, void* o,
-               float* lse, void* stream) {
+               float* lse, hipStream_t stream) {
   int st = check_fp8(p, signs);
   if (st != FA_OK) return st;
   if (!o || !lse || !aligned16(o) || ((uintptr_t)lse & 3u)) return FA_ERR_ARG;
@@ -358,7 +358,7 @@ int fa_fwd_fp8(const fa_problem* p, const float* signs, const void* workspace, s
   f.window = p->window;
   f.group = group_of(p);
   f.c = p->scale * fa::kLog2e;
-  return fa::launch_fp8_fwd(f, p->dtype, p->d, p->causal != 0, (hipStream_t)stream) == hipSuccess
+  return fa::launch_fp8_fwd(f, p->dtype, p->d, p->causal != 0, stream) == hipSuccess
              ? FA_OK
              : FA_ERR_LAUNCH;
 }
@@ -384,8 +384,7 @@ int bwd_setup(const fa_problem* p, const void* q, const void* k, const void* v, 
     if (!aligned16(ptr)) return FA_ERR_ARG;
   if ((uintptr_t)lse & 3u) return FA_ERR_ARG;
   const size_t need = fa_workspace_size(p, 1);
-  if (!workspace || ws_bytes < need) return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FA_ERR_ARG;
+  if (!workspace || ws_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
   b->q = q;
   b->k = k;
   b->v = v;
@@ -468,40 +467,40 @@ extern "C" {
 
 int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
-           size_t ws_bytes, void* stream) {
+           size_t ws_bytes, hipStream_t stream) {
   fa::BwdParams b;
   int st = bwd_setup(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, true, true, &b);
   if (st != FA_OK) return st;
-  st = run_dq(p, b, (hipStream_t)stream);
+  st = run_dq(p, b, stream);
   if (st != FA_OK) return st;
-  return run_dkdv(p, b, (hipStream_t)stream);
+  return run_dkdv(p, b, stream);
 }
 
 int fa_bwd_dq(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
               const void* dout, const float* lse, void* dq, void* workspace, size_t ws_bytes,
-              void* stream) {
+              hipStream_t stream) {
   fa::BwdParams b;
   int st = bwd_setup(p, q, k, v, o, dout, lse, dq, nullptr, nullptr, workspace, ws_bytes, true,
                      false, &b);
   if (st != FA_OK) return st;
-  return run_dq(p, b, (hipStream_t)stream);
+  return run_dq(p, b, stream);
 }
 
 int fa_bwd_dkdv(const fa_problem* p, const void* q, const void* k, const void* v,
                 const void* dout, const float* lse, void* dk, void* dv, void* workspace,
-                size_t ws_bytes, void* stream) {
+                size_t ws_bytes, hipStream_t stream) {
   fa::BwdParams b;
   int st = bwd_setup(p, q, k, v, nullptr, dout, lse, nullptr, dk, dv, workspace, ws_bytes, false,
                      true, &b);
   if (st != FA_OK) return st;
-  return run_dkdv(p, b, (hipStream_t)stream);
+  return run_dkdv(p, b, stream);
 }
 
 int fa_mask_compile(const uint8_t* mask, int32_t nb, int32_t* row_ptr, int32_t* col_idx,
-                    int32_t* col_ptr, int32_t* row_idx, void* stream) {
+                    int32_t* col_ptr, int32_t* row_idx, hipStream_t stream) {
   if (!mask || nb <= 0 || !row_ptr || !col_idx || !col_ptr || !row_idx) return FA_ERR_ARG;
   return fa::launch_mask_compile(mask, nb, row_ptr, col_idx, col_ptr, row_idx,
-                                 (hipStream_t)stream) == hipSuccess
+                                 stream) == hipSuccess
              ? FA_OK
              : FA_ERR_LAUNCH;
 }

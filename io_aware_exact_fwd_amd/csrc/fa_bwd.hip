@@ -19,9 +19,8 @@
 //   bwd_dkdv_kernel  key-outer (128 keys per workgroup, 4 waves x 32 keys;
 //                    64-query steps, each run as two 32-query blocks): per
 //                    block S, dP, dS with one key per lane, then dV += P^T dO
-//                    and dK += dS^T Q.  In fp16 at head dim 64 the scale is
-//                    folded into K and -LSE, -D into the accumulators (see the
-//                    kernel).
+//                    and dK += dS^T Q.  At head dim 64 the dP accumulators
+//                    start at -D (see the kernel).
 // The price is computing S and dP in both kernels: 14 d multiply-add FLOPs
 // per visible pair instead of 10 d.
 #include <type_traits>
@@ -62,9 +61,6 @@ namespace fa {
 #endif
 #ifndef FA_DKDV_QT
 #define FA_DKDV_QT 64
-#endif
-#ifndef FA_DKDV_FOLD
-#define FA_DKDV_FOLD 1  // 1: fp16, d = 64: scale in K, -LSE and -D in the accumulators
 #endif
 #ifndef FA_DKDV_QBLK
 #define FA_DKDV_QBLK 1  // 32-query blocks of a step handled together (scores to products)
@@ -360,10 +356,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
 void bwd_dkdv_kernel(BwdParams p) {
   using G = DkvGeom<D>;
   using V8 = typename Vec8<T>::type;
-  // the folded form (below) for fp16 at head dim 64: measured 6.5 % faster
-  // there, while at head dim 128 in bf16 it was 5 % slower and bf16's coarser
-  // rounding of K c shows in the gradients
-  constexpr bool kFold = FA_DKDV_FOLD && D == 64 && __is_same(T, _Float16);
+  // At head dim 64 without dropout the dP accumulators start at -D (an
+  // exact float32 value), so dS = P o dp is one instruction.  The scale is
+  // not folded into K: K c rounded to the input type moves every score by up
+  // to |S c| 2^-11, which for large logits (|S c| ~ 100) breaks the
+  // gradients' tolerance.
+  constexpr bool kFoldD = D == 64 && !DROP;
   __shared__ __attribute__((aligned(16))) char smem[G::NST * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
 
   const int tid = threadIdx.x;
@@ -405,18 +403,6 @@ void bwd_dkdv_kernel(BwdParams p) {
   // it still thinks pending -- and, counts being in issue order, for the
   // prefetch copies issued after them.
   wait_all_memory();
-  // Folded form: K c (c = scale log2 e) rounded to the input type makes the
-  // score product give S c directly; the accumulators start at -LSE log2 e
-  // (scores) and -D (dP, without dropout), so P = 2^s and dS = P o dp take
-  // one instruction each.  The rounding of K c changes P by about one unit in
-  // the input type's last place, well inside the gradients' tolerance.
-  if constexpr (kFold) {
-#pragma unroll
-    for (int t = 0; t < G::NKS; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[t][e] = (T)((float)kf[t][e] * p.c);
-  }
-
   f32x16 dka[G::NDB], dva[G::NDB];
 #pragma unroll
   for (int i = 0; i < G::NDB; ++i) {
@@ -453,8 +439,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   // Wait until this wave's copies of the next step have landed (those of the
   // step after it may stay in flight), then wave 0 converts that step's rows
   // in place: LSE -> LSE log2(e) (+inf for a row with no visible key, so P =
-  // 0), D -> D / mult under dropout (see the dS step).  The barrier that
-  // follows publishes the stage.
+  // 0), D -> D / mult under dropout (see the dS step), D -> -D where the dP
+  // accumulators start from it.  The barrier that follows publishes the stage.
   auto land_next = [&](bool younger_in_flight, char* st) {
     if (G::NST > 2 && younger_in_flight) {
       if (wave == 0)
@@ -470,14 +456,9 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int i = lane; i < G::QT; i += 64) {
         const float l = ls[i];
-        if constexpr (kFold) {
-          ls[i] = l != kNegInf ? -l * kLog2e : kNegInf;  // score accumulators start here
-          if constexpr (DROP) ds[i] = ds[i] / p.drop.mult;
-          else ds[i] = -ds[i];                            // dP accumulators start here
-        } else {
-          ls[i] = l != kNegInf ? l * kLog2e : __builtin_huge_valf();
-          if constexpr (DROP) ds[i] = ds[i] / p.drop.mult;
-        }
+        ls[i] = l != kNegInf ? l * kLog2e : __builtin_huge_valf();
+        if constexpr (DROP) ds[i] = ds[i] / p.drop.mult;
+        if constexpr (kFoldD) ds[i] = -ds[i];  // dP accumulators start here
       }
     }
   };
@@ -517,26 +498,16 @@ void bwd_dkdv_kernel(BwdParams p) {
       f32x16 s[NQ], dp[NQ];
 #pragma unroll
       for (int i = 0; i < NQ; ++i) {
-        if constexpr (kFold) {
+        s[i] = f32x16{0};
+        if constexpr (kFoldD) {
           // register r of a block holds query row 8 (r / 4) + 4 g + r % 4
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            const f32x4 l4 = *(const f32x4*)(lsm + (QB0 + i) * 32 + rr * 8 + g * 4);
+            const f32x4 d4 = *(const f32x4*)(lsm + G::LBYTES / 4 + (QB0 + i) * 32 + rr * 8 + g * 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[i][rr * 4 + e] = l4[e];
-          }
-          if constexpr (!DROP) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const f32x4 d4 = *(const f32x4*)(lsm + G::LBYTES / 4 + (QB0 + i) * 32 + rr * 8 + g * 4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) dp[i][rr * 4 + e] = d4[e];
-            }
-          } else {
-            dp[i] = f32x16{0};
+            for (int e = 0; e < 4; ++e) dp[i][rr * 4 + e] = d4[e];
           }
         } else {
-          s[i] = f32x16{0};
           dp[i] = f32x16{0};
         }
 #pragma unroll
@@ -584,22 +555,21 @@ void bwd_dkdv_kernel(BwdParams p) {
                                     smem + G::NST * G::STAGE + wave * kDropLdsPerWave, lane);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          f32x4 l4 = {0.f, 0.f, 0.f, 0.f}, d4 = {0.f, 0.f, 0.f, 0.f};
-          if (!kFold) l4 = *(const f32x4*)(lsm + qb * 32 + rr * 8 + g * 4);
-          if (!kFold || DROP) d4 = *(const f32x4*)(lsm + G::LBYTES / 4 + qb * 32 + rr * 8 + g * 4);
+          const f32x4 l4 = *(const f32x4*)(lsm + qb * 32 + rr * 8 + g * 4);
+          f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+          if (!kFoldD) d4 = *(const f32x4*)(lsm + G::LBYTES / 4 + qb * 32 + rr * 8 + g * 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = rr * 4 + e;
-            const float pr = kFold ? fast_exp2(s[i][r])
-                                          : fast_exp2(__builtin_fmaf(s[i][r], p.c, -l4[e]));
+            const float pr = fast_exp2(__builtin_fmaf(s[i][r], p.c, -l4[e]));
             if constexpr (DROP) {
               const bool keep = keep_byte(kw[rr], e, p.drop.t8);
               s[i][r] = keep ? pr : 0.f;                             // Z01 o P
               dp[i][r] = pr * ((keep ? dp[i][r] : 0.f) - d4[e]);  // dS / mult
             } else {
               s[i][r] = pr;  // P
-              // dS (scale applied to dK at the end); folded: dp already holds dP - D
-              dp[i][r] = kFold ? pr * dp[i][r] : pr * (dp[i][r] - d4[e]);
+              // dS (scale applied to dK at the end); dp may already hold dP - D
+              dp[i][r] = kFoldD ? pr * dp[i][r] : pr * (dp[i][r] - d4[e]);
             }
           }
         }

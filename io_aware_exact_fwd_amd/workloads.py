@@ -49,6 +49,12 @@ the N(0, 1) draw of ``make_inputs`` with a few head-dim coordinates of Q and
 K multiplied by large factors, the case the rotation exists for); the
 rotation's signs are drawn by ``make_signs``.
 
+Large logits (parity cases of the online softmax's rescaling): inputs with a
+few outlier coordinates (``make_outlier_inputs``), and inputs whose logits
+rise along the key sequence (``make_rising_inputs``: every query and key gets
+a common component whose size grows with the key's position, so each row's
+running maximum keeps growing by several units in base 2).
+
   long_wide_fp8 long_wide's shape (B=2 H=16 N=8192 d=128 causal) through the
                 FP8 forward, bf16 in and out
 """
@@ -66,6 +72,7 @@ __all__ = [
     "make_inputs",
     "make_decode_inputs",
     "make_outlier_inputs",
+    "make_rising_inputs",
     "make_signs",
     "butterfly_block_mask",
     "kept_pairs_per_head",
@@ -184,6 +191,34 @@ def make_outlier_inputs(B, H, N, d, dtype="bf16", seed=None, hkv=None,
             for c, f in outliers:
                 x[..., c] *= f
         out.append(x.to(_torch_dtype(dtype)).contiguous())
+    return tuple(out)
+
+
+def make_rising_inputs(B, H, N, d, dtype="f16", seed=None, hkv=None, scale=None, step=64,
+                       rise2=6.0, lift=4.0, nq=None):
+    """``make_inputs`` (or, with ``nq``, ``make_decode_inputs``) with logits
+    that rise along the key sequence: coordinate 0 of every query gets
+    + ``lift`` and coordinate 0 of key j gets + inc * (j // step), with inc
+    chosen so that the scaled score of a query grows by about ``rise2`` in
+    base 2 (scale * log2(e) * lift * inc = rise2) from one block of ``step``
+    keys to the next.  Each row's running maximum then keeps growing by more
+    than a few units as the keys go by, which is the case the online
+    softmax's rescaling step exists for.  Added before the rounding to
+    ``dtype``; dO (if drawn) is unchanged.  scale defaults to 1/sqrt(d)."""
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    inc = rise2 / (scale * math.log2(math.e) * lift)
+    if nq is None:
+        q, k, v, do = make_inputs(B, H, N, d, "f32", seed, hkv)
+    else:
+        q, k, v = make_decode_inputs(B, H, N, d, nq, "f32", seed, hkv)
+        do = None
+    import torch
+
+    q[..., 0] += lift
+    k[..., 0] += inc * (torch.arange(N, dtype=torch.float32) // step)
+    out = [x.to(_torch_dtype(dtype)).contiguous() for x in (q, k, v)]
+    if do is not None:
+        out.append(do.to(_torch_dtype(dtype)).contiguous())
     return tuple(out)
 
 

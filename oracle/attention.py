@@ -251,12 +251,20 @@ def _backward_head(q, k, v, do, spec, head):
 
 
 def _as_bhnd(x):
+    """View as (B, H, N, d); the float64 upcast happens per head (``_f64``)."""
     x = np.asarray(x)
     if x.ndim == 2:
         x = x[None, None]
     if x.ndim != 4:
         raise ValueError("expected (B, H, N, d) or (N, d)")
-    return x.astype(np.float64)
+    if not np.issubdtype(x.dtype, np.floating):
+        raise ValueError("expected a float array")
+    return x
+
+
+def _f64(x):
+    """Exact upcast of one head's (N, d) slice to float64."""
+    return np.asarray(x, dtype=np.float64)
 
 
 def _select(x, heads):
@@ -294,7 +302,8 @@ def attention_forward(q, k, v, scale, causal=False, block_mask=None, mask_block=
                  row_chunk, q_offset)
     outs, lses = [], []
     for b, h in _select(q, heads):
-        o, lse = _forward_head(q[b, h], k[b, h // g], v[b, h // g], spec, b * q.shape[1] + h)
+        o, lse = _forward_head(_f64(q[b, h]), _f64(k[b, h // g]), _f64(v[b, h // g]), spec,
+                               b * q.shape[1] + h)
         outs.append(o)
         lses.append(lse)
     o = np.stack(outs)
@@ -322,8 +331,8 @@ def attention_backward(q, k, v, do, scale, causal=False, block_mask=None, mask_b
     spec = _Spec(scale, causal, block_mask, mask_block, window, dropout_p, seed, offset,
                  row_chunk)
     sel = _select(q, heads)
-    res = [_backward_head(q[b, h], k[b, h // g], v[b, h // g], do[b, h], spec,
-                          b * q.shape[1] + h) for b, h in sel]
+    res = [_backward_head(_f64(q[b, h]), _f64(k[b, h // g]), _f64(v[b, h // g]),
+                          _f64(do[b, h]), spec, b * q.shape[1] + h) for b, h in sel]
     dq, dk, dv, dd, ddot = (np.stack([r[i] for r in res]) for i in range(5))
     if heads is None:
         shp = (q.shape[0], q.shape[1])

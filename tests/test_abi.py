@@ -137,6 +137,43 @@ def test_workspace_checked_before_launch():
                     None) == B.FA_ERR_WORKSPACE
 
 
+def test_misaligned_workspace_same_status_everywhere():
+    """A workspace that is not 16-byte aligned is FA_ERR_WORKSPACE from every
+    entry point that takes one (the lists it holds are read with loads that
+    ignore the low address bits)."""
+    L = B.lib()
+    pm = _problem(N=512, block_mask=FAKE, mask_block=128)
+    assert _fwd(pm, ws=FAKE + 4, ws_n=1 << 20) == B.FA_ERR_WORKSPACE
+    for p in (_problem(), pm):
+        n = B.fa_workspace_size(p, 1)
+        args = [FAKE] * 9
+        assert L.fa_bwd(ctypes.byref(p), *args, FAKE + 8, n + 64, None) == B.FA_ERR_WORKSPACE
+        assert L.fa_bwd_dq(ctypes.byref(p), *args[:7], FAKE + 8, n + 64,
+                           None) == B.FA_ERR_WORKSPACE
+        assert L.fa_bwd_dkdv(ctypes.byref(p), *args[:7], FAKE + 8, n + 64,
+                             None) == B.FA_ERR_WORKSPACE
+    pd = _problem(N=4096, H=8, H_kv=2)
+    need = B.fa_decode_workspace_size(pd, 1)
+    assert L.fa_fwd_decode(ctypes.byref(pd), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, need + 64,
+                           None) == B.FA_ERR_WORKSPACE
+
+
+def test_binding_checks_block_mask_shape():
+    """The C ABI only sees a pointer to the mask; the binding rejects a mask
+    whose shape is not (N / mask_block, N / mask_block)."""
+    import numpy as np
+    import torch
+
+    q = torch.zeros((1, 1, 512, 64), dtype=torch.float16)
+    ok = B._mask_arg(np.ones((4, 4), np.uint8), q, 128)
+    assert ok.shape == (4, 4) and ok.dtype == torch.uint8
+    for bad, mb in ((np.ones((2, 2), np.uint8), 128), (np.ones((4, 2), np.uint8), 128),
+                    (np.ones(16, np.uint8), 128), (np.ones((4, 4), np.uint8), 256),
+                    (np.ones((4, 4), np.uint8), 0), (np.ones((3, 3), np.uint8), 200)):
+        with pytest.raises(ValueError):
+            B._mask_arg(bad, q, mb)
+
+
 def test_mask_compile_argument_checks():
     L = B.lib()
     assert L.fa_mask_compile(None, 4, FAKE, FAKE, FAKE, FAKE, None) == B.FA_ERR_ARG

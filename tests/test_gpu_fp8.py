@@ -43,7 +43,7 @@ import torch
 
 from io_aware_exact_fwd_amd import fa_fwd_fp8, fp8_quantize, fp8_workspace_views
 from io_aware_exact_fwd_amd.workloads import (WORKLOADS, make_inputs, make_outlier_inputs,
-                                              make_signs)
+                                              make_rising_inputs, make_signs)
 from oracle import attention_forward
 from oracle.attention import visibility
 from oracle.fp8 import (E4M3_MAX, block_dequantize, block_quantize, e4m3_decode, e4m3_encode,
@@ -76,7 +76,7 @@ TINY = {"tiny": 2.0 ** -120, "small": 2.0 ** -95}  # magnitudes near float32 und
 
 
 def _inputs(kind, B, H, hkv, N, d, dtype, qmul=1.0):
-    gen = make_outlier_inputs if kind == "outlier" else make_inputs
+    gen = {"outlier": make_outlier_inputs, "rising": make_rising_inputs}.get(kind, make_inputs)
     q, k, v, _ = gen(B, H, N, d, dtype, hkv=hkv)
     if qmul != 1.0:
         q = (q.float() * qmul).to(q.dtype)
@@ -153,6 +153,8 @@ CASES = [
     ("outlier", "bf16", 64, 1, 4, 4, 1500, True, 300, 1.0),   # causal window
     ("normal", "f16", 128, 1, 2, 2, 700, False, 100, 1.0),    # two-sided window
     ("normal", "bf16", 64, 1, 2, 2, 1024, True, 0, 6.0),      # peaked rows: the lazy reference moves
+    ("rising", "f16", 64, 1, 2, 2, 1000, True, 0, 1.0),       # the reference moves from a finite value
+    ("rising", "bf16", 128, 1, 2, 1, 1000, False, 0, 1.0),
     ("normal", "f16", 128, 2, 2, 1, 640, False, 0, 4.0),
     ("tiny", "bf16", 128, 1, 2, 2, 200, True, 0, 1.0),      # block exponents at the -127 floor
     ("small", "bf16", 64, 1, 2, 2, 200, False, 0, 1.0),     # exponents near -100
