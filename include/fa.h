@@ -99,7 +99,10 @@ enum fa_status {
   FA_ERR_WORKSPACE = -3,    /* workspace missing, smaller than required, or not
                                16-byte aligned (every entry point that takes
                                one)                                            */
-  FA_ERR_LAUNCH = -4        /* the HIP runtime rejected a kernel launch       */
+  FA_ERR_LAUNCH = -4,       /* the HIP runtime rejected a kernel launch, or a
+                               HIP query needed to set up the call failed      */
+  FA_ERR_SCRATCH = -5       /* the problem needs more scratch than the static
+                               buffer of fa_fwd_decode_noalloc holds           */
 };
 
 typedef struct fa_problem {
@@ -183,6 +186,23 @@ int fa_mask_compile(const uint8_t* mask, int32_t nb, int32_t* row_ptr, int32_t* 
 size_t fa_decode_workspace_size(const fa_problem* p, int32_t n_q);
 int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k, const void* v,
                   void* o, float* lse, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* fa_fwd_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as fa_fwd_decode, without the workspace:
+ * the float32 split partials live in a static device buffer inside the
+ * library, 64 MiB (67108864 bytes) per GPU, held from the first call on that
+ * GPU until the process ends.  A problem whose fa_decode_workspace_size
+ * exceeds 64 MiB returns FA_ERR_SCRATCH before anything is enqueued (e.g.
+ * d = 128 with more than 63 query rows per K/V head, rows = H / H_kv * n_q).
+ * The call allocates nothing and clears nothing (every partial the merge
+ * reads is written first in the same call).  `stream` must belong to the
+ * current device (else FA_ERR_ARG).  All calls on one GPU share that GPU's
+ * buffer: calls whose work overlaps on one GPU (other streams, other host
+ * threads) race on it and must be ordered by the caller, e.g. by issuing
+ * them on one stream. */
+int fa_fwd_decode_noalloc(const fa_problem* p, int32_t n_q, const void* q, const void* k,
+                          const void* v, void* o, float* lse, hipStream_t stream);
 
 /* FP8 forward: block quantisation with a random Hadamard-style rotation
  * ("Atencao Eficiente em Escala", section 10 on FlashAttention-3: Q, K, V are

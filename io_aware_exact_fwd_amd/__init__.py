@@ -8,6 +8,7 @@ arguments to its C ABI (``include/fa.h``) and never computes on the CPU.
     dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=True, scale=0.125)
     o = attention(q, k, v, causal=True)        # differentiable wrapper
     o, lse = fa_fwd_decode(q_last, k, v)       # last n_q positions vs N keys
+    o, lse = fa_fwd_decode_noalloc(q_last, k, v, out=o, lse=lse)  # no allocation
     o, lse = fa_fwd_fp8(q, k, v, signs)        # FP8 with block scales + rotation
 """
 
@@ -23,6 +24,7 @@ from .binding import (  # noqa: F401
     fa_bwd_dq,
     fa_fwd,
     fa_fwd_decode,
+    fa_fwd_decode_noalloc,
     fa_fwd_fp8,
     fa_fp8_workspace_size,
     fp8_quantize,

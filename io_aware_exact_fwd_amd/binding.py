@@ -6,8 +6,8 @@ is missing, or a tensor is not a contiguous GPU tensor of a supported type,
 the call raises -- there is no CPU or PyTorch fallback.
 
 Names follow the C ABI: ``fa_fwd``, ``fa_bwd``, ``fa_mask_compile``,
-``fa_workspace_size``, ``fa_fwd_decode``, ``fa_decode_workspace_size``,
-``fa_status_string``, ``fa_version``.
+``fa_workspace_size``, ``fa_fwd_decode``, ``fa_fwd_decode_noalloc``,
+``fa_decode_workspace_size``, ``fa_status_string``, ``fa_version``.
 """
 
 from __future__ import annotations
@@ -21,9 +21,12 @@ LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = 0, -1, -2, -3, -4
+FA_ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 64 << 20  # static scratch of fa_fwd_decode_noalloc, per GPU
 
 EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv",
            "fa_mask_compile", "fa_decode_workspace_size", "fa_fwd_decode",
+           "fa_fwd_decode_noalloc",
            "fa_fp8_workspace_size", "fa_fp8_quantize", "fa_fwd_fp8",
            "fa_status_string", "fa_version")
 
@@ -85,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_workspace_size.restype = sz
     L.fa_fwd_decode.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.fa_fwd_decode.restype = ctypes.c_int
+    L.fa_fwd_decode_noalloc.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp]
+    L.fa_fwd_decode_noalloc.restype = ctypes.c_int
     L.fa_fp8_workspace_size.argtypes = [pp]
     L.fa_fp8_workspace_size.restype = sz
     L.fa_fp8_quantize.argtypes = [pp, vp, vp, vp, vp, vp, sz, vp]
@@ -216,11 +221,7 @@ def fa_decode_workspace_size(p: FaProblem, n_q: int) -> int:
     return int(lib().fa_decode_workspace_size(ctypes.byref(p), int(n_q)))
 
 
-def fa_fwd_decode(q, k, v, causal=True, scale=None, window=0, out=None, lse=None):
-    """Decode-shaped forward: q (B, H, n_q, d) holds the LAST n_q positions of
-    a sequence whose N keys and values are k, v (B, H_kv, N, d).  Returns
-    (O like q, LSE float32 (B, H, n_q), natural log).  The keys are split over
-    workgroups and the partial results merged inside the library."""
+def _decode_args(q, k, v, causal, scale, window, out, lse):
     import torch
 
     _check_tensors(q)
@@ -237,12 +238,41 @@ def fa_fwd_decode(q, k, v, causal=True, scale=None, window=0, out=None, lse=None
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensors(q, o)
+    return p, n_q, o, lse_t
+
+
+def fa_fwd_decode(q, k, v, causal=True, scale=None, window=0, out=None, lse=None):
+    """Decode-shaped forward: q (B, H, n_q, d) holds the LAST n_q positions of
+    a sequence whose N keys and values are k, v (B, H_kv, N, d).  Returns
+    (O like q, LSE float32 (B, H, n_q), natural log).  The keys are split over
+    workgroups and the partial results merged inside the library."""
+    import torch
+
+    p, n_q, o, lse_t = _decode_args(q, k, v, causal, scale, window, out, lse)
     ws_n = fa_decode_workspace_size(p, n_q)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
     st = lib().fa_fwd_decode(ctypes.byref(p), n_q, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                              o.data_ptr(), lse_t.data_ptr(), ws.data_ptr(), ws_n, _stream(q))
     if st != FA_OK:
         raise FaError("fa_fwd_decode", st)
+    return o, lse_t
+
+
+def fa_fwd_decode_noalloc(q, k, v, causal=True, scale=None, window=0, out=None, lse=None):
+    """``fa_fwd_decode`` whose split partials live in the library's static
+    per-GPU scratch (``NOALLOC_SCRATCH_BYTES``) instead of a workspace; for
+    callers that cannot allocate.  Pass ``out`` and ``lse`` to allocate
+    nothing at all.  Calls that overlap on one GPU share the scratch and must
+    be ordered (one stream)."""
+    import torch
+
+    p, n_q, o, lse_t = _decode_args(q, k, v, causal, scale, window, out, lse)
+    with torch.cuda.device(q.device):
+        st = lib().fa_fwd_decode_noalloc(ctypes.byref(p), n_q, q.data_ptr(), k.data_ptr(),
+                                         v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
+                                         _stream(q))
+    if st != FA_OK:
+        raise FaError("fa_fwd_decode_noalloc", st)
     return o, lse_t
 
 

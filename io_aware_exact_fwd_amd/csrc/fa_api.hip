@@ -4,13 +4,18 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
+
+// Size of the static scratch of fa_fwd_decode_noalloc (include/fa.h).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -213,27 +218,22 @@ int check_decode(const fa_problem* p, int32_t n_q) {
   return FA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t fa_decode_workspace_size(const fa_problem* p, int32_t n_q) {
-  if (check_decode(p, n_q) != FA_OK) return 0;
-  const DecodeShape g = decode_shape(p, n_q);
-  if (g.nsplit == 1) return 0;
-  const size_t rows = (size_t)p->B * p->H * n_q;
-  return align_up(rows * g.nsplit * p->d * sizeof(float)) + align_up(rows * g.nsplit * sizeof(float));
-}
-
-int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k, const void* v,
-                  void* o, float* lse, void* workspace, size_t ws_bytes, hipStream_t stream) {
+// Argument checks shared by the two decode entry points.
+int check_decode_call(const fa_problem* p, int32_t n_q, const void* q, const void* k,
+                      const void* v, const void* o, const float* lse) {
   int st = check_decode(p, n_q);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o || !lse) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
     return FA_ERR_ARG;
-  const size_t need = fa_decode_workspace_size(p, n_q);
-  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+// Enqueue the split and merge kernels; `workspace` holds the float32
+// partials (unused when one split suffices).  Every partial slot that the
+// merge reads is written by the split kernel first, so nothing needs clearing.
+int run_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k, const void* v,
+               void* o, float* lse, void* workspace, hipStream_t stream) {
   const DecodeShape g = decode_shape(p, n_q);
   fa::DecParams d;
   d.q = q;
@@ -259,6 +259,78 @@ int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k
   return fa::launch_decode(d, p->dtype, p->d, p->causal != 0, stream) == hipSuccess
              ? FA_OK
              : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+// Scratch of fa_fwd_decode_noalloc: the float32 split partials of callers that
+// cannot allocate.  Each GPU the library runs on holds its own copy for the
+// life of the process.  In host code `scratch` names a host-side stand-in, not
+// the device memory: host code uses only the device address that
+// hipGetSymbolAddress returns for the current device (scratch_of_stream_device).
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// This device's address of `scratch`, looked up once per device (with that
+// device current) on the first call that needs it.  The stream must belong to
+// the current device (NULL: the current device's default stream).
+int scratch_of_stream_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return FA_ERR_ARG;
+    if (sdev != dev) return FA_ERR_ARG;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return FA_ERR_LAUNCH;
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_decode_workspace_size(const fa_problem* p, int32_t n_q) {
+  if (check_decode(p, n_q) != FA_OK) return 0;
+  const DecodeShape g = decode_shape(p, n_q);
+  if (g.nsplit == 1) return 0;
+  const size_t rows = (size_t)p->B * p->H * n_q;
+  return align_up(rows * g.nsplit * p->d * sizeof(float)) + align_up(rows * g.nsplit * sizeof(float));
+}
+
+int fa_fwd_decode(const fa_problem* p, int32_t n_q, const void* q, const void* k, const void* v,
+                  void* o, float* lse, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_decode_call(p, n_q, q, k, v, o, lse);
+  if (st != FA_OK) return st;
+  const size_t need = fa_decode_workspace_size(p, n_q);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
+  return run_decode(p, n_q, q, k, v, o, lse, workspace, stream);
+}
+
+int fa_fwd_decode_noalloc(const fa_problem* p, int32_t n_q, const void* q, const void* k,
+                          const void* v, void* o, float* lse, hipStream_t stream) {
+  int st = check_decode_call(p, n_q, q, k, v, o, lse);
+  if (st != FA_OK) return st;
+  const size_t need = fa_decode_workspace_size(p, n_q);
+  if (need > kScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_of_stream_device(stream, &ws);
+    if (st != FA_OK) return st;
+  }
+  return run_decode(p, n_q, q, k, v, o, lse, ws, stream);
 }
 
 }  // extern "C"
@@ -512,6 +584,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "unsupported problem";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_SCRATCH: return "problem needs more than the library's static scratch";
     default: return "unknown status";
   }
 }

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.fa_version() == 10300
+    assert B.fa_version() == 10400
     assert B.fa_status_string(0) == "ok"
     assert "workspace" in B.fa_status_string(B.FA_ERR_WORKSPACE)
     assert B.fa_status_string(12345) == "unknown status"
@@ -305,3 +305,27 @@ def test_fp8_workspace_views_match_the_documented_layout(B_, H, Hkv, N, d):
         spans.append((start, start + views[name].numel()))
     assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
     assert spans[-1][1] <= need < spans[-1][1] + 256
+
+
+def test_decode_noalloc_checks_before_any_gpu_call():
+    """fa_fwd_decode_noalloc checks its arguments and the scratch limit before
+    touching the GPU: invalid problems, null or misaligned pointers, and a
+    problem whose partials exceed the 64 MiB static scratch."""
+    L = B.lib()
+    for kw, n_q, status in (({}, 0, B.FA_ERR_ARG), ({"dtype": B.FA_F32}, 1, B.FA_ERR_UNSUPPORTED),
+                            ({"dropout_p": 0.1}, 1, B.FA_ERR_UNSUPPORTED),
+                            ({"d": 96}, 1, B.FA_ERR_UNSUPPORTED)):
+        p = _problem(**kw)
+        assert L.fa_fwd_decode_noalloc(ctypes.byref(p), n_q, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       None) == status
+    p = _problem(N=4096, H=8, H_kv=2)
+    assert L.fa_fwd_decode_noalloc(ctypes.byref(p), 1, FAKE, None, FAKE, FAKE, FAKE,
+                                   None) == B.FA_ERR_ARG
+    assert L.fa_fwd_decode_noalloc(ctypes.byref(p), 1, FAKE, FAKE, FAKE, FAKE + 4, FAKE,
+                                   None) == B.FA_ERR_ARG
+    # 128 rows of one K/V head, 2048 splits of 32 keys, d = 128: 134 MB of partials
+    big = _problem(B=1, H=8, H_kv=1, N=65536, d=128, causal=1, dtype=B.FA_BF16)
+    assert B.fa_decode_workspace_size(big, 16) > B.NOALLOC_SCRATCH_BYTES
+    assert L.fa_fwd_decode_noalloc(ctypes.byref(big), 16, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == B.FA_ERR_SCRATCH
+    assert "scratch" in B.fa_status_string(B.FA_ERR_SCRATCH)
