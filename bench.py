@@ -497,12 +497,15 @@ def main():
     ext = dict(window=w.window)
     if w.dropout:
         ext.update(dropout_p=w.dropout, seed=DROPOUT_SEED, offset=0)
-    p, ws, ws_n, bmt = bwd_workspace(q, w.causal, w.scale, bmd, w.mask_block, k=k, **ext)
+    # one workspace for the whole step: the forward compiles the block lists
+    # into it and the backward reuses them (FA_REUSE_LISTS)
+    p, ws, ws_n, bmt = bwd_workspace(q, w.causal, w.scale, bmd, w.mask_block, k=k,
+                                     reuse_lists=bmd is not None, **ext)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        fa_fwd(q, k, v, w.causal, w.scale, bmt, w.mask_block, out=o, lse=lse, **ext)
+        fa_fwd(q, k, v, w.causal, w.scale, bmt, w.mask_block, out=o, lse=lse, workspace=ws, **ext)
         if ev is not None:
             ev[1].record()
         fa_bwd_dq(p, q, k, v, o, do, lse, dq, ws, ws_n)

@@ -92,7 +92,7 @@ enum fa_status {
   FA_ERR_ARG = -1,          /* null pointer, non-positive size, scale not finite
                                and positive, misaligned pointer, negative
                                window, H_kv not dividing H, dropout_p outside
-                               [0, 1), reserved field not 0                   */
+                               [0, 1), an unknown flag bit                     */
   FA_ERR_UNSUPPORTED = -2,  /* d not in {64, 128}; unknown dtype; a block mask
                                whose block is not a positive multiple of 128 or
                                does not divide N                               */
@@ -118,12 +118,29 @@ typedef struct fa_problem {
   uint64_t seed;              /* dropout generator key                         */
   uint32_t offset;            /* dropout counter word: one value per call that
                                  must draw a fresh mask with the same seed     */
-  uint32_t reserved;          /* must be 0                                     */
+  uint32_t flags;             /* 0, or FA_REUSE_LISTS (below)                  */
 } fa_problem;
+
+/* fa_problem.flags bits.
+ * FA_REUSE_LISTS: the workspace passed to this call already holds the block
+ *   lists compiled for this problem's block_mask, N and mask_block -- written
+ *   by an earlier fa_fwd, fa_bwd or fa_bwd_dq call on the same buffer -- so
+ *   this call skips compiling them.  The lists sit at the start of both the
+ *   forward and the backward workspace, so a caller that gives the forward
+ *   and the backward of one step the same buffer (of fa_workspace_size(p, 1)
+ *   bytes) compiles the mask once per step.  The library cannot check the
+ *   contents: with lists of another mask, or none, the behaviour is undefined
+ *   (wrong results, or reads outside the workspace).  Ignored without a
+ *   block mask and for FA_F32 (which reads the mask itself). */
+#define FA_REUSE_LISTS 1u
 
 /* Bytes of device workspace that fa_fwd (pass 0) or fa_bwd (pass 1) needs for
  * problem p; 0 if none.  Host-only arithmetic, no GPU call.  Returns 0 for an
- * invalid problem (the entry point itself then reports the error). */
+ * invalid problem (the entry point itself then reports the error).  Layout:
+ * with a block mask (FA_F16, FA_BF16) the compiled block lists come first in
+ * both passes; the backward then holds D (float32, B*H*N) on the next
+ * 256-byte boundary.  The backward's size is never smaller than the
+ * forward's, so one buffer of the backward's size serves both. */
 size_t fa_workspace_size(const fa_problem* p, int pass);
 
 /* Forward.  Reads q, k, v; overwrites o (B,H,N,d, dtype) and lse (B,H,N,
@@ -137,7 +154,8 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
  * dropout: the same seed and offset, so the same mask is regenerated).
  * Overwrites (does not accumulate into) dq, dk, dv.  workspace: at least
  * fa_workspace_size(p, 1) bytes; it receives D_i = dO_i . O_i (float32, B*H*N)
- * and, with a block mask, the compiled block lists. */
+ * and, with a block mask, the compiled block lists (unless FA_REUSE_LISTS
+ * says they are there already). */
 int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
            size_t ws_bytes, hipStream_t stream);

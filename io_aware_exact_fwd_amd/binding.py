@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = 0, -1, -2, -3, -4
 FA_ERR_SCRATCH = -5
+FA_REUSE_LISTS = 1  # fa_problem.flags: the workspace already holds the compiled block lists
 NOALLOC_SCRATCH_BYTES = 64 << 20  # static scratch of fa_fwd_decode_noalloc, per GPU
 
 EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv",
@@ -47,7 +48,7 @@ class FaProblem(ctypes.Structure):
         ("dropout_p", ctypes.c_float),
         ("seed", ctypes.c_uint64),
         ("offset", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -122,7 +123,7 @@ def _dtype_code(t):
 
 
 def make_problem(q, causal=False, scale=None, block_mask=None, mask_block=128, k=None,
-                 window=0, dropout_p=0.0, seed=0, offset=0) -> FaProblem:
+                 window=0, dropout_p=0.0, seed=0, offset=0, flags=0) -> FaProblem:
     """Problem descriptor for (B, H, N, d) tensor q (and K/V tensor k, whose
     head count gives H_kv); scale defaults to 1/sqrt(d)."""
     if q.dim() != 4:
@@ -142,7 +143,7 @@ def make_problem(q, causal=False, scale=None, block_mask=None, mask_block=128, k
     p.dropout_p = float(dropout_p)
     p.seed = int(seed) & (2**64 - 1)
     p.offset = int(offset) & (2**32 - 1)
-    p.reserved = 0
+    p.flags = int(flags)
     return p
 
 
@@ -195,23 +196,38 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def fa_fwd(q, k, v, causal=False, scale=None, block_mask=None, mask_block=128, out=None,
-           lse=None, window=0, dropout_p=0.0, seed=0, offset=0):
-    """Forward: returns (O, LSE); O like q, LSE float32 (B, H, N), natural log.
-    k, v may have fewer heads than q (grouped / multi-query attention)."""
+def _workspace(ws, need, dev):
+    """A uint8 GPU workspace of at least `need` bytes: the caller's, or a new one."""
     import torch
 
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if ws.dtype != torch.uint8 or not ws.is_cuda or not ws.is_contiguous() or ws.numel() < need:
+        raise ValueError(f"workspace must be a contiguous uint8 GPU tensor of >= {need} bytes")
+    return ws
+
+
+def fa_fwd(q, k, v, causal=False, scale=None, block_mask=None, mask_block=128, out=None,
+           lse=None, window=0, dropout_p=0.0, seed=0, offset=0, workspace=None,
+           reuse_lists=False):
+    """Forward: returns (O, LSE); O like q, LSE float32 (B, H, N), natural log.
+    k, v may have fewer heads than q (grouped / multi-query attention).
+    workspace: optional uint8 GPU tensor (e.g. the backward's, which is at
+    least as large); reuse_lists: it already holds this mask's block lists."""
     _check_qkv(q, k, v)
     bm = _mask_arg(block_mask, q, mask_block)
-    p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset)
+    p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset,
+                     FA_REUSE_LISTS if reuse_lists else 0)
     B, H, N, d = q.shape
+    import torch
+
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensors(q, o)
     ws_n = fa_workspace_size(p, 0)
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    ws = _workspace(workspace, ws_n, q.device)
     st = lib().fa_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                      lse_t.data_ptr(), ws.data_ptr(), ws_n, _stream(q))
+                      lse_t.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q))
     if st != FA_OK:
         raise FaError("fa_fwd", st)
     return o, lse_t
@@ -358,8 +374,10 @@ def fa_fwd_fp8(q, k, v, signs, causal=False, scale=None, window=0, out=None, lse
 
 
 def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, block_mask=None, mask_block=128,
-           window=0, dropout_p=0.0, seed=0, offset=0):
-    """Backward of <O, dO>: returns (dQ, dK, dV); dQ like q, dK and dV like k."""
+           window=0, dropout_p=0.0, seed=0, offset=0, workspace=None, reuse_lists=False):
+    """Backward of <O, dO>: returns (dQ, dK, dV); dQ like q, dK and dV like k.
+    workspace / reuse_lists: as for ``fa_fwd`` (a forward given the same
+    buffer leaves the block lists there for the backward)."""
     import torch
 
     _check_qkv(q, k, v)
@@ -367,25 +385,29 @@ def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, block_mask=None, mas
     if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
         raise ValueError("lse must be a contiguous float32 GPU tensor")
     bm = _mask_arg(block_mask, q, mask_block)
-    p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset)
+    p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset,
+                     FA_REUSE_LISTS if reuse_lists else 0)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_n = fa_workspace_size(p, 1)
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    ws = _workspace(workspace, ws_n, q.device)
     st = lib().fa_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                       dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                      dv.data_ptr(), ws.data_ptr(), ws_n, _stream(q))
+                      dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q))
     if st != FA_OK:
         raise FaError("fa_bwd", st)
     return dq, dk, dv
 
 
 def bwd_workspace(q, causal=False, scale=None, block_mask=None, mask_block=128, k=None,
-                  window=0, dropout_p=0.0, seed=0, offset=0):
-    """(problem, workspace tensor, workspace bytes, mask) for the two backward stages."""
+                  window=0, dropout_p=0.0, seed=0, offset=0, reuse_lists=False):
+    """(problem, workspace tensor, workspace bytes, mask) for the two backward
+    stages; reuse_lists sets FA_REUSE_LISTS in the problem (for a workspace
+    that a forward on the same buffer has filled)."""
     import torch
 
     bm = _mask_arg(block_mask, q, mask_block)
-    p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset)
+    p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset,
+                     FA_REUSE_LISTS if reuse_lists else 0)
     ws_n = fa_workspace_size(p, 1)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
     return p, ws, ws_n, bm

@@ -37,7 +37,7 @@ int check_problem(const fa_problem* p) {
   if (p->window < 0) return FA_ERR_ARG;
   if (p->H_kv < 0 || (p->H_kv > 0 && p->H % p->H_kv != 0)) return FA_ERR_ARG;
   if (!(p->dropout_p >= 0.f && p->dropout_p < 1.f)) return FA_ERR_ARG;
-  if (p->reserved != 0) return FA_ERR_ARG;
+  if ((p->flags & ~FA_REUSE_LISTS) != 0) return FA_ERR_ARG;
   if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (p->d != 64 && p->d != 128) return FA_ERR_UNSUPPORTED;
   // one head must be addressable with 32-bit byte offsets
@@ -114,7 +114,7 @@ extern "C" {
 size_t fa_workspace_size(const fa_problem* p, int pass) {
   if (check_problem(p) != FA_OK) return 0;
   if (pass == 0) return lists_bytes(p);
-  return dvec_bytes(p) + lists_bytes(p);
+  return lists_bytes(p) + dvec_bytes(p);
 }
 
 int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -168,7 +168,8 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
   const bool masked = p->block_mask != nullptr;
   if (masked) {
     Lists l = carve_lists(p, (char*)workspace);
-    if (fa::launch_mask_compile(p->block_mask, p->N / p->mask_block, l.row_ptr, l.col_idx,
+    if (!(p->flags & FA_REUSE_LISTS) &&
+        fa::launch_mask_compile(p->block_mask, p->N / p->mask_block, l.row_ptr, l.col_idx,
                                 l.col_ptr, l.row_idx, s) != hipSuccess)
       return FA_ERR_LAUNCH;
     f.m = mask_lists(p, l);
@@ -466,7 +467,7 @@ int bwd_setup(const fa_problem* p, const void* q, const void* k, const void* v, 
   b->dq = const_cast<void*>(dq);
   b->dk = const_cast<void*>(dk);
   b->dv = const_cast<void*>(dv);
-  b->dvec = (float*)workspace;
+  b->dvec = (float*)((char*)workspace + lists_bytes(p));
   b->N = p->N;
   b->nheads = p->B * p->H;
   b->window = p->window;
@@ -475,7 +476,7 @@ int bwd_setup(const fa_problem* p, const void* q, const void* k, const void* v, 
   b->scale = p->scale;
   b->m = no_lists();
   b->drop = drop_params(p);
-  if (p->block_mask) b->m = mask_lists(p, carve_lists(p, (char*)workspace + dvec_bytes(p)));
+  if (p->block_mask) b->m = mask_lists(p, carve_lists(p, (char*)workspace));
   return FA_OK;
 }
 
@@ -509,7 +510,8 @@ int run_dq(const fa_problem* p, fa::BwdParams b, hipStream_t s) {
   if (p->dtype == FA_F32)
     return fa::launch_f32_dq(f32_params(p, b), s) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
   const bool masked = p->block_mask != nullptr;
-  if (masked && fa::launch_mask_compile(p->block_mask, p->N / p->mask_block,
+  if (masked && !(p->flags & FA_REUSE_LISTS) &&
+      fa::launch_mask_compile(p->block_mask, p->N / p->mask_block,
                                         (int32_t*)b.m.row_ptr, (int32_t*)b.m.col_idx,
                                         (int32_t*)b.m.col_ptr, (int32_t*)b.m.row_idx,
                                         s) != hipSuccess)

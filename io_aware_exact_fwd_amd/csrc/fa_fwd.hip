@@ -8,8 +8,10 @@
 //      on the matrix cores, fp32 accumulate -- they never leave registers;
 //      every K fragment read from LDS feeds QB products;
 //   2. applies the causal / sequence-end mask on the tiles that need it;
-//   3. runs the online-softmax update in the base-2 domain: row maximum of
-//      the tile, P = 2^(S * scale * log2 e - m), running row sum l += rowsum P;
+//   3. runs the online-softmax update in the base-2 domain, 16 keys at a
+//      time: P = 2^(S * scale * log2 e - m) against the row's reference m
+//      (moved, with O and l rescaled, only when the weights would overflow;
+//      see below), running row sum l += rowsum P;
 //   4. accumulates O^T += V_j^T P^T on the matrix cores (P rounded to the
 //      input type, V read from LDS with transpose reads, each V fragment
 //      feeding QB products).
@@ -24,10 +26,14 @@
 // Reference maximum.  The recurrence rescales the accumulated O and l by
 // 2^(m_old - m_new) whenever the row maximum grows.  Any reference value gives
 // the same O / l and the same m + log2 l, as long as the exponentials stay in
-// range; so the reference is only moved when the tile maximum exceeds it by
-// more than kRescaleTau (P <= 2^kRescaleTau = 256, exact in fp16/bf16 range).
-// With scores of moderate spread this skips nearly every rescale.  The move is
-// decided per wave (any row over the threshold moves all rows of the wave).
+// range; so no row maximum is computed on the common path: each 16-key step
+// takes its weights against the row's current reference, and only when the
+// new row sum overflows a limit (an fp16 weight above 65504 is infinite; see
+// kRowSumLimit) -- or the row has no reference yet -- the step's scores give
+// the new maximum, O and l are rescaled and the step's weights recomputed.
+// The reference is always a maximum of scores the row has seen, so the
+// largest weight so far is >= 1 and the sums keep their precision.  The move
+// is decided per wave (any row over the limit moves all rows of the wave).
 //
 // Register layout: computing S^T (keys as rows) rather than S puts one query
 // per lane (lanes l and l+32 share it), so row reductions are in-lane plus one
@@ -42,7 +48,12 @@
 
 namespace fa {
 
-constexpr float kRescaleTau = 8.0f;
+// A step whose new row sum is not below kRowSumLimit moves the reference.
+// fp16 weights above 65504 round to infinity, which the sum carries; bf16 and
+// float32 weights stay finite, and the limit keeps each one (and the O
+// accumulators, sums of them times V) far from float32 overflow.
+constexpr float kRowSumLimit = 0x1p64f;
+constexpr float kNoRef = __builtin_huge_valf();  // row sum while a row has no reference
 
 // Tuning knobs of the dense head-dim-64 forward: waves per workgroup, 32-row
 // query blocks per wave, waves per SIMD the register budget targets.  Measured
@@ -63,6 +74,9 @@ constexpr float kRescaleTau = 8.0f;
 #endif
 #ifndef FA_FWD64_WPE
 #define FA_FWD64_WPE 4
+#endif
+#ifndef FA_FWD_CHECK_KEYS
+#define FA_FWD_CHECK_KEYS 16
 #endif
 // Block-sparse, head dim 64: LDS stages and waves per SIMD.  Three stages keep
 // the copies of two scattered key tiles in flight (48 KiB per workgroup, so
@@ -148,16 +162,19 @@ void fwd_kernel(FwdParams p) {
       qf[qb][t] = __builtin_bit_cast(
           V8, buf_load16(bq, (uint32_t)((qw0 + qb * 32 + l32) * D + t * 16 + g * 8) * sizeof(T)));
 
+  // Per row: m_ref, the reference maximum (-inf until the row has seen a
+  // key); ref, the value the weights are taken against (m_ref, or 0 while
+  // there is none); l_run, the running sum of the weights (kNoRef while there
+  // is no reference, which sends the first step to the reference move).
   f32x16 o[QB][G::NDB];
-  float m_ref[QB], ref[QB], l_run[QB], thr[QB];  // thr = m_ref + kRescaleTau
+  float m_ref[QB], ref[QB], l_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
     for (int i = 0; i < G::NDB; ++i) o[qb][i] = f32x16{0};
     m_ref[qb] = kNegInf;
-    thr[qb] = kNegInf;
     ref[qb] = 0.f;
-    l_run[qb] = 0.f;
+    l_run[qb] = kNoRef;
   }
 
   // K and V tiles go straight from global memory to LDS
@@ -251,13 +268,13 @@ void fwd_kernel(FwdParams p) {
           }
         }
       }
-      // 3-4. per 32-key half kb: row maxima of the half, reference move if
-      // needed, P = 2^(S c - ref) packed to the input type, row sums, then
-      // O^T += V^T P^T for its two key steps.  With both halves' scores
-      // computed first, the exponentials of half 0 overlap the score products
-      // of half 1 still in flight, and those of half 1 the P V products of
-      // half 0.  The reference may move between the halves; O and l are
-      // rescaled with it, so the result is the same.
+      // 3-4. per 16-key step: P = 2^(S c - ref) against the row's current
+      // reference, packed to the input type, row sums, then O^T += V^T P^T.
+      // The reference moves only when a step's weights would overflow (see
+      // the header); one compare of the new row sum detects it.  With both
+      // halves' scores computed first, the exponentials of half 0 overlap the
+      // score products of half 1 still in flight, and those of half 1 the P V
+      // products of half 0.
 #pragma unroll
       for (int j = 0; j < NKB; ++j) {
         const int kb = KB0 + j;
@@ -270,57 +287,82 @@ void fwd_kernel(FwdParams p) {
             kw[qb] = drop_bytes_query_lanes(p.drop, (uint32_t)head, k0 + kb * 32, qw0 + qb * 32,
                                             smem + NST * G::STAGE + wave * kDropLdsPerWave, lane);
         }
-        float mxs[QB];
-        bool move = false;
+        // the weights of 16 keys (step th of the half), their sum (fp16: of
+        // the rounded weights that P V uses; bf16: of the float32 weights,
+        // bf16 rounding being too coarse for the LSE) added to lp
+        u32x4 w[QB][2];
+        auto weights = [&](int qb, int th, float& lp) __attribute__((always_inline)) {
+          const int r0 = th * 8;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          mxs[qb] = max16(s[qb][j]) * p.c;
-          move |= mxs[qb] > thr[qb];
-        }
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {
-          FA_KEEP_BRANCH();
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const float m_new = vmax(m_ref[qb], pair_max(mxs[qb]));
-            const float r_new = (m_new == kNegInf) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_ref[qb] - r_new);  // 0 while m_ref = -inf
-            l_run[qb] *= alpha;
-#pragma unroll
-            for (int i = 0; i < G::NDB; ++i) o[qb][i] *= alpha;
-            m_ref[qb] = m_new;
-            thr[qb] = m_new + kRescaleTau;
-            ref[qb] = r_new;
+          for (int h = 0; h < 4; ++h) {
+            const float e0 = fast_exp2(__builtin_fmaf(s[qb][j][r0 + 2 * h], p.c, -ref[qb]));
+            const float e1 = fast_exp2(__builtin_fmaf(s[qb][j][r0 + 2 * h + 1], p.c, -ref[qb]));
+            w[qb][th][h] = pack2<T>(e0, e1);
+            if constexpr (__is_same(T, _Float16)) lp = add_pair<T>(w[qb][th][h], lp);
+            else lp += e0 + e1;
           }
-        }
+        };
+        // CHK: keys whose weights are checked together (16: each step; 32:
+        // the half)
+        constexpr int CHK = FA_FWD_CHECK_KEYS;
 #pragma unroll
-        for (int th = 0; th < 2; ++th) {
-          const int t = kb * 2 + th, r0 = th * 8;
-          V8 bp[QB];
+        for (int c = 0; c < 32 / CHK; ++c) {
+          const int th0 = c * (CHK / 16), nth = CHK / 16;
+          float l_new[QB];
+          bool bad = false;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
-            u32x4 w;
-            float lp = 0.f;  // bf16: this 16-key step's fp32 sum
+            float lp = 0.f;
+            for (int th = th0; th < th0 + nth; ++th) weights(qb, th, lp);
+            l_new[qb] = l_run[qb] + lp;
+            bad |= !(l_new[qb] < kRowSumLimit);
+          }
+          if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+            FA_KEEP_BRANCH();
+            // move each row's reference to the maximum of the row so far
+            // (these scores included) and redo the weights
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              const float e0 = fast_exp2(__builtin_fmaf(s[qb][j][r0 + 2 * h], p.c, -ref[qb]));
-              const float e1 = fast_exp2(__builtin_fmaf(s[qb][j][r0 + 2 * h + 1], p.c, -ref[qb]));
-              w[h] = pack2<T>(e0, e1);
-              if constexpr (__is_same(T, _Float16)) {
-                l_run[qb] = add_pair<T>(w[h], l_run[qb]);  // fp16: the rounded weights P V uses
-              } else {
-                lp += e0 + e1;  // bf16 rounding is too coarse for the LSE: fp32 sum
-              }
-              // dropout zeroes weights after the row sum: LSE normalises P itself
-              if constexpr (DROP) w[h] &= keep_pair_mask(kw[qb][th * 2 + (h >> 1)], h & 1, bias);
+            for (int qb = 0; qb < QB; ++qb) {
+              float mx = kNegInf;
+#pragma unroll
+              for (int r = th0 * 8; r < (th0 + nth) * 8; ++r) mx = vmax(mx, s[qb][j][r]);
+              const float m_new = vmax(m_ref[qb], pair_max(mx * p.c));
+              const float r_new = m_new == kNegInf ? 0.f : m_new;
+              const bool had = m_ref[qb] != kNegInf;
+              float alpha = fast_exp2(had ? ref[qb] - r_new : kNegInf);  // 0 without a reference
+              __asm__ volatile("" : "+v"(alpha));  // one rescale path, not one per case
+#pragma unroll
+              for (int i = 0; i < G::NDB; ++i) o[qb][i] *= alpha;
+              l_run[qb] = had ? l_run[qb] * alpha : (m_new == kNegInf ? kNoRef : 0.f);
+              m_ref[qb] = m_new;
+              ref[qb] = r_new;
+              float lp = 0.f;
+              for (int th = th0; th < th0 + nth; ++th) weights(qb, th, lp);
+              l_new[qb] = l_run[qb] + lp;
             }
-            if constexpr (!__is_same(T, _Float16)) l_run[qb] += lp;
-            bp[qb] = __builtin_bit_cast(V8, w);
           }
 #pragma unroll
-          for (int db = 0; db < G::NDB; ++db) {
-            const V8 a = toff.template tr_operand<T>(vs, t * 16, db);
+          for (int qb = 0; qb < QB; ++qb) l_run[qb] = l_new[qb];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(a, bp[qb], o[qb][db]);
+          for (int th = th0; th < th0 + nth; ++th) {
+            const int t = kb * 2 + th;
+            V8 bp[QB];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+              // dropout zeroes weights after the row sum: LSE normalises P itself
+              if constexpr (DROP) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                  w[qb][th][h] &= keep_pair_mask(kw[qb][th * 2 + (h >> 1)], h & 1, bias);
+              }
+              bp[qb] = __builtin_bit_cast(V8, w[qb][th]);
+            }
+#pragma unroll
+            for (int db = 0; db < G::NDB; ++db) {
+              const V8 a = toff.template tr_operand<T>(vs, t * 16, db);
+#pragma unroll
+              for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(a, bp[qb], o[qb][db]);
+            }
           }
         }
       }
@@ -351,7 +393,7 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int q = qw0 + qb * 32 + l32;
-    const float lt = pair_sum(l_run[qb]);
+    const float lt = pair_sum(m_ref[qb] == kNegInf ? 0.f : l_run[qb]);
     const float inv = lt > 0.f ? (DROP ? p.drop.mult : 1.f) / lt : 0.f;
     if (q < N) {
       T* orow = (T*)p.o + head_off + (size_t)q * D;

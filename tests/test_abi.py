@@ -53,7 +53,7 @@ def _problem(**kw):
     p.dropout_p = kw.get("dropout_p", 0.0)
     p.seed = kw.get("seed", 0)
     p.offset = kw.get("offset", 0)
-    p.reserved = kw.get("reserved", 0)
+    p.flags = kw.get("flags", 0)
     return p
 
 
@@ -63,7 +63,7 @@ def test_problem_struct_layout_matches_header():
     off = {name: getattr(B.FaProblem, name).offset for name, _ in B.FaProblem._fields_}
     assert off["scale"] == 24 and off["block_mask"] == 32 and off["mask_block"] == 40
     assert off["window"] == 44 and off["H_kv"] == 48 and off["dropout_p"] == 52
-    assert off["seed"] == 56 and off["offset"] == 64 and off["reserved"] == 68
+    assert off["seed"] == 56 and off["offset"] == 64 and off["flags"] == 68
     assert ctypes.sizeof(B.FaProblem) == 72
 
 
@@ -111,7 +111,8 @@ def _fwd(p, ws=None, ws_n=0, ptrs=(FAKE,) * 5):
     ({"dropout_p": 1.0}, B.FA_ERR_ARG),
     ({"dropout_p": -0.1}, B.FA_ERR_ARG),
     ({"dropout_p": math.nan}, B.FA_ERR_ARG),
-    ({"reserved": 1}, B.FA_ERR_ARG),
+    ({"flags": 2}, B.FA_ERR_ARG),          # an unknown flag bit
+    ({"flags": 0x80000001}, B.FA_ERR_ARG),
 ])
 def test_invalid_problems_rejected(kw, status):
     assert _fwd(_problem(**kw)) == status

@@ -191,3 +191,33 @@ def test_backward_stages_equal_fused_entry_point():
     torch.cuda.synchronize()
     for a, b in zip(g, (dq, dk, dv)):
         assert torch.equal(a, b)
+
+
+def test_shared_workspace_reuses_block_lists():
+    """A forward and a backward given one workspace: the backward called with
+    FA_REUSE_LISTS (lists left by the forward) gives bitwise the results of
+    separate calls that each compile the mask, also through the two stages."""
+    from io_aware_exact_fwd_amd import bwd_workspace, fa_bwd_dkdv, fa_bwd_dq, fa_workspace_size
+    from io_aware_exact_fwd_amd.binding import make_problem
+
+    dev = torch.device("cuda:0")
+    say("[case] shared workspace, block lists reused")
+    bm = torch.as_tensor(_mask_with_holes(8), device=dev)
+    q, k, v, do = (t.to(dev) for t in make_inputs(1, 4, 1024, 64, "f16", hkv=2))
+    kw = dict(causal=True, scale=0.125, block_mask=bm, mask_block=128, window=500)
+    o1, l1 = fa_fwd(q, k, v, **kw)
+    g1 = fa_bwd(q, k, v, o1, do, l1, **kw)
+    p = make_problem(q, True, 0.125, bm, 128, k, 500)
+    ws = torch.empty(fa_workspace_size(p, 1), dtype=torch.uint8, device=dev)
+    assert fa_workspace_size(p, 1) >= fa_workspace_size(p, 0) > 0
+    o2, l2 = fa_fwd(q, k, v, workspace=ws, **kw)
+    g2 = fa_bwd(q, k, v, o2, do, l2, workspace=ws, reuse_lists=True, **kw)
+    p3, ws3, ws3_n, bm3 = bwd_workspace(q, k=k, reuse_lists=True, **kw)
+    o3, l3 = fa_fwd(q, k, v, workspace=ws3, **kw)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd_dq(p3, q, k, v, o3, do, l3, dq, ws3, ws3_n)
+    fa_bwd_dkdv(p3, q, k, v, do, l3, dk, dv, ws3, ws3_n)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
+    for a, b, c in zip(g1, g2, (dq, dk, dv)):
+        assert torch.equal(a, b) and torch.equal(a, c)
