@@ -50,8 +50,8 @@ def _compile(src: str, hipcc: str, build_dir: str, defines) -> str:
 
 
 def build(verbose: bool = True, defines=(), out: str = LIB) -> str:
-    """Compile and link; `defines` are extra preprocessor definitions (tuning
-    knobs of the kernels), `out` the library path."""
+    """Compile and link; `defines` are extra preprocessor definitions passed
+    to every source, `out` the library path."""
     hipcc = _hipcc()
     build_dir = BUILD if out == LIB else out + ".objs"
     os.makedirs(build_dir, exist_ok=True)

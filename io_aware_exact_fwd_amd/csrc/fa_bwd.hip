@@ -32,63 +32,26 @@
 
 namespace fa {
 
-// Tuning knobs: waves per SIMD of the dQ kernel, query rows per step and waves
-// per SIMD of the dK/dV kernel.  At head dim 64, running the two 32-key halves
-// of a tile one after the other (scores to dQ) keeps dQ within 124 VGPRs, so
-// it runs at four waves per SIMD: 3-4 % faster on MI355X than both halves at
-// once at three waves (150 VGPRs), with bitwise the same dQ.  Likewise dK/dV
-// handles the 32-query blocks of a step one after the other: at head dim 64
-// it fits 168 VGPRs, three waves per SIMD instead of two (dK/dV 5 % faster),
-// and at head dim 128 it runs 10 % faster at the same occupancy; 128-query
-// steps (half the barriers, two LDS stages) measured slower.  Measured on MI355X at head dim 128: dQ under
-// dropout fits two waves per SIMD (234-240 VGPRs) and runs 19 % faster than
-// with one; dK/dV needs about 350 registers (VGPRs and AGPRs) and spills at
-// two waves per SIMD, running at half the speed.
-#ifndef FA_DQ_WPE
-#define FA_DQ_WPE 4
-#endif
-#ifndef FA_DQ64_MASKED_NST
-#define FA_DQ64_MASKED_NST 2  // 3 measured 4 % slower on the N = 65536 butterfly workload
-#endif
-#ifndef FA_DQ64_DROP_DENSE_WPE
-#define FA_DQ64_DROP_DENSE_WPE 4  // dropout without a block mask: 128 VGPRs, 3.5 % faster than 3
-#endif
-#ifndef FA_DQ64_DROP_WPE
-#define FA_DQ64_DROP_WPE 3  // dropout with a block mask: four waves would spill
-#endif
-#ifndef FA_DQ128_WPE
-#define FA_DQ128_WPE 2
-#endif
-#ifndef FA_DKDV_QT
-#define FA_DKDV_QT 64
-#endif
-#ifndef FA_DKDV_QBLK
-#define FA_DKDV_QBLK 1  // 32-query blocks of a step handled together (scores to products)
-#endif
-#ifndef FA_DKDV_NST
-#define FA_DKDV_NST 2  // LDS stages of the d = 64 dK/dV ring (2 or 3)
-#endif
-#ifndef FA_DKDV_AHEAD
-#define FA_DKDV_AHEAD 4  // LDS reads issued ahead of the score products (0: compiler's order)
-#endif
-#ifndef FA_DQ_HALVES
-#define FA_DQ_HALVES 1  // 1: each 32-key half of a tile runs scores to dQ before the next
-#endif
-#ifndef FA_DQ_AHEAD
-#define FA_DQ_AHEAD 0
-#endif
-#ifndef FA_DKDV64_WPE
-#define FA_DKDV64_WPE 3
-#endif
-#ifndef FA_DKDV64_DROP_WPE
-#define FA_DKDV64_DROP_WPE 2  // dropout's generator registers: three waves would spill
-#endif
-#ifndef FA_DKDV128_WPE
-#define FA_DKDV128_WPE 1
-#endif
-#ifndef FA_DQ128_DROP_WPE
-#define FA_DQ128_DROP_WPE 2
-#endif
+// Waves per SIMD each kernel's register budget targets, measured on MI355X.
+// dQ runs the two 32-key halves of a tile one after the other (scores to dQ),
+// which keeps it within 124 VGPRs at head dim 64: four waves per SIMD, 3-4 %
+// faster than both halves at once at three waves (150 VGPRs).  Likewise dK/dV
+// handles the two 32-query blocks of a 64-query step one after the other: at
+// head dim 64 it fits the 168 VGPRs of three waves (5 % faster than two), and
+// at head dim 128 it runs 10 % faster at the same occupancy; 128-query steps
+// (half the barriers) and a three-stage LDS ring measured slower.  At head dim
+// 128, dQ under dropout fits two waves (19 % faster than one); dK/dV needs
+// about 350 registers (VGPRs and AGPRs) and spills at two waves per SIMD.
+constexpr int kDqWpe64 = 4;
+constexpr int kDqWpe64DropDense = 4;  // dropout without a block mask: 128 VGPRs, 3.5 % faster than 3
+constexpr int kDqWpe64DropMasked = 3; // dropout with a block mask: four waves would spill
+constexpr int kDqWpe128 = 2;
+constexpr int kDqWpe128Drop = 2;
+constexpr int kDkdvWpe64 = 3;
+constexpr int kDkdvWpe64Drop = 2;     // dropout's generator registers: three waves would spill
+constexpr int kDkdvWpe128 = 1;
+constexpr int kDkdvQueries = 64;      // queries per dK/dV step (two 32-query blocks)
+constexpr int kDkdvAhead = 4;         // LDS operand reads issued ahead of the score products
 
 // ============================================================================
 // dQ kernel
@@ -103,14 +66,10 @@ struct DqGeom {
   static constexpr int NKS = D / 16;
   // waves per SIMD the registers allow
   static constexpr int wpe(bool drop, bool masked) {
-    if (D == 128) return drop ? FA_DQ128_DROP_WPE : FA_DQ128_WPE;
-    if (masked && nst(masked) > 2) return 3;  // LDS: three 48 KiB workgroups per CU
-    if (drop) return masked ? FA_DQ64_DROP_WPE : FA_DQ64_DROP_DENSE_WPE;
-    return FA_DQ_WPE;
+    if (D == 128) return drop ? kDqWpe128Drop : kDqWpe128;
+    if (drop) return masked ? kDqWpe64DropMasked : kDqWpe64DropDense;
+    return kDqWpe64;
   }
-  // LDS stages: block-sparse at head dim 64 may keep the copies of two key
-  // tiles in flight (its kept tiles are scattered over the sequence)
-  static constexpr int nst(bool masked) { return masked && D == 64 ? FA_DQ64_MASKED_NST : 2; }
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
@@ -120,8 +79,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
 void bwd_dq_kernel(BwdParams p) {
   using G = DqGeom<D>;
   using V8 = typename Vec8<T>::type;
-  constexpr int NST = G::nst(MASKED);
-  __shared__ __attribute__((aligned(16))) char smem[NST * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -188,22 +146,17 @@ void bwd_dq_kernel(BwdParams p) {
 
   const int ntiles = tiles.count;
   if (ntiles > 0) gload(0, 0);
-  if (NST > 2 && ntiles > 1) gload(1, 1);
   wait_all_memory();
   __syncthreads();
 
   const TileOffsets<D> toff(lane);
-  // With NST stages the copies of tile it + NST - 1 are issued at the start of
-  // step it, and a step ends once this thread's copies of the next tile have
-  // landed (those of the tile after it may stay in flight: the loop issues no
-  // other vector-memory operations, and they complete in issue order).
-  constexpr int COPIES = 2 * (G::KT * D / 8 / 256);  // K and V copies per thread per tile
-  // one key tile; the LDS stage is a compile-time constant (NST steps per
-  // iteration of the loop below), so it joins the reads' immediate offsets
+  // The copies of tile it + 1 are issued at the start of step it, and a step
+  // ends once this thread's copies have landed.  One key tile per step; the
+  // LDS stage is a compile-time constant (two steps per iteration of the loop
+  // below), so it joins the reads' immediate offsets.
   auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
     constexpr int cur = decltype(stage)::value;
-    constexpr int pre = (cur + NST - 1) % NST;  // stage of tile it + NST - 1
-    if (it + NST - 1 < ntiles) gload(it + NST - 1, pre);
+    if (it + 1 < ntiles) gload(it + 1, 1 - cur);
 
     const int k0 = tiles.pos0(it);
     const char* ks = smem + cur * G::STAGE;
@@ -213,9 +166,10 @@ void bwd_dq_kernel(BwdParams p) {
     // key halves KB0 .. KB0 + NKB - 1 of the tile: scores, dP, dS, then dQ
     auto halves = [&](auto kb0_c, auto nkb_c) __attribute__((always_inline)) {
       constexpr int KB0 = decltype(kb0_c)::value, NKB = decltype(nkb_c)::value;
+      static_assert(NKB == 1, "one 32-key half at a time");
       // a half no row of the wave sees adds nothing (the later half of a
       // causal diagonal tile)
-      if (NKB == 1 && (k0 + KB0 * 32 > band.hi(qw_last) || k0 + KB0 * 32 + 31 < band.lo(qw0))) return;
+      if (k0 + KB0 * 32 > band.hi(qw_last) || k0 + KB0 * 32 + 31 < band.lo(qw0)) return;
       f32x16 s[NKB], dp[NKB];
 #pragma unroll
       for (int i = 0; i < NKB; ++i) {
@@ -229,7 +183,6 @@ void bwd_dq_kernel(BwdParams p) {
           dp[i] = mfma32(b, dof[t], dp[i]);
         }
       }
-      sched_reads_ahead<2 * NKB * G::NKS, FA_DQ_AHEAD>();
       // hide keys outside the row's band (future, outside the window, past
       // the end): key of register r is k0 + g*4 + C(kb, r) with
       // C = kb*32 + (r/4)*8 + r%4; hidden iff C < lb or C > ub
@@ -261,7 +214,7 @@ void bwd_dq_kernel(BwdParams p) {
         u32x4 kw;
         if constexpr (DROP)
           kw = drop_bytes_query_lanes(p.drop, (uint32_t)head, k0 + (KB0 + i) * 32, qw0,
-                                      smem + NST * G::STAGE + wave * kDropLdsPerWave, lane);
+                                      smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pr = fast_exp2(__builtin_fmaf(s[i][r], p.c, -lse2));
@@ -287,26 +240,15 @@ void bwd_dq_kernel(BwdParams p) {
         }
     };
     if (active) {
-      if constexpr (FA_DQ_HALVES) {
-        halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-        halves(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
-      } else {
-        halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
-      }
+      halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+      halves(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
     }
-    // this thread's copies of tile it + 1 have landed
-    if (NST > 2 && it + 2 < ntiles)
-      __builtin_amdgcn_s_waitcnt(vmcnt_at_most(COPIES));
-    else
-      wait_all_memory();
+    wait_all_memory();  // this thread's copies of tile it + 1 have landed
     __syncthreads();
   };
-  for (int it = 0; it < ntiles; it += NST) {
+  for (int it = 0; it < ntiles; it += 2) {
     step(it, std::integral_constant<int, 0>{});
     if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
-    if constexpr (NST > 2) {
-      if (it + 2 < ntiles) step(it + 2, std::integral_constant<int, 2>{});
-    }
   }
 
   if (q < N) {
@@ -329,24 +271,17 @@ void bwd_dq_kernel(BwdParams p) {
 // ============================================================================
 template <int D>
 struct DkvGeom {
-  static constexpr int QT = FA_DKDV_QT;     // queries per step
+  static constexpr int QT = kDkdvQueries;   // queries per step
   static constexpr int TBYTES = QT * D * 2;  // Q / dO tile, swizzled (no padding)
-  static constexpr int NL = (QT + 63) / 64;  // 64-row copies of LSE (and of D) per step
-  static constexpr int LBYTES = NL * 256;    // LSE (or D) of the step's rows, one dword per lane
+  static constexpr int LBYTES = 256;         // LSE (or D) of the step's rows, one dword per lane
   static constexpr int STAGE = 2 * TBYTES + 2 * LBYTES;  // Q, dO, LSE, D
-  static constexpr int NST = D == 64 ? FA_DKDV_NST : 2;   // stages in the LDS ring
-  static_assert(NST == 2 || NST == 3, "the step loop unrolls two or three stages");
-  static constexpr int COPIES = 2 * (QT * D / 8 / 256);    // Q and dO copies per thread per step
-  static constexpr int LCOPIES = 2 * NL;    // LSE and D copies per step (wave 0)
-  static_assert(QT % 32 == 0 && QT <= 128, "whole 32-query blocks, within a 128-row mask block");
+  static_assert(QT == 64, "one 64-lane copy of LSE and D per step; two 32-query blocks");
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
   static constexpr int NQB = QT / 32;       // 32-query blocks per step
-  static constexpr int QBLK = FA_DKDV_QBLK < NQB ? FA_DKDV_QBLK : NQB;  // blocks handled together
-  static_assert(NQB % QBLK == 0, "the step splits into whole groups of blocks");
   // waves per SIMD the registers allow
   static constexpr int wpe(bool drop) {
-    return D == 64 ? (drop ? FA_DKDV64_DROP_WPE : FA_DKDV64_WPE) : FA_DKDV128_WPE;
+    return D == 64 ? (drop ? kDkdvWpe64Drop : kDkdvWpe64) : kDkdvWpe128;
   }
 };
 
@@ -362,7 +297,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   // to |S c| 2^-11, which for large logits (|S c| ~ 100) breaks the
   // gradients' tolerance.
   constexpr bool kFoldD = D == 64 && !DROP;
-  __shared__ __attribute__((aligned(16))) char smem[G::NST * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -413,9 +348,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   // Q, dO, LSE and D of a step go straight from global memory to LDS (no
   // registers, no store instructions): Q and dO by all waves, LSE and D by
   // wave 0, one row per lane (lanes past QT and rows past N read as zeros;
-  // such rows are hidden by the masks).  With NST = 3 stages the copies of
-  // step it + 2 are issued at the start of step it, so a step waits only for
-  // copies issued a whole step earlier.
+  // such rows are hidden by the masks).  The copies of step it + 1 are issued
+  // at the start of step it.
   auto gload = [&](int it, char* st) {
     const int r = it / nqt;
     const int qs = tiles.pos0(it - r * nqt);
@@ -427,29 +361,18 @@ void bwd_dkdv_kernel(BwdParams p) {
     if (wave == 0) {
       const Buf bl = make_buf(p.lse + qh * N, (uint32_t)N * 4);
       const Buf bd = make_buf(p.dvec + qh * N, (uint32_t)N * 4);
-#pragma unroll
-      for (int c = 0; c < G::NL; ++c) {
-        const int r = c * 64 + lane;
-        const uint32_t off = r < G::QT ? (uint32_t)(qs + r) * 4 : 0x80000000u;
-        dma4(bl, off, st + 2 * G::TBYTES + c * 256);
-        dma4(bd, off, st + 2 * G::TBYTES + G::LBYTES + c * 256);
-      }
+      const uint32_t off = (uint32_t)(qs + lane) * 4;
+      dma4(bl, off, st + 2 * G::TBYTES);
+      dma4(bd, off, st + 2 * G::TBYTES + G::LBYTES);
     }
   };
-  // Wait until this wave's copies of the next step have landed (those of the
-  // step after it may stay in flight), then wave 0 converts that step's rows
+  // Wait until this wave's copies of the next step have landed, then wave 0
+  // converts that step's rows
   // in place: LSE -> LSE log2(e) (+inf for a row with no visible key, so P =
   // 0), D -> D / mult under dropout (see the dS step), D -> -D where the dP
   // accumulators start from it.  The barrier that follows publishes the stage.
-  auto land_next = [&](bool younger_in_flight, char* st) {
-    if (G::NST > 2 && younger_in_flight) {
-      if (wave == 0)
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(G::COPIES + G::LCOPIES));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(G::COPIES));
-    } else {
-      wait_all_memory();
-    }
+  auto land_next = [&](char* st) {
+    wait_all_memory();
     if (wave == 0) {
       float* ls = (float*)(st + 2 * G::TBYTES);
       float* ds = (float*)(st + 2 * G::TBYTES + G::LBYTES);
@@ -465,19 +388,17 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   const int ntiles = nqt * p.group;
   if (ntiles > 0) gload(0, smem);
-  if (G::NST > 2 && ntiles > 1) gload(1, smem + G::STAGE);
-  land_next(ntiles > 1, smem);
+  land_next(smem);
   __syncthreads();
 
   const TileOffsets<D> toff(lane);
-  // one query step; its LDS stage (it mod NST) is a compile-time constant
-  // (NST steps per iteration of the loop below), so stage addresses join the
+  // one query step; its LDS stage (it mod 2) is a compile-time constant (two
+  // steps per iteration of the loop below), so stage addresses join the
   // reads' immediate offsets
   auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
     constexpr int cur = decltype(stage)::value;
-    constexpr int nxt = cur + 1 == G::NST ? 0 : cur + 1;  // stage of step it + 1
-    constexpr int pre = (cur + G::NST - 1) % G::NST;      // stage of step it + NST - 1
-    if (it + G::NST - 1 < ntiles) gload(it + G::NST - 1, smem + pre * G::STAGE);
+    constexpr int nxt = 1 - cur;  // stage of step it + 1
+    if (it + 1 < ntiles) gload(it + 1, smem + nxt * G::STAGE);
 
     const int qs0 = tiles.pos0(it % nqt);
     const int qh = kvh * p.group + it / nqt;  // query head of this step
@@ -518,7 +439,7 @@ void bwd_dkdv_kernel(BwdParams p) {
           dp[i] = mfma32(b, vf[t], dp[i]);
         }
       }
-      sched_reads_ahead<2 * NQ * G::NKS, FA_DKDV_AHEAD>();
+      sched_reads_ahead<2 * NQ * G::NKS, kDkdvAhead>();
       // hide queries outside this lane's key band (before the key under
       // causal, outside the window, past the end).  Query of register r in
       // block qb is qs0 + g*4 + C(qb, r), C = qb*32 + (r/4)*8 + r%4; hidden
@@ -552,7 +473,7 @@ void bwd_dkdv_kernel(BwdParams p) {
         u32x4 kw;
         if constexpr (DROP)
           kw = drop_bytes_key_lanes(p.drop, (uint32_t)qh, kw0, qs0 + qb * 32,
-                                    smem + G::NST * G::STAGE + wave * kDropLdsPerWave, lane);
+                                    smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const f32x4 l4 = *(const f32x4*)(lsm + qb * 32 + rr * 8 + g * 4);
@@ -592,31 +513,22 @@ void bwd_dkdv_kernel(BwdParams p) {
       }
     };
     if (active) {
-      if constexpr (G::QBLK >= G::NQB) {
-        qblocks(std::integral_constant<int, 0>{}, std::integral_constant<int, G::NQB>{});
-      } else {
-        static_for<G::NQB / G::QBLK>([&](auto b) __attribute__((always_inline)) {
-          qblocks(std::integral_constant<int, decltype(b)::value * G::QBLK>{},
-                  std::integral_constant<int, G::QBLK>{});
-        });
-      }
+      qblocks(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+      qblocks(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
     }
-    if (it + 1 < ntiles) land_next(it + 2 < ntiles, smem + nxt * G::STAGE);
+    if (it + 1 < ntiles) land_next(smem + nxt * G::STAGE);
     __syncthreads();
   };
-  for (int it = 0; it < ntiles; it += G::NST) {
+  for (int it = 0; it < ntiles; it += 2) {
     step(it, std::integral_constant<int, 0>{});
     if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
-    if constexpr (G::NST > 2) {
-      if (it + 2 < ntiles) step(it + 2, std::integral_constant<int, 2>{});
-    }
   }
 
   // C layout: lane -> head-dim column, register -> key row.  Each wave turns
   // its 32 x D blocks of dK and dV into row-major order in LDS (the stages
   // are free once every wave has left the loop), then stores 16-byte pieces
   // of whole rows.
-  static_assert(4 * 2 * 32 * D * (int)sizeof(T) <= G::NST * G::STAGE, "epilogue fits the stages");
+  static_assert(4 * 2 * 32 * D * (int)sizeof(T) <= 2 * G::STAGE, "epilogue fits the stages");
   const float fk = DROP ? p.scale * p.drop.mult : p.scale;
   const float fv = DROP ? p.drop.mult : 1.f;
   __syncthreads();

@@ -26,22 +26,18 @@ namespace {
 
 constexpr float kDecTau = 8.0f;  // reference move threshold (base 2), as in the forward
 
-#ifndef FA_DEC_NST
-#define FA_DEC_NST 4  // LDS stages of the split kernel: one computed, the others in flight
-#endif
-#ifndef FA_DEC_WPE64
-#define FA_DEC_WPE64 2
-#endif
-#ifndef FA_DEC_WPE128
-#define FA_DEC_WPE128 2
-#endif
+// Split kernel: LDS stages (one computed, the others in flight) and waves per
+// SIMD.  Measured on MI355X: one to three tiles in flight and two or three
+// waves per SIMD ran the same (the kernel streams K and V near the HBM rate).
+constexpr int kDecStages = 4;
+constexpr int kDecWpe = 2;
 
 template <int D>
 struct DecGeom {
   static constexpr int KT = kDecKeys;          // keys per tile
-  static constexpr int NST = FA_DEC_NST;       // LDS stages: one computed, NST - 1 in flight
+  static constexpr int NST = kDecStages;       // LDS stages: one computed, NST - 1 in flight
   static_assert(NST >= 2, "at least one tile in flight");
-  static constexpr int WPE = D == 64 ? FA_DEC_WPE64 : FA_DEC_WPE128;  // waves per SIMD
+  static constexpr int WPE = kDecWpe;           // waves per SIMD
   static constexpr int KBYTES = KT * D * 2;    // K tile, swizzled
   static constexpr int VBYTES = KT * D * 2;    // V tile, swizzled
   static constexpr int STAGE = KBYTES + VBYTES;

@@ -1,11 +1,13 @@
 // fa_f32.hip -- float32 path (vector ALU, one query or one key per thread).
 //
-// float32 inputs have no matrix-core path that keeps float32 products on
-// gfx950, so this path computes in float32 on the vector units.  It follows the
-// same method as the matrix-core kernels -- key tiles staged in LDS, running
+// gfx950's matrix cores do take float32 operands (v_mfma_f32_32x32x2_f32 and
+// its 16x16x4 form), at about the rate of the packed float32 vector units; this
+// path nevertheless computes on the vector units on purpose: it serves small
+// float32 problems (a correctness workload, not a throughput one) and keeps the
+// plainest per-thread form of the method -- key tiles staged in LDS, running
 // row maximum and sum with rescaling, deferred normalisation, and a backward
-// that rebuilds P from Q, K and the LSE with D_i = dO_i . O_i -- in the plainest
-// per-thread form.  It serves small float32 problems; it is not tuned.
+// that rebuilds P from Q, K and the LSE with D_i = dO_i . O_i.  Visibility is
+// tested per (query, key) pair; no tile is skipped.  It is not tuned.
 #include <math.h>
 
 #include "fa_common.hpp"
