@@ -42,8 +42,11 @@ int check_problem(const fa_problem* p) {
   if (p->d != 64 && p->d != 128) return FA_ERR_UNSUPPORTED;
   // one head must be addressable with 32-bit byte offsets
   if ((int64_t)p->N * p->d * elem_bytes(p->dtype) > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
+  // workgroup counts (heads x 64-row tiles) must fit a 32-bit grid; both
+  // factors are below 2^31 here, so the product fits 64 bits
   const int64_t heads = (int64_t)p->B * p->H;
-  if (heads * ((p->N + 63) / 64) > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (heads > (int64_t)INT32_MAX || heads * ((p->N + 63) / 64) > (int64_t)INT32_MAX)
+    return FA_ERR_UNSUPPORTED;
   if (p->block_mask) {
     if (p->mask_block <= 0 || p->mask_block % 128 != 0) return FA_ERR_UNSUPPORTED;
     if (p->N % p->mask_block != 0) return FA_ERR_UNSUPPORTED;
