@@ -105,6 +105,39 @@ def lib() -> ctypes.CDLL:
     return L
 
 
+def use_library(path: str):
+    """Context manager: route the calls of this module through the library at
+    `path` (e.g. the debug build, ``build.LIB_DEBUG``) instead of the default
+    one, then restore it.  Not thread-safe."""
+    import contextlib
+
+    @contextlib.contextmanager
+    def _swap():
+        global _lib, LIB_PATH
+        saved = (_lib, LIB_PATH)
+        _lib, LIB_PATH = None, path
+        try:
+            yield lib()
+        finally:
+            _lib, LIB_PATH = saved
+
+    return _swap()
+
+
+def fa_debug_set_tile_visits(visits) -> None:
+    """Debug library only (include/fa_debug.h): later forward / backward calls
+    add their tile visits to `visits` (int32 GPU tensor of 3 * B*H * nb * nb,
+    nb = ceil(N / 128)); None clears."""
+    L = lib()
+    if not hasattr(L, "fa_debug_set_tile_visits"):
+        raise RuntimeError("fa_debug_set_tile_visits: not the debug library")
+    L.fa_debug_set_tile_visits.argtypes = [ctypes.c_void_p]
+    L.fa_debug_set_tile_visits.restype = ctypes.c_int
+    st = L.fa_debug_set_tile_visits(None if visits is None else visits.data_ptr())
+    if st != FA_OK:
+        raise FaError("fa_debug_set_tile_visits", st)
+
+
 def fa_status_string(status: int) -> str:
     return lib().fa_status_string(int(status)).decode()
 

@@ -1,6 +1,7 @@
 """Build libfa_mi355x.so (the HIP kernels and the C ABI) for gfx950.
 
-    python -m io_aware_exact_fwd_amd.build
+    python -m io_aware_exact_fwd_amd.build            # libfa_mi355x.so
+    python -m io_aware_exact_fwd_amd.build --debug    # libfa_mi355x_debug.so
 
 Compiles every ``csrc/*.hip`` with hipcc for --offload-arch=gfx950 (in
 parallel, objects under ``_build/``) and links the shared library next to this
@@ -20,6 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa_mi355x.so")
+# the debug build (include/fa_debug.h): NaN-filled LDS and tile-visit counters
+LIB_DEBUG = os.path.join(HERE, "libfa_mi355x_debug.so")
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled for all device code.
@@ -49,11 +52,15 @@ def _compile(src: str, hipcc: str, build_dir: str, defines) -> str:
     return obj
 
 
-def build(verbose: bool = True, defines=(), out: str = LIB) -> str:
+def build(verbose: bool = True, defines=(), out: str = LIB, debug: bool = False) -> str:
     """Compile and link; `defines` are extra preprocessor definitions passed
-    to every source, `out` the library path."""
+    to every source, `out` the library path; debug=True builds the debug
+    library (FA_DEBUG_BUILD=1) as libfa_mi355x_debug.so."""
     hipcc = _hipcc()
-    build_dir = BUILD if out == LIB else out + ".objs"
+    if debug:
+        defines = (*defines, "FA_DEBUG_BUILD=1")
+        out = LIB_DEBUG if out == LIB else out
+    build_dir = BUILD if out == LIB else (BUILD + "_debug" if out == LIB_DEBUG else out + ".objs")
     os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     workers = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "8"))))
@@ -71,5 +78,5 @@ def build(verbose: bool = True, defines=(), out: str = LIB) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(debug="--debug" in sys.argv[1:])
     sys.exit(0)

@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;
 
 // Size of the static scratch of fa_fwd_decode_noalloc (include/fa.h).
 constexpr size_t kScratchBytes = (size_t)64 << 20;
@@ -103,6 +103,11 @@ fa::DropParams drop_params(const fa_problem* p) {
   return d;
 }
 
+// Debug build only: the tile-visit counter array set by
+// fa_debug_set_tile_visits (see include/fa_debug.h); null in production.
+int32_t* g_debug_visits = nullptr;
+int32_t* debug_visits() { return fa::kDebugBuild ? g_debug_visits : nullptr; }
+
 fa::MaskLists no_lists() {
   fa::MaskLists m;
   m.row_ptr = m.col_idx = m.col_ptr = m.row_idx = nullptr;
@@ -168,6 +173,7 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
   f.c = c;
   f.m = no_lists();
   f.drop = drop_params(p);
+  f.visits = debug_visits();
   const bool masked = p->block_mask != nullptr;
   if (masked) {
     Lists l = carve_lists(p, (char*)workspace);
@@ -479,6 +485,7 @@ int bwd_setup(const fa_problem* p, const void* q, const void* k, const void* v, 
   b->scale = p->scale;
   b->m = no_lists();
   b->drop = drop_params(p);
+  b->visits = debug_visits();
   if (p->block_mask) b->m = mask_lists(p, carve_lists(p, (char*)workspace));
   return FA_OK;
 }
@@ -595,5 +602,12 @@ const char* fa_status_string(int status) {
 }
 
 int fa_version(void) { return kVersion; }
+
+#if FA_DEBUG_BUILD
+int fa_debug_set_tile_visits(int32_t* visits) {
+  g_debug_visits = visits;
+  return FA_OK;
+}
+#endif
 
 }  // extern "C"

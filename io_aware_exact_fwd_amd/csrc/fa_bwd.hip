@@ -80,6 +80,7 @@ void bwd_dq_kernel(BwdParams p) {
   using G = DqGeom<D>;
   using V8 = typename Vec8<T>::type;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
+  debug_fill_lds_nan(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,8 +138,11 @@ void bwd_dq_kernel(BwdParams p) {
   for (int i = 0; i < G::NDB; ++i) acc[i] = f32x16{0};
 
   // K and V tiles go straight from global memory to LDS
+  const int nb128 = (N + 127) / 128;
   auto gload = [&](int it, int stage) {
     const int k0 = tiles.pos0(it);
+    // debug build: counters of the dQ kernel follow the forward's
+    debug_visit(p.visits, ((size_t)(p.nheads + head) * p.ntiles + qt) * nb128 + k0 / 128, G::KT);
     char* ks = smem + stage * G::STAGE;
     dma_tile<D, G::KT>(bk, k0, ks, wave, lane);
     dma_tile<D, G::KT>(bv, k0, ks + G::KBYTES, wave, lane);
@@ -298,6 +302,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   // gradients' tolerance.
   constexpr bool kFoldD = D == 64 && !DROP;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
+  debug_fill_lds_nan(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -350,10 +355,14 @@ void bwd_dkdv_kernel(BwdParams p) {
   // wave 0, one row per lane (lanes past QT and rows past N read as zeros;
   // such rows are hidden by the masks).  The copies of step it + 1 are issued
   // at the start of step it.
+  const int nb128 = (N + 127) / 128;
   auto gload = [&](int it, char* st) {
     const int r = it / nqt;
     const int qs = tiles.pos0(it - r * nqt);
     const size_t qh = (size_t)kvh * p.group + r;  // query head
+    // debug build: counters of the dK/dV kernel follow those of the forward
+    // and the dQ kernel (B*H_kv*group = B*H query heads each)
+    debug_visit(p.visits, ((size_t)(2 * p.nheads * p.group + qh) * p.ntiles + kt) * nb128 + qs / 128, G::QT);
     const Buf bq = make_buf((const T*)p.q + qh * N * D, head_bytes);
     const Buf bdo = make_buf((const T*)p.dout + qh * N * D, head_bytes);
     dma_tile<D, G::QT>(bq, qs, st, wave, lane);

@@ -24,7 +24,18 @@
 #include <type_traits>
 #include <utility>
 
+// Debug build (libfa_mi355x_debug.so, compiled with FA_DEBUG_BUILD=1): each
+// tiled kernel fills its LDS with NaN before first use, so a read of LDS that
+// was never written shows up in the outputs, and the forward and backward
+// kernels count the tiles they load (see debug_visit).  The production library
+// compiles both to nothing.
+#ifndef FA_DEBUG_BUILD
+#define FA_DEBUG_BUILD 0
+#endif
+
 namespace fa {
+
+constexpr bool kDebugBuild = FA_DEBUG_BUILD != 0;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -345,6 +356,23 @@ constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Debug build: fill `bytes` of LDS at `lds` with a quiet NaN (every thread
+// of the workgroup calls it first thing; it ends with a barrier).
+__device__ __forceinline__ void debug_fill_lds_nan(char* lds, int bytes) {
+  if constexpr (kDebugBuild) {
+    for (int i = (int)threadIdx.x * 4; i < bytes; i += (int)blockDim.x * 4)
+      *(uint32_t*)(lds + i) = 0x7FC00000u;
+    __syncthreads();
+  }
+}
+
+// Debug build: add `amount` to visits[idx] once per workgroup (thread 0).
+__device__ __forceinline__ void debug_visit(int32_t* visits, size_t idx, int amount) {
+  if constexpr (kDebugBuild) {
+    if (visits != nullptr && threadIdx.x == 0) atomicAdd(visits + idx, amount);
+  }
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 }  // namespace fa

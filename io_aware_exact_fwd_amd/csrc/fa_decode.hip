@@ -53,6 +53,7 @@ void decode_split_kernel(DecParams p) {
   using G = DecGeom<D>;
   using V8 = typename Vec8<T>::type;
   __shared__ __attribute__((aligned(16))) char smem[G::NST * G::STAGE];
+  debug_fill_lds_nan(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

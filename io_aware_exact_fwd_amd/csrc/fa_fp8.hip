@@ -121,6 +121,7 @@ __global__ __launch_bounds__(128) void fp8_quant_kernel(Fp8QuantParams p) {
   constexpr int H = D / 2;       // values per lane
   __shared__ __attribute__((aligned(16))) char tile[64 * RB];
   __shared__ float wave_max[2];
+  debug_fill_lds_nan(tile, sizeof(tile));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_id();
@@ -281,6 +282,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 void fp8_fwd_kernel(Fp8FwdParams p) {
   using G = Fp8Geom<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
+  debug_fill_lds_nan(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -86,6 +86,7 @@ void fwd_kernel(FwdParams p) {
   using V8 = typename Vec8<T>::type;
   constexpr int BR = kFwdWaves * 32;  // query rows per workgroup
   __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? kFwdWaves * kDropLdsPerWave : 0)];
+  debug_fill_lds_nan(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,8 +131,10 @@ void fwd_kernel(FwdParams p) {
   float m_ref = kNegInf, ref = 0.f, l_run = kNoRef;
 
   // K and V tiles go straight from global memory to LDS
+  const int nb128 = (N + 127) / 128;
   auto gload = [&](int it, int stage) {
     const int k0 = tiles.pos0(it);
+    debug_visit(p.visits, ((size_t)head * p.nqt + qt) * nb128 + k0 / 128, G::KT);
     char* ks = smem + stage * G::STAGE;
     dma_tile<D, G::KT>(bk, k0, ks, wave, lane);
     dma_tile<D, G::KT>(bv, k0, ks + G::KBYTES, wave, lane);

@@ -46,6 +46,7 @@ struct FwdParams {
   float c;        // scale * log2(e)
   MaskLists m;
   DropParams drop;
+  int32_t* visits;  // debug build: tile-visit counters (see fa_debug_set_tile_visits), else null
 };
 
 struct BwdParams {
@@ -68,6 +69,7 @@ struct BwdParams {
   float scale;
   MaskLists m;
   DropParams drop;
+  int32_t* visits;  // debug build: tile-visit counters, else null
 };
 
 // Decode-shaped forward (fa_decode.hip): n_q queries per head at positions

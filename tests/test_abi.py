@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.fa_version() == 10400
+    assert B.fa_version() == 10500
     assert B.fa_status_string(0) == "ok"
     assert "workspace" in B.fa_status_string(B.FA_ERR_WORKSPACE)
     assert B.fa_status_string(12345) == "unknown status"
@@ -330,3 +330,18 @@ def test_decode_noalloc_checks_before_any_gpu_call():
     assert L.fa_fwd_decode_noalloc(ctypes.byref(big), 16, FAKE, FAKE, FAKE, FAKE, FAKE,
                                    None) == B.FA_ERR_SCRATCH
     assert "scratch" in B.fa_status_string(B.FA_ERR_SCRATCH)
+
+
+def test_debug_header_entry_only_in_debug_library():
+    """include/fa_debug.h declares what only the debug build exports."""
+    from io_aware_exact_fwd_amd.build import LIB_DEBUG
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "fa_debug.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["fa_debug_set_tile_visits"]
+    assert not hasattr(ctypes.CDLL(B.LIB_PATH), names[0])
+    if os.path.exists(LIB_DEBUG):
+        dbg = ctypes.CDLL(LIB_DEBUG)
+        for n in names + _declared_functions():
+            assert hasattr(dbg, n), n
