@@ -72,7 +72,7 @@ struct DqGeom {
   }
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
+template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP, bool PERSIST>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(DqGeom<D>::wpe(DROP, MASKED),
                                               DqGeom<D>::wpe(DROP, MASKED))))
@@ -82,191 +82,209 @@ void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
   debug_fill_lds_nan(smem, sizeof(smem));
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane_ = threadIdx.x & 63;
   const int wave = wave_id();
-  const int g = lane >> 5;
-  const int l32 = lane & 31;
-
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = logical / p.ntiles;
-  int qt = logical % p.ntiles;
-  if (CAUSAL) qt = p.ntiles - 1 - qt;
   const int N = p.N;
-  const int q0 = qt * kFwdRows;
-  const int qw0 = q0 + wave * 32;
-  const int q = qw0 + l32;
-  const int q_hi = min(q0 + kFwdRows, N) - 1;
 
-  const size_t head_off = (size_t)head * N * D;
-  const size_t kv_off = (size_t)(head / p.group) * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * sizeof(T);
-  const Buf bq = make_buf((const T*)p.q + head_off, head_bytes);
-  const Buf bk = make_buf((const T*)p.k + kv_off, head_bytes);
-  const Buf bv = make_buf((const T*)p.v + kv_off, head_bytes);
-  const Buf bo = make_buf((const T*)p.o + head_off, head_bytes);
-  const Buf bdo = make_buf((const T*)p.dout + head_off, head_bytes);
+  // one query tile of one head
+  auto tile = [&](const int head, const int qt) __attribute__((always_inline)) {
+    int lane = lane_;
+    // in the persistent loop, lane-only values are recomputed per tile rather
+    // than kept live across it (registers)
+    if constexpr (PERSIST) __asm__ volatile("" : "+v"(lane));
+    const int g = lane >> 5;
+    const int l32 = lane & 31;
+    const int q0 = qt * kFwdRows;
+    const int qw0 = q0 + wave * 32;
+    const int q = qw0 + l32;
+    const int q_hi = min(q0 + kFwdRows, N) - 1;
 
-  const Band band{N, p.window, CAUSAL};
-  const auto tiles = key_tiles<G::KT, MASKED>(p.m, band, q0, q_hi);
+    const size_t head_off = (size_t)head * N * D;
+    const size_t kv_off = (size_t)(head / p.group) * N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * sizeof(T);
+    const Buf bq = make_buf((const T*)p.q + head_off, head_bytes);
+    const Buf bk = make_buf((const T*)p.k + kv_off, head_bytes);
+    const Buf bv = make_buf((const T*)p.v + kv_off, head_bytes);
+    const Buf bo = make_buf((const T*)p.o + head_off, head_bytes);
+    const Buf bdo = make_buf((const T*)p.dout + head_off, head_bytes);
 
-  // Q and dO fragments (B operands, k = head dim); D_i = dO_i . O_i
-  V8 qf[G::NKS], dof[G::NKS];
-  float dpart = 0.f;
+    const Band band{N, p.window, CAUSAL};
+    const auto tiles = key_tiles<G::KT, MASKED>(p.m, band, q0, q_hi);
+
+    // Q and dO fragments (B operands, k = head dim); D_i = dO_i . O_i
+    V8 qf[G::NKS], dof[G::NKS];
+    float dpart = 0.f;
 #pragma unroll
-  for (int t = 0; t < G::NKS; ++t) {
-    const uint32_t off = (uint32_t)(q * D + t * 16 + g * 8) * sizeof(T);
-    qf[t] = __builtin_bit_cast(V8, buf_load16(bq, off));
-    dof[t] = __builtin_bit_cast(V8, buf_load16(bdo, off));
-    const V8 of = __builtin_bit_cast(V8, buf_load16(bo, off));
+    for (int t = 0; t < G::NKS; ++t) {
+      const uint32_t off = (uint32_t)(q * D + t * 16 + g * 8) * sizeof(T);
+      qf[t] = __builtin_bit_cast(V8, buf_load16(bq, off));
+      dof[t] = __builtin_bit_cast(V8, buf_load16(bdo, off));
+      const V8 of = __builtin_bit_cast(V8, buf_load16(bo, off));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dpart += to_f32(dof[t][i]) * to_f32(of[i]);
-  }
-  const float dq_d = pair_sum(dpart);
-  // Under dropout dS = mult * P o (keep o dP' - D / mult), dP' = dO V^T: the
-  // mask selects dP', and mult joins the scale of the finished dQ.
-  const float d_sub = DROP ? dq_d / p.drop.mult : dq_d;
-  float lse2 = __builtin_huge_valf();  // rows past the end or with no visible key: P = 0
-  if (q < N) {
-    const float lse = p.lse[(size_t)head * N + q];
-    if (lse != kNegInf) lse2 = lse * kLog2e;
-    if (g == 0) p.dvec[(size_t)head * N + q] = dq_d;
-  }
+      for (int i = 0; i < 8; ++i) dpart += to_f32(dof[t][i]) * to_f32(of[i]);
+    }
+    const float dq_d = pair_sum(dpart);
+    // Under dropout dS = mult * P o (keep o dP' - D / mult), dP' = dO V^T: the
+    // mask selects dP', and mult joins the scale of the finished dQ.
+    const float d_sub = DROP ? dq_d / p.drop.mult : dq_d;
+    float lse2 = __builtin_huge_valf();  // rows past the end or with no visible key: P = 0
+    if (q < N) {
+      const float lse = p.lse[(size_t)head * N + q];
+      if (lse != kNegInf) lse2 = lse * kLog2e;
+      if (g == 0) p.dvec[(size_t)head * N + q] = dq_d;
+    }
 
-  f32x16 acc[G::NDB];
+    f32x16 acc[G::NDB];
 #pragma unroll
-  for (int i = 0; i < G::NDB; ++i) acc[i] = f32x16{0};
+    for (int i = 0; i < G::NDB; ++i) acc[i] = f32x16{0};
 
-  // K and V tiles go straight from global memory to LDS
-  const int nb128 = (N + 127) / 128;
-  auto gload = [&](int it, int stage) {
-    const int k0 = tiles.pos0(it);
-    // debug build: counters of the dQ kernel follow the forward's
-    debug_visit(p.visits, ((size_t)(p.nheads + head) * p.ntiles + qt) * nb128 + k0 / 128, G::KT);
-    char* ks = smem + stage * G::STAGE;
-    dma_tile<D, G::KT>(bk, k0, ks, wave, lane);
-    dma_tile<D, G::KT>(bv, k0, ks + G::KBYTES, wave, lane);
-  };
+    // K and V tiles go straight from global memory to LDS
+    const int nb128 = (N + 127) / 128;
+    auto gload = [&](int it, int stage) {
+      const int k0 = tiles.pos0(it);
+      // debug build: counters of the dQ kernel follow the forward's
+      debug_visit(p.visits, ((size_t)(p.nheads + head) * p.ntiles + qt) * nb128 + k0 / 128, G::KT);
+      char* ks = smem + stage * G::STAGE;
+      dma_tile<D, G::KT>(bk, k0, ks, wave, lane);
+      dma_tile<D, G::KT>(bv, k0, ks + G::KBYTES, wave, lane);
+    };
 
-  const int ntiles = tiles.count;
-  if (ntiles > 0) gload(0, 0);
-  wait_all_memory();
-  __syncthreads();
+    const int ntiles = tiles.count;
+    if (ntiles > 0) gload(0, 0);
+    wait_all_memory();
+    __syncthreads();
 
-  const TileOffsets<D> toff(lane);
-  // The copies of tile it + 1 are issued at the start of step it, and a step
-  // ends once this thread's copies have landed.  One key tile per step; the
-  // LDS stage is a compile-time constant (two steps per iteration of the loop
-  // below), so it joins the reads' immediate offsets.
-  auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
-    constexpr int cur = decltype(stage)::value;
-    if (it + 1 < ntiles) gload(it + 1, 1 - cur);
+    const TileOffsets<D> toff(lane);
+    // The copies of tile it + 1 are issued at the start of step it, and a step
+    // ends once this thread's copies have landed.  One key tile per step; the
+    // LDS stage is a compile-time constant (two steps per iteration of the loop
+    // below), so it joins the reads' immediate offsets.
+    auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
+      constexpr int cur = decltype(stage)::value;
+      if (it + 1 < ntiles) gload(it + 1, 1 - cur);
 
-    const int k0 = tiles.pos0(it);
-    const char* ks = smem + cur * G::STAGE;
-    const char* vs = ks + G::KBYTES;
-    const int qw_last = qw0 + 31;
-    const bool active = k0 <= band.hi(qw_last) && k0 + G::KT - 1 >= band.lo(qw0);
-    // key halves KB0 .. KB0 + NKB - 1 of the tile: scores, dP, dS, then dQ
-    auto halves = [&](auto kb0_c, auto nkb_c) __attribute__((always_inline)) {
-      constexpr int KB0 = decltype(kb0_c)::value, NKB = decltype(nkb_c)::value;
-      static_assert(NKB == 1, "one 32-key half at a time");
-      // a half no row of the wave sees adds nothing (the later half of a
-      // causal diagonal tile)
-      if (k0 + KB0 * 32 > band.hi(qw_last) || k0 + KB0 * 32 + 31 < band.lo(qw0)) return;
-      f32x16 s[NKB], dp[NKB];
+      const int k0 = tiles.pos0(it);
+      const char* ks = smem + cur * G::STAGE;
+      const char* vs = ks + G::KBYTES;
+      const int qw_last = qw0 + 31;
+      const bool active = k0 <= band.hi(qw_last) && k0 + G::KT - 1 >= band.lo(qw0);
+      // key halves KB0 .. KB0 + NKB - 1 of the tile: scores, dP, dS, then dQ
+      auto halves = [&](auto kb0_c, auto nkb_c) __attribute__((always_inline)) {
+        constexpr int KB0 = decltype(kb0_c)::value, NKB = decltype(nkb_c)::value;
+        static_assert(NKB == 1, "one 32-key half at a time");
+        // a half no row of the wave sees adds nothing (the later half of a
+        // causal diagonal tile)
+        if (k0 + KB0 * 32 > band.hi(qw_last) || k0 + KB0 * 32 + 31 < band.lo(qw0)) return;
+        f32x16 s[NKB], dp[NKB];
 #pragma unroll
-      for (int i = 0; i < NKB; ++i) {
-        s[i] = f32x16{0};
-        dp[i] = f32x16{0};
+        for (int i = 0; i < NKB; ++i) {
+          s[i] = f32x16{0};
+          dp[i] = f32x16{0};
 #pragma unroll
-        for (int t = 0; t < G::NKS; ++t) {
-          const V8 a = toff.template row_operand<T>(ks, (KB0 + i) * 32, t);
-          s[i] = mfma32(a, qf[t], s[i]);
-          const V8 b = toff.template row_operand<T>(vs, (KB0 + i) * 32, t);
-          dp[i] = mfma32(b, dof[t], dp[i]);
+          for (int t = 0; t < G::NKS; ++t) {
+            const V8 a = toff.template row_operand<T>(ks, (KB0 + i) * 32, t);
+            s[i] = mfma32(a, qf[t], s[i]);
+            const V8 b = toff.template row_operand<T>(vs, (KB0 + i) * 32, t);
+            dp[i] = mfma32(b, dof[t], dp[i]);
+          }
         }
-      }
-      // hide keys outside the row's band (future, outside the window, past
-      // the end): key of register r is k0 + g*4 + C(kb, r) with
-      // C = kb*32 + (r/4)*8 + r%4; hidden iff C < lb or C > ub
-      // one compare-and-select per bound, each only where some row needs it
-      // (an OR of the two compares would route every element through the
-      // scalar unit)
-      if (k0 + KB0 * 32 + NKB * 32 - 1 > band.hi(qw0)) {
-        const int ub = band.hi(q) - k0 - g * 4;
+        // hide keys outside the row's band (future, outside the window, past
+        // the end): key of register r is k0 + g*4 + C(kb, r) with
+        // C = kb*32 + (r/4)*8 + r%4; hidden iff C < lb or C > ub
+        // one compare-and-select per bound, each only where some row needs it
+        // (an OR of the two compares would route every element through the
+        // scalar unit)
+        if (k0 + KB0 * 32 + NKB * 32 - 1 > band.hi(qw0)) {
+          const int ub = band.hi(q) - k0 - g * 4;
 #pragma unroll
-        for (int i = 0; i < NKB; ++i)
+          for (int i = 0; i < NKB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int C = (KB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
+              s[i][r] = C > ub ? kNegInf : s[i][r];
+            }
+        }
+        if (k0 + KB0 * 32 < band.lo(qw_last)) {
+          const int lb = band.lo(q) - k0 - g * 4;
+#pragma unroll
+          for (int i = 0; i < NKB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int C = (KB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
+              s[i][r] = C < lb ? kNegInf : s[i][r];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NKB; ++i) {
+          u32x4 kw;
+          if constexpr (DROP)
+            kw = drop_bytes_query_lanes(p.drop, (uint32_t)head, k0 + (KB0 + i) * 32, qw0,
+                                        smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int C = (KB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
-            s[i][r] = C > ub ? kNegInf : s[i][r];
+            const float pr = fast_exp2(__builtin_fmaf(s[i][r], p.c, -lse2));
+            float dpr = dp[i][r];
+            if constexpr (DROP) dpr = keep_byte(kw[r >> 2], r & 3, p.drop.t8) ? dpr : 0.f;
+            s[i][r] = pr * (dpr - d_sub);  // dS^T (scale applied to dQ at the end)
           }
-      }
-      if (k0 + KB0 * 32 < band.lo(qw_last)) {
-        const int lb = band.lo(q) - k0 - g * 4;
-#pragma unroll
-        for (int i = 0; i < NKB; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int C = (KB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
-            s[i][r] = C < lb ? kNegInf : s[i][r];
-          }
-      }
-#pragma unroll
-      for (int i = 0; i < NKB; ++i) {
-        u32x4 kw;
-        if constexpr (DROP)
-          kw = drop_bytes_query_lanes(p.drop, (uint32_t)head, k0 + (KB0 + i) * 32, qw0,
-                                      smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(__builtin_fmaf(s[i][r], p.c, -lse2));
-          float dpr = dp[i][r];
-          if constexpr (DROP) dpr = keep_byte(kw[r >> 2], r & 3, p.drop.t8) ? dpr : 0.f;
-          s[i][r] = pr * (dpr - d_sub);  // dS^T (scale applied to dQ at the end)
         }
-      }
-      // dQ^T += K^T dS^T : A = K^T via transpose reads of the K tile
-      V8 bs[2 * NKB];
+        // dQ^T += K^T dS^T : A = K^T via transpose reads of the K tile
+        V8 bs[2 * NKB];
 #pragma unroll
-      for (int t = 0; t < 2 * NKB; ++t) {
-        const int i = t >> 1, r0 = (t & 1) * 8;
-        bs[t] = pack8<T>(s[i][r0 + 0], s[i][r0 + 1], s[i][r0 + 2], s[i][r0 + 3],
-                         s[i][r0 + 4], s[i][r0 + 5], s[i][r0 + 6], s[i][r0 + 7]);
+        for (int t = 0; t < 2 * NKB; ++t) {
+          const int i = t >> 1, r0 = (t & 1) * 8;
+          bs[t] = pack8<T>(s[i][r0 + 0], s[i][r0 + 1], s[i][r0 + 2], s[i][r0 + 3],
+                           s[i][r0 + 4], s[i][r0 + 5], s[i][r0 + 6], s[i][r0 + 7]);
+        }
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+          for (int t = 0; t < 2 * NKB; ++t) {
+            const V8 a = toff.template tr_operand<T>(ks, (2 * KB0 + t) * 16, db);
+            acc[db] = mfma32(a, bs[t], acc[db]);
+          }
+      };
+      if (active) {
+        halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+        halves(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
       }
+      wait_all_memory();  // this thread's copies of tile it + 1 have landed
+      __syncthreads();
+    };
+    for (int it = 0; it < ntiles; it += 2) {
+      step(it, std::integral_constant<int, 0>{});
+      if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
+    }
+
+    if (q < N) {
+      T* row = (T*)p.dq + head_off + (size_t)q * D;
+      const float f = DROP ? p.scale * p.drop.mult : p.scale;
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
-        for (int t = 0; t < 2 * NKB; ++t) {
-          const V8 a = toff.template tr_operand<T>(ks, (2 * KB0 + t) * 16, db);
-          acc[db] = mfma32(a, bs[t], acc[db]);
+        for (int rr = 0; rr < 4; ++rr) {
+          u32x2 w;
+          w[0] = pack2<T>(acc[db][rr * 4 + 0] * f, acc[db][rr * 4 + 1] * f);
+          w[1] = pack2<T>(acc[db][rr * 4 + 2] * f, acc[db][rr * 4 + 3] * f);
+          *(u32x2*)(row + db * 32 + rr * 8 + g * 4) = w;
         }
-    };
-    if (active) {
-      halves(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-      halves(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
     }
-    wait_all_memory();  // this thread's copies of tile it + 1 have landed
-    __syncthreads();
   };
-  for (int it = 0; it < ntiles; it += 2) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
-  }
 
-  if (q < N) {
-    T* row = (T*)p.dq + head_off + (size_t)q * D;
-    const float f = DROP ? p.scale * p.drop.mult : p.scale;
-#pragma unroll
-    for (int db = 0; db < G::NDB; ++db)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        u32x2 w;
-        w[0] = pack2<T>(acc[db][rr * 4 + 0] * f, acc[db][rr * 4 + 1] * f);
-        w[1] = pack2<T>(acc[db][rr * 4 + 2] * f, acc[db][rr * 4 + 3] * f);
-        *(u32x2*)(row + db * 32 + rr * 8 + g * 4) = w;
-      }
+  if constexpr (PERSIST) {
+    // causal work units: the tile pair (ntiles - 1 - u, u) of a head, the
+    // longer rows first; every unit costs about the same
+    const int units = (p.ntiles + 1) / 2, total = p.nheads * units;
+    for (int b = blockIdx.x; b < total; b += gridDim.x) {
+      const int logical = xcd_remap(b, total);
+      const int head = logical / units, u = logical % units;
+      const int nsub = 2 * u + 1 != p.ntiles ? 2 : 1;
+      for (int e = 0; e < nsub; ++e) tile(head, e == 0 ? p.ntiles - 1 - u : u);
+    }
+  } else {
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int head = logical / p.ntiles, qt = logical % p.ntiles;
+    tile(head, CAUSAL ? p.ntiles - 1 - qt : qt);  // causal: the longer rows first
   }
 }
 
@@ -289,7 +307,7 @@ struct DkvGeom {
   }
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
+template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP, bool PERSIST>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(DkvGeom<D>::wpe(DROP), DkvGeom<D>::wpe(DROP))))
 void bwd_dkdv_kernel(BwdParams p) {
@@ -304,291 +322,328 @@ void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
   debug_fill_lds_nan(smem, sizeof(smem));
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane_ = threadIdx.x & 63;
   const int wave = wave_id();
-  const int g = lane >> 5;
-  const int l32 = lane & 31;
-
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int kvh = logical / p.ntiles;  // K/V head
-  const int kt = logical % p.ntiles;   // ascending: under causal, longest first
   const int N = p.N;
-  const int k0 = kt * kBwdKeys;
-  const int kw0 = k0 + wave * 32;
-  const int key = kw0 + l32;          // this lane's key
 
-  const size_t kv_off = (size_t)kvh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * sizeof(T);
-  const Buf bk = make_buf((const T*)p.k + kv_off, head_bytes);
-  const Buf bv = make_buf((const T*)p.v + kv_off, head_bytes);
+  // one key tile of one K/V head
+  auto tile = [&](const int kvh, const int kt) __attribute__((always_inline)) {
+    int lane = lane_;
+    // in the persistent loop, lane-only values are recomputed per tile rather
+    // than kept live across it (registers)
+    if constexpr (PERSIST) __asm__ volatile("" : "+v"(lane));
+    const int g = lane >> 5;
+    const int l32 = lane & 31;
+    const int k0 = kt * kBwdKeys;
+    const int kw0 = k0 + wave * 32;
+    const int key = kw0 + l32;          // this lane's key
 
-  // The same query tiles are visited for each of the `group` query heads that
-  // read this K/V head; iteration it covers head it / nqt, tile it % nqt, and
-  // dK, dV sum over all of them in registers.
-  const Band band{N, p.window, CAUSAL};
-  const auto tiles = query_tiles<G::QT, MASKED>(p.m, band, k0, k0 + kBwdKeys - 1);
-  const int nqt = tiles.count;
+    const size_t kv_off = (size_t)kvh * N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * sizeof(T);
+    const Buf bk = make_buf((const T*)p.k + kv_off, head_bytes);
+    const Buf bv = make_buf((const T*)p.v + kv_off, head_bytes);
 
-  // K and V fragments: B operands of S = Q K^T and dP = dO V^T (k = head dim)
-  V8 kf[G::NKS], vf[G::NKS];
+    // The same query tiles are visited for each of the `group` query heads that
+    // read this K/V head; iteration it covers head it / nqt, tile it % nqt, and
+    // dK, dV sum over all of them in registers.
+    const Band band{N, p.window, CAUSAL};
+    const auto tiles = query_tiles<G::QT, MASKED>(p.m, band, k0, k0 + kBwdKeys - 1);
+    const int nqt = tiles.count;
+
+    // K and V fragments: B operands of S = Q K^T and dP = dO V^T (k = head dim)
+    V8 kf[G::NKS], vf[G::NKS];
 #pragma unroll
-  for (int t = 0; t < G::NKS; ++t) {
-    const uint32_t off = (uint32_t)(key * D + t * 16 + g * 8) * sizeof(T);
-    kf[t] = __builtin_bit_cast(V8, buf_load16(bk, off));
-    vf[t] = __builtin_bit_cast(V8, buf_load16(bv, off));
-  }
-  // Wait for these here: the copies below are invisible to the compiler's
-  // own wait counting, which would otherwise wait inside the loop for loads
-  // it still thinks pending -- and, counts being in issue order, for the
-  // prefetch copies issued after them.
-  wait_all_memory();
-  f32x16 dka[G::NDB], dva[G::NDB];
-#pragma unroll
-  for (int i = 0; i < G::NDB; ++i) {
-    dka[i] = f32x16{0};
-    dva[i] = f32x16{0};
-  }
-
-  // Q, dO, LSE and D of a step go straight from global memory to LDS (no
-  // registers, no store instructions): Q and dO by all waves, LSE and D by
-  // wave 0, one row per lane (lanes past QT and rows past N read as zeros;
-  // such rows are hidden by the masks).  The copies of step it + 1 are issued
-  // at the start of step it.
-  const int nb128 = (N + 127) / 128;
-  auto gload = [&](int it, char* st) {
-    const int r = it / nqt;
-    const int qs = tiles.pos0(it - r * nqt);
-    const size_t qh = (size_t)kvh * p.group + r;  // query head
-    // debug build: counters of the dK/dV kernel follow those of the forward
-    // and the dQ kernel (B*H_kv*group = B*H query heads each)
-    debug_visit(p.visits, ((size_t)(2 * p.nheads * p.group + qh) * p.ntiles + kt) * nb128 + qs / 128, G::QT);
-    const Buf bq = make_buf((const T*)p.q + qh * N * D, head_bytes);
-    const Buf bdo = make_buf((const T*)p.dout + qh * N * D, head_bytes);
-    dma_tile<D, G::QT>(bq, qs, st, wave, lane);
-    dma_tile<D, G::QT>(bdo, qs, st + G::TBYTES, wave, lane);
-    if (wave == 0) {
-      const Buf bl = make_buf(p.lse + qh * N, (uint32_t)N * 4);
-      const Buf bd = make_buf(p.dvec + qh * N, (uint32_t)N * 4);
-      const uint32_t off = (uint32_t)(qs + lane) * 4;
-      dma4(bl, off, st + 2 * G::TBYTES);
-      dma4(bd, off, st + 2 * G::TBYTES + G::LBYTES);
+    for (int t = 0; t < G::NKS; ++t) {
+      const uint32_t off = (uint32_t)(key * D + t * 16 + g * 8) * sizeof(T);
+      kf[t] = __builtin_bit_cast(V8, buf_load16(bk, off));
+      vf[t] = __builtin_bit_cast(V8, buf_load16(bv, off));
     }
-  };
-  // Wait until this wave's copies of the next step have landed, then wave 0
-  // converts that step's rows
-  // in place: LSE -> LSE log2(e) (+inf for a row with no visible key, so P =
-  // 0), D -> D / mult under dropout (see the dS step), D -> -D where the dP
-  // accumulators start from it.  The barrier that follows publishes the stage.
-  auto land_next = [&](char* st) {
+    // Wait for these here: the copies below are invisible to the compiler's
+    // own wait counting, which would otherwise wait inside the loop for loads
+    // it still thinks pending -- and, counts being in issue order, for the
+    // prefetch copies issued after them.
     wait_all_memory();
-    if (wave == 0) {
-      float* ls = (float*)(st + 2 * G::TBYTES);
-      float* ds = (float*)(st + 2 * G::TBYTES + G::LBYTES);
+    f32x16 dka[G::NDB], dva[G::NDB];
 #pragma unroll
-      for (int i = lane; i < G::QT; i += 64) {
-        const float l = ls[i];
-        ls[i] = l != kNegInf ? l * kLog2e : __builtin_huge_valf();
-        if constexpr (DROP) ds[i] = ds[i] / p.drop.mult;
-        if constexpr (kFoldD) ds[i] = -ds[i];  // dP accumulators start here
-      }
+    for (int i = 0; i < G::NDB; ++i) {
+      dka[i] = f32x16{0};
+      dva[i] = f32x16{0};
     }
-  };
 
-  const int ntiles = nqt * p.group;
-  if (ntiles > 0) gload(0, smem);
-  land_next(smem);
-  __syncthreads();
-
-  const TileOffsets<D> toff(lane);
-  // one query step; its LDS stage (it mod 2) is a compile-time constant (two
-  // steps per iteration of the loop below), so stage addresses join the
-  // reads' immediate offsets
-  auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
-    constexpr int cur = decltype(stage)::value;
-    constexpr int nxt = 1 - cur;  // stage of step it + 1
-    if (it + 1 < ntiles) gload(it + 1, smem + nxt * G::STAGE);
-
-    const int qs0 = tiles.pos0(it % nqt);
-    const int qh = kvh * p.group + it / nqt;  // query head of this step
-    const char* qsm = smem + cur * G::STAGE;
-    const char* dsm = qsm + G::TBYTES;
-    const float* lsm = (const float*)(dsm + G::TBYTES);
-    // the wave's keys [kw0, kw_last] are seen by queries [qlo(kw0), qhi(kw_last)]
-    // between them, and by all of them in [qlo(kw_last), qhi(kw0)]
-    const int kw_last = kw0 + 31;
-    const bool active = qs0 <= band.qhi(kw_last) && qs0 + G::QT - 1 >= band.qlo(kw0);
-    // 32-query blocks QB0 .. QB0 + NQ - 1 of the step: scores, dP, softmax,
-    // dS, then their dV and dK products
-    auto qblocks = [&](auto qb0_c, auto nq_c) __attribute__((always_inline)) {
-      constexpr int QB0 = decltype(qb0_c)::value, NQ = decltype(nq_c)::value;
-      const int qa = qs0 + QB0 * 32, qz = qa + NQ * 32 - 1;  // the blocks' queries
-      // blocks that see none of the wave's keys add nothing
-      if (NQ < G::NQB && (qa > band.qhi(kw_last) || qz < band.qlo(kw0))) return;
-      f32x16 s[NQ], dp[NQ];
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        s[i] = f32x16{0};
-        if constexpr (kFoldD) {
-          // register r of a block holds query row 8 (r / 4) + 4 g + r % 4
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const f32x4 d4 = *(const f32x4*)(lsm + G::LBYTES / 4 + (QB0 + i) * 32 + rr * 8 + g * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dp[i][rr * 4 + e] = d4[e];
-          }
-        } else {
-          dp[i] = f32x16{0};
-        }
-#pragma unroll
-        for (int t = 0; t < G::NKS; ++t) {
-          const V8 a = toff.template row_operand<T>(qsm, (QB0 + i) * 32, t);
-          s[i] = mfma32(a, kf[t], s[i]);
-          const V8 b = toff.template row_operand<T>(dsm, (QB0 + i) * 32, t);
-          dp[i] = mfma32(b, vf[t], dp[i]);
-        }
+    // Q, dO, LSE and D of a step go straight from global memory to LDS (no
+    // registers, no store instructions): Q and dO by all waves, LSE and D by
+    // wave 0, one row per lane (lanes past QT and rows past N read as zeros;
+    // such rows are hidden by the masks).  The copies of step it + 1 are issued
+    // at the start of step it.
+    const int nb128 = (N + 127) / 128;
+    auto gload = [&](int it, char* st) {
+      const int r = it / nqt;
+      const int qs = tiles.pos0(it - r * nqt);
+      const size_t qh = (size_t)kvh * p.group + r;  // query head
+      // debug build: counters of the dK/dV kernel follow those of the forward
+      // and the dQ kernel (B*H_kv*group = B*H query heads each)
+      debug_visit(p.visits, ((size_t)(2 * p.nheads * p.group + qh) * p.ntiles + kt) * nb128 + qs / 128, G::QT);
+      const Buf bq = make_buf((const T*)p.q + qh * N * D, head_bytes);
+      const Buf bdo = make_buf((const T*)p.dout + qh * N * D, head_bytes);
+      dma_tile<D, G::QT>(bq, qs, st, wave, lane);
+      dma_tile<D, G::QT>(bdo, qs, st + G::TBYTES, wave, lane);
+      if (wave == 0) {
+        const Buf bl = make_buf(p.lse + qh * N, (uint32_t)N * 4);
+        const Buf bd = make_buf(p.dvec + qh * N, (uint32_t)N * 4);
+        const uint32_t off = (uint32_t)(qs + lane) * 4;
+        dma4(bl, off, st + 2 * G::TBYTES);
+        dma4(bd, off, st + 2 * G::TBYTES + G::LBYTES);
       }
-      sched_reads_ahead<2 * NQ * G::NKS, kDkdvAhead>();
-      // hide queries outside this lane's key band (before the key under
-      // causal, outside the window, past the end).  Query of register r in
-      // block qb is qs0 + g*4 + C(qb, r), C = qb*32 + (r/4)*8 + r%4; hidden
-      // iff C < lb or C > ub
-      if (qa < band.qlo(kw_last)) {
-        const int lb = band.qlo(key) - qs0 - g * 4;
+    };
+    // Wait until this wave's copies of the next step have landed, then wave 0
+    // converts that step's rows
+    // in place: LSE -> LSE log2(e) (+inf for a row with no visible key, so P =
+    // 0), D -> D / mult under dropout (see the dS step), D -> -D where the dP
+    // accumulators start from it.  The barrier that follows publishes the stage.
+    auto land_next = [&](char* st) {
+      wait_all_memory();
+      if (wave == 0) {
+        float* ls = (float*)(st + 2 * G::TBYTES);
+        float* ds = (float*)(st + 2 * G::TBYTES + G::LBYTES);
 #pragma unroll
-        for (int i = 0; i < NQ; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int C = (QB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
-            s[i][r] = C < lb ? kNegInf : s[i][r];
-          }
-      }
-      if (qz > band.qhi(kw0)) {
-        const int ub = band.qhi(key) - qs0 - g * 4;
-#pragma unroll
-        for (int i = 0; i < NQ; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int C = (QB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
-            s[i][r] = C > ub ? kNegInf : s[i][r];
-          }
-      }
-      // Under dropout (keep mask Z01, scale mult): dV = mult (Z01 o P)^T dO and
-      // dS = mult * P o (Z01 o dP' - D / mult); both mult factors join the
-      // finished dV and dK, and the D loaded with the tile is already / mult.
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const int qb = QB0 + i;
-        u32x4 kw;
-        if constexpr (DROP)
-          kw = drop_bytes_key_lanes(p.drop, (uint32_t)qh, kw0, qs0 + qb * 32,
-                                    smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const f32x4 l4 = *(const f32x4*)(lsm + qb * 32 + rr * 8 + g * 4);
-          f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
-          if (!kFoldD) d4 = *(const f32x4*)(lsm + G::LBYTES / 4 + qb * 32 + rr * 8 + g * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = rr * 4 + e;
-            const float pr = fast_exp2(__builtin_fmaf(s[i][r], p.c, -l4[e]));
-            if constexpr (DROP) {
-              const bool keep = keep_byte(kw[rr], e, p.drop.t8);
-              s[i][r] = keep ? pr : 0.f;                             // Z01 o P
-              dp[i][r] = pr * ((keep ? dp[i][r] : 0.f) - d4[e]);  // dS / mult
-            } else {
-              s[i][r] = pr;  // P
-              // dS (scale applied to dK at the end); dp may already hold dP - D
-              dp[i][r] = kFoldD ? pr * dp[i][r] : pr * (dp[i][r] - d4[e]);
-            }
-          }
-        }
-      }
-      // dV += P^T dO,  dK += dS^T Q ; k-step t covers queries 16t .. 16t+15
-#pragma unroll
-      for (int t = 0; t < 2 * NQ; ++t) {
-        const int i = t >> 1, r0 = (t & 1) * 8;
-        const V8 ap = pack8<T>(s[i][r0 + 0], s[i][r0 + 1], s[i][r0 + 2], s[i][r0 + 3],
-                               s[i][r0 + 4], s[i][r0 + 5], s[i][r0 + 6], s[i][r0 + 7]);
-        const V8 ad = pack8<T>(dp[i][r0 + 0], dp[i][r0 + 1], dp[i][r0 + 2], dp[i][r0 + 3],
-                               dp[i][r0 + 4], dp[i][r0 + 5], dp[i][r0 + 6], dp[i][r0 + 7]);
-#pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
-          const V8 bdo_ = toff.template tr_operand<T>(dsm, (2 * QB0 + t) * 16, db);
-          dva[db] = mfma32(ap, bdo_, dva[db]);
-          const V8 bq_ = toff.template tr_operand<T>(qsm, (2 * QB0 + t) * 16, db);
-          dka[db] = mfma32(ad, bq_, dka[db]);
+        for (int i = lane; i < G::QT; i += 64) {
+          const float l = ls[i];
+          ls[i] = l != kNegInf ? l * kLog2e : __builtin_huge_valf();
+          if constexpr (DROP) ds[i] = ds[i] / p.drop.mult;
+          if constexpr (kFoldD) ds[i] = -ds[i];  // dP accumulators start here
         }
       }
     };
-    if (active) {
-      qblocks(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-      qblocks(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
-    }
-    if (it + 1 < ntiles) land_next(smem + nxt * G::STAGE);
-    __syncthreads();
-  };
-  for (int it = 0; it < ntiles; it += 2) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
-  }
 
-  // C layout: lane -> head-dim column, register -> key row.  Each wave turns
-  // its 32 x D blocks of dK and dV into row-major order in LDS (the stages
-  // are free once every wave has left the loop), then stores 16-byte pieces
-  // of whole rows.
-  static_assert(4 * 2 * 32 * D * (int)sizeof(T) <= 2 * G::STAGE, "epilogue fits the stages");
-  const float fk = DROP ? p.scale * p.drop.mult : p.scale;
-  const float fv = DROP ? p.drop.mult : 1.f;
-  __syncthreads();
-  T* ek = (T*)(smem + wave * 2 * 32 * D * sizeof(T));
-  T* ev = ek + 32 * D;
+    const int ntiles = nqt * p.group;
+    if (ntiles > 0) gload(0, smem);
+    land_next(smem);
+    __syncthreads();
+
+    const TileOffsets<D> toff(lane);
+    // one query step; its LDS stage (it mod 2) is a compile-time constant (two
+    // steps per iteration of the loop below), so stage addresses join the
+    // reads' immediate offsets
+    auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
+      constexpr int cur = decltype(stage)::value;
+      constexpr int nxt = 1 - cur;  // stage of step it + 1
+      if (it + 1 < ntiles) gload(it + 1, smem + nxt * G::STAGE);
+
+      const int qs0 = tiles.pos0(it % nqt);
+      const int qh = kvh * p.group + it / nqt;  // query head of this step
+      const char* qsm = smem + cur * G::STAGE;
+      const char* dsm = qsm + G::TBYTES;
+      const float* lsm = (const float*)(dsm + G::TBYTES);
+      // the wave's keys [kw0, kw_last] are seen by queries [qlo(kw0), qhi(kw_last)]
+      // between them, and by all of them in [qlo(kw_last), qhi(kw0)]
+      const int kw_last = kw0 + 31;
+      const bool active = qs0 <= band.qhi(kw_last) && qs0 + G::QT - 1 >= band.qlo(kw0);
+      // 32-query blocks QB0 .. QB0 + NQ - 1 of the step: scores, dP, softmax,
+      // dS, then their dV and dK products
+      auto qblocks = [&](auto qb0_c, auto nq_c) __attribute__((always_inline)) {
+        constexpr int QB0 = decltype(qb0_c)::value, NQ = decltype(nq_c)::value;
+        const int qa = qs0 + QB0 * 32, qz = qa + NQ * 32 - 1;  // the blocks' queries
+        // blocks that see none of the wave's keys add nothing
+        if (NQ < G::NQB && (qa > band.qhi(kw_last) || qz < band.qlo(kw0))) return;
+        f32x16 s[NQ], dp[NQ];
 #pragma unroll
-  for (int db = 0; db < G::NDB; ++db)
+        for (int i = 0; i < NQ; ++i) {
+          s[i] = f32x16{0};
+          if constexpr (kFoldD) {
+            // register r of a block holds query row 8 (r / 4) + 4 g + r % 4
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = (r >> 2) * 8 + g * 4 + (r & 3);
-      ek[row * D + db * 32 + l32] = (T)(dka[db][r] * fk);
-      ev[row * D + db * 32 + l32] = (T)(dva[db][r] * fv);
+            for (int rr = 0; rr < 4; ++rr) {
+              const f32x4 d4 = *(const f32x4*)(lsm + G::LBYTES / 4 + (QB0 + i) * 32 + rr * 8 + g * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dp[i][rr * 4 + e] = d4[e];
+            }
+          } else {
+            dp[i] = f32x16{0};
+          }
+#pragma unroll
+          for (int t = 0; t < G::NKS; ++t) {
+            const V8 a = toff.template row_operand<T>(qsm, (QB0 + i) * 32, t);
+            s[i] = mfma32(a, kf[t], s[i]);
+            const V8 b = toff.template row_operand<T>(dsm, (QB0 + i) * 32, t);
+            dp[i] = mfma32(b, vf[t], dp[i]);
+          }
+        }
+        sched_reads_ahead<2 * NQ * G::NKS, kDkdvAhead>();
+        // hide queries outside this lane's key band (before the key under
+        // causal, outside the window, past the end).  Query of register r in
+        // block qb is qs0 + g*4 + C(qb, r), C = qb*32 + (r/4)*8 + r%4; hidden
+        // iff C < lb or C > ub
+        if (qa < band.qlo(kw_last)) {
+          const int lb = band.qlo(key) - qs0 - g * 4;
+#pragma unroll
+          for (int i = 0; i < NQ; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int C = (QB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
+              s[i][r] = C < lb ? kNegInf : s[i][r];
+            }
+        }
+        if (qz > band.qhi(kw0)) {
+          const int ub = band.qhi(key) - qs0 - g * 4;
+#pragma unroll
+          for (int i = 0; i < NQ; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int C = (QB0 + i) * 32 + (r >> 2) * 8 + (r & 3);
+              s[i][r] = C > ub ? kNegInf : s[i][r];
+            }
+        }
+        // Under dropout (keep mask Z01, scale mult): dV = mult (Z01 o P)^T dO and
+        // dS = mult * P o (Z01 o dP' - D / mult); both mult factors join the
+        // finished dV and dK, and the D loaded with the tile is already / mult.
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          const int qb = QB0 + i;
+          u32x4 kw;
+          if constexpr (DROP)
+            kw = drop_bytes_key_lanes(p.drop, (uint32_t)qh, kw0, qs0 + qb * 32,
+                                      smem + 2 * G::STAGE + wave * kDropLdsPerWave, lane);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const f32x4 l4 = *(const f32x4*)(lsm + qb * 32 + rr * 8 + g * 4);
+            f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+            if (!kFoldD) d4 = *(const f32x4*)(lsm + G::LBYTES / 4 + qb * 32 + rr * 8 + g * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = rr * 4 + e;
+              const float pr = fast_exp2(__builtin_fmaf(s[i][r], p.c, -l4[e]));
+              if constexpr (DROP) {
+                const bool keep = keep_byte(kw[rr], e, p.drop.t8);
+                s[i][r] = keep ? pr : 0.f;                             // Z01 o P
+                dp[i][r] = pr * ((keep ? dp[i][r] : 0.f) - d4[e]);  // dS / mult
+              } else {
+                s[i][r] = pr;  // P
+                // dS (scale applied to dK at the end); dp may already hold dP - D
+                dp[i][r] = kFoldD ? pr * dp[i][r] : pr * (dp[i][r] - d4[e]);
+              }
+            }
+          }
+        }
+        // dV += P^T dO,  dK += dS^T Q ; k-step t covers queries 16t .. 16t+15
+#pragma unroll
+        for (int t = 0; t < 2 * NQ; ++t) {
+          const int i = t >> 1, r0 = (t & 1) * 8;
+          const V8 ap = pack8<T>(s[i][r0 + 0], s[i][r0 + 1], s[i][r0 + 2], s[i][r0 + 3],
+                                 s[i][r0 + 4], s[i][r0 + 5], s[i][r0 + 6], s[i][r0 + 7]);
+          const V8 ad = pack8<T>(dp[i][r0 + 0], dp[i][r0 + 1], dp[i][r0 + 2], dp[i][r0 + 3],
+                                 dp[i][r0 + 4], dp[i][r0 + 5], dp[i][r0 + 6], dp[i][r0 + 7]);
+#pragma unroll
+          for (int db = 0; db < G::NDB; ++db) {
+            const V8 bdo_ = toff.template tr_operand<T>(dsm, (2 * QB0 + t) * 16, db);
+            dva[db] = mfma32(ap, bdo_, dva[db]);
+            const V8 bq_ = toff.template tr_operand<T>(qsm, (2 * QB0 + t) * 16, db);
+            dka[db] = mfma32(ad, bq_, dka[db]);
+          }
+        }
+      };
+      if (active) {
+        qblocks(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+        qblocks(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+      }
+      if (it + 1 < ntiles) land_next(smem + nxt * G::STAGE);
+      __syncthreads();
+    };
+    for (int it = 0; it < ntiles; it += 2) {
+      step(it, std::integral_constant<int, 0>{});
+      if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
     }
-  __syncthreads();
-  constexpr int CPR = D / 8;  // 16-byte pieces per row
+
+    // C layout: lane -> head-dim column, register -> key row.  Each wave turns
+    // its 32 x D blocks of dK and dV into row-major order in LDS (the stages
+    // are free once every wave has left the loop), then stores 16-byte pieces
+    // of whole rows.
+    static_assert(4 * 2 * 32 * D * (int)sizeof(T) <= 2 * G::STAGE, "epilogue fits the stages");
+    const float fk = DROP ? p.scale * p.drop.mult : p.scale;
+    const float fv = DROP ? p.drop.mult : 1.f;
+    __syncthreads();
+    T* ek = (T*)(smem + wave * 2 * 32 * D * sizeof(T));
+    T* ev = ek + 32 * D;
 #pragma unroll
-  for (int i = 0; i < 32 * CPR / 64; ++i) {
-    const int c = i * 64 + lane, row = c / CPR, piece = c % CPR;
-    if (kw0 + row < N) {
-      const size_t idx = kv_off + (size_t)(kw0 + row) * D + piece * 8;
-      *(u32x4*)((T*)p.dk + idx) = *(const u32x4*)(ek + row * D + piece * 8);
-      *(u32x4*)((T*)p.dv + idx) = *(const u32x4*)(ev + row * D + piece * 8);
+    for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (r >> 2) * 8 + g * 4 + (r & 3);
+        ek[row * D + db * 32 + l32] = (T)(dka[db][r] * fk);
+        ev[row * D + db * 32 + l32] = (T)(dva[db][r] * fv);
+      }
+    __syncthreads();
+    constexpr int CPR = D / 8;  // 16-byte pieces per row
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+      const int c = i * 64 + lane, row = c / CPR, piece = c % CPR;
+      if (kw0 + row < N) {
+        const size_t idx = kv_off + (size_t)(kw0 + row) * D + piece * 8;
+        *(u32x4*)((T*)p.dk + idx) = *(const u32x4*)(ek + row * D + piece * 8);
+        *(u32x4*)((T*)p.dv + idx) = *(const u32x4*)(ev + row * D + piece * 8);
+      }
     }
+    // the next tile's copies overwrite the LDS this epilogue reads
+    if constexpr (PERSIST) __syncthreads();
+  };
+
+  if constexpr (PERSIST) {
+    // causal work units: the tile pair (u, ntiles - 1 - u) of a K/V head, the
+    // longer columns first; every unit costs about the same
+    const int units = (p.ntiles + 1) / 2, total = p.nheads * units;
+    for (int b = blockIdx.x; b < total; b += gridDim.x) {
+      const int logical = xcd_remap(b, total);
+      const int kvh = logical / units, u = logical % units;
+      const int nsub = 2 * u + 1 != p.ntiles ? 2 : 1;
+      for (int e = 0; e < nsub; ++e) tile(kvh, e == 0 ? u : p.ntiles - 1 - u);
+    }
+  } else {
+    // in order: under causal masking the longer columns first
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    tile(logical / p.ntiles, logical % p.ntiles);
   }
 }
 
 template <typename T, int D, bool DROP>
 static hipError_t launch_dq_t(const BwdParams& p, bool causal, bool masked, hipStream_t s) {
-  dim3 grid(p.nheads * p.ntiles), block(kThreads);
+  const int units = p.nheads * p.ntiles;
+  // causal work without a window or block mask runs on a persistent grid over
+  // tile pairs (not under dropout at head dim 64: the unit loop's registers
+  // would spill); the rest one workgroup per tile
+  if constexpr (!(DROP && D == 64))
+    if (causal && !masked && p.window == 0) {
+      launch_units<bwd_dq_kernel<T, D, true, false, DROP, true>>(p, p.nheads * ((p.ntiles + 1) / 2), true, s);
+      return hipGetLastError();
+    }
   if (causal && masked)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, true, DROP>), grid, block, 0, s, p);
+    launch_units<bwd_dq_kernel<T, D, true, true, DROP, false>>(p, units, false, s);
   else if (causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, false, DROP>), grid, block, 0, s, p);
+    launch_units<bwd_dq_kernel<T, D, true, false, DROP, false>>(p, units, false, s);
   else if (masked)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, true, DROP>), grid, block, 0, s, p);
+    launch_units<bwd_dq_kernel<T, D, false, true, DROP, false>>(p, units, false, s);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, false, DROP>), grid, block, 0, s, p);
+    launch_units<bwd_dq_kernel<T, D, false, false, DROP, false>>(p, units, false, s);
   return hipGetLastError();
 }
 
 template <typename T, int D, bool DROP>
 static hipError_t launch_dkdv_t(const BwdParams& p, bool causal, bool masked, hipStream_t s) {
-  dim3 grid(p.nheads * p.ntiles), block(kThreads);
+  const int units = p.nheads * p.ntiles;
+  // causal work without a window or block mask runs on a persistent grid over
+  // tile pairs at head dim 64 (at 128, one wave per SIMD, one workgroup per
+  // tile measured faster); the rest one workgroup per tile
+  if constexpr (D == 64)
+    if (causal && !masked && p.window == 0) {
+      launch_units<bwd_dkdv_kernel<T, D, true, false, DROP, true>>(p, p.nheads * ((p.ntiles + 1) / 2), true, s);
+      return hipGetLastError();
+    }
   if (causal && masked)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, true, DROP>), grid, block, 0, s, p);
+    launch_units<bwd_dkdv_kernel<T, D, true, true, DROP, false>>(p, units, false, s);
   else if (causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, false, DROP>), grid, block, 0, s, p);
+    launch_units<bwd_dkdv_kernel<T, D, true, false, DROP, false>>(p, units, false, s);
   else if (masked)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, true, DROP>), grid, block, 0, s, p);
+    launch_units<bwd_dkdv_kernel<T, D, false, true, DROP, false>>(p, units, false, s);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, false, DROP>), grid, block, 0, s, p);
+    launch_units<bwd_dkdv_kernel<T, D, false, false, DROP, false>>(p, units, false, s);
   return hipGetLastError();
 }
 

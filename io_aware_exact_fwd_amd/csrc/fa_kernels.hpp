@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fa {
 
 // Tile geometry of the matrix-core kernels.
@@ -159,6 +161,53 @@ struct F32Params {
 };
 
 // Each launcher returns hipSuccess or the launch error.
+// ---- persistent grids ----------------------------------------------------------
+// The forward and backward kernels launch at most as many workgroups as the GPU
+// holds at once; each walks a static list of work units (unit b of the
+// head-major order goes to workgroup b mod grid).  One workgroup per unit
+// leaves CUs idle between workgroups: the dispatcher hands them out in order,
+// one XCD after the other, and a workgroup whose XCD is full holds back all
+// later ones.
+// Compute units of the current device (cached per device; 1 if the query
+// fails, which only narrows the grid).
+inline int cu_count() {
+  constexpr int kDevices = 64;
+  static std::atomic<int> cache[kDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < kDevices) {
+    const int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+  }
+  int n = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 1;
+  if (dev >= 0 && dev < kDevices) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+// Grid of a persistent launch: min(units, CUs x workgroups of Kernel per CU);
+// the occupancy is queried once per kernel.
+template <auto Kernel>
+inline int persistent_grid(int units) {
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel, kThreads, 0) != hipSuccess || n < 1) n = 1;
+    return n;
+  }();
+  const long long g = (long long)cu_count() * per_cu;
+  return (int)(units < g ? units : g);
+}
+// Launch Kernel over `units` work units: a persistent grid, or one workgroup
+// per unit.  The kernels take persistent grids for causal work without a
+// window or block mask, split into units of equal cost (the tile pairs t and
+// n - 1 - t of a head); units of uneven cost (a block mask's, a window's)
+// measured faster one workgroup each, balanced by the dispatcher.
+template <auto Kernel, typename Params>
+inline void launch_units(const Params& p, int units, bool persistent, hipStream_t s) {
+  const int grid = persistent ? persistent_grid<Kernel>(units) : units;
+  hipLaunchKernelGGL(Kernel, dim3(grid), dim3(kThreads), 0, s, p);
+}
+
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, bool causal, bool masked,
                       hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int d, bool causal, bool masked,
