@@ -277,220 +277,238 @@ struct Fp8Geom {
 // (measured 4 % faster than two)
 constexpr int kFp8Wpe128 = 3;
 
-template <typename T, int D, bool CAUSAL, int WPE>
+template <typename T, int D, bool CAUSAL, int WPE, bool PERSIST>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WPE, WPE)))
 void fp8_fwd_kernel(Fp8FwdParams p) {
   using G = Fp8Geom<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
   debug_fill_lds_nan(smem, sizeof(smem));
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane_ = threadIdx.x & 63;
   const int wave = wave_id();
-  const int g = lane >> 5;
-  const int l32 = lane & 31;
-
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = logical / p.nqt;
-  int qt = logical % p.nqt;
-  if (CAUSAL) qt = p.nqt - 1 - qt;  // longest rows first
   const int N = p.N;
-  const int q0 = qt * 128;
-  const int qw0 = q0 + wave * 32;
-  const int qw_last = qw0 + 31;
-  const int q_hi = min(q0 + 128, N) - 1;
-  const int kvh = head / p.group;
-  const int nblk = p.N64 / 64;
 
-  const Buf bq = make_buf(p.qc + (size_t)head * p.N64 * D, (uint32_t)p.N64 * D);
-  const Buf bk = make_buf(p.kc + (size_t)kvh * p.N64 * D, (uint32_t)p.N64 * D);
-  const Buf bv = make_buf(p.vc + (size_t)kvh * p.N64 * D, (uint32_t)p.N64 * D);
-  // this wave's Q block scale (E8M0); a wave wholly past N64 (only in the last
-  // query tile) reads zero codes and writes nothing
-  const int sq = qw0 < p.N64 ? 127 + p.qe[(size_t)head * nblk + qw0 / 64] : 127;
-  const int8_t* ke = p.ke + (size_t)kvh * nblk;
-  const int8_t* ve = p.ve + (size_t)kvh * nblk;
+  // one query tile of one head
+  auto tile = [&](const int head, const int qt) __attribute__((always_inline)) {
+    int lane = lane_;
+    // in the persistent loop, lane-only values are recomputed per tile rather
+    // than kept live across it (registers)
+    if constexpr (PERSIST) __asm__ volatile("" : "+v"(lane));
+    const int g = lane >> 5;
+    const int l32 = lane & 31;
+    const int q0 = qt * 128;
+    const int qw0 = q0 + wave * 32;
+    const int qw_last = qw0 + 31;
+    const int q_hi = min(q0 + 128, N) - 1;
+    const int kvh = head / p.group;
+    const int nblk = p.N64 / 64;
 
-  const Band band{N, p.window, CAUSAL};
-  MaskLists none;
-  none.row_ptr = none.col_idx = none.col_ptr = none.row_idx = nullptr;
-  none.mask_block = 0;
-  const auto tiles = key_tiles<G::KT, false>(none, band, q0, q_hi);
-  const int ntiles = tiles.count;
+    const Buf bq = make_buf(p.qc + (size_t)head * p.N64 * D, (uint32_t)p.N64 * D);
+    const Buf bk = make_buf(p.kc + (size_t)kvh * p.N64 * D, (uint32_t)p.N64 * D);
+    const Buf bv = make_buf(p.vc + (size_t)kvh * p.N64 * D, (uint32_t)p.N64 * D);
+    // this wave's Q block scale (E8M0); a wave wholly past N64 (only in the last
+    // query tile) reads zero codes and writes nothing
+    const int sq = qw0 < p.N64 ? 127 + p.qe[(size_t)head * nblk + qw0 / 64] : 127;
+    const int8_t* ke = p.ke + (size_t)kvh * nblk;
+    const int8_t* ve = p.ve + (size_t)kvh * nblk;
 
-  // Q codes: B operand of S^T = K Q^T, 32 consecutive head-dim bytes per lane
-  i32x8 qf[G::NKS];
-#pragma unroll
-  for (int t = 0; t < G::NKS; ++t) {
-    const uint32_t off = (uint32_t)((qw0 + l32) * D + 64 * t + 32 * g);
-    const u32x4 lo = buf_load16(bq, off), hi = buf_load16(bq, off + 16);
-    qf[t] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-  }
+    const Band band{N, p.window, CAUSAL};
+    MaskLists none;
+    none.row_ptr = none.col_idx = none.col_ptr = none.row_idx = nullptr;
+    none.mask_block = 0;
+    const auto tiles = key_tiles<G::KT, false>(none, band, q0, q_hi);
+    const int ntiles = tiles.count;
 
-  f32x16 o[G::NDB];
+    // Q codes: B operand of S^T = K Q^T, 32 consecutive head-dim bytes per lane
+    i32x8 qf[G::NKS];
 #pragma unroll
-  for (int i = 0; i < G::NDB; ++i) o[i] = f32x16{0};
-  float m_ref = kNegInf, ref = 0.f, l_run = 0.f;
-
-  auto gload = [&](int it, int stage) {
-    const int k0 = tiles.pos0(it);
-    char* ks = smem + stage * G::STAGE;
-    dma_tile8<D, 64>(bk, (uint32_t)k0 * D, ks, wave, lane);
-    dma_tile8<64, D>(bv, (uint32_t)(k0 / 64) * D * 64, ks + G::KBYTES, wave, lane);
-  };
-  if (ntiles > 0) gload(0, 0);
-  wait_all_memory();
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < ntiles) gload(it + 1, cur ^ 1);
-    const int k0 = tiles.pos0(it);
-    const char* ks = smem + cur * G::STAGE;
-    const char* vs = ks + G::KBYTES;
-    if (k0 <= band.hi(qw_last) && k0 + G::KT - 1 >= band.lo(qw0)) {
-      const int sk = 127 + ke[k0 / 64];
-      const int sv = 127 + ve[k0 / 64];
-      // S^T = K Q^T, dequantised by the block scales inside the product
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{0};
-#pragma unroll
-        for (int t = 0; t < G::NKS; ++t) {
-          const int r = kb * 32 + l32;
-          const u32x4 lo = *(const u32x4*)(ks + swz8_off<D>(r, 4 * t + 2 * g));
-          const u32x4 hi = *(const u32x4*)(ks + swz8_off<D>(r, 4 * t + 2 * g + 1));
-          const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[t], s[kb], 0, 0, 0, sk, 0, sq);
-        }
-      }
-      // keys outside the row's band; key of register r of block kb is
-      // k0 + g*4 + C, C = kb*32 + (r/4)*8 + r%4
-      if (k0 + G::KT - 1 > band.hi(qw0)) {
-        const int ub = band.hi(qw0 + l32) - k0 - g * 4;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
-            s[kb][r] = C > ub ? kNegInf : s[kb][r];
-          }
-      }
-      if (k0 < band.lo(qw_last)) {
-        const int lb = band.lo(qw0 + l32) - k0 - g * 4;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
-            s[kb][r] = C < lb ? kNegInf : s[kb][r];
-          }
-      }
-      // online softmax over the whole tile, then one P V product per
-      // 32-column block of O
-      const float mx = vmax(max16(s[0]), max16(s[1])) * p.c;
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kFp8Tau) != 0) {
-        FA_KEEP_BRANCH();
-        const float m_new = vmax(m_ref, pair_max(mx));
-        const float r_new = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_ref - r_new);  // 0 while m_ref = -inf
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < G::NDB; ++i) o[i] *= alpha;
-        m_ref = m_new;
-        ref = r_new;
-      }
-      // P = 2^(S c - ref) <= 256, rounded to E4M3; byte i = 16 kb + r of the
-      // lane's operand is key kappa(g, i) of the tile
-      uint32_t pw[8];
-      float lp = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = 4 * q;
-          const float e0 = fast_exp2(__builtin_fmaf(s[kb][r], p.c, -ref));
-          const float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], p.c, -ref));
-          const float e2 = fast_exp2(__builtin_fmaf(s[kb][r + 2], p.c, -ref));
-          const float e3 = fast_exp2(__builtin_fmaf(s[kb][r + 3], p.c, -ref));
-          lp += (e0 + e1) + (e2 + e3);  // row sum of the unrounded weights
-          pw[kb * 4 + q] = fp8x2<true>(e2, e3, fp8x2<false>(e0, e1, 0u));
-        }
-      l_run += lp;
-      const i32x8 pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
-      // O'^T += V^T P^T: row db*32 + l32 of the V codes tile, bytes 32 g ..
-#pragma unroll
-      for (int db = 0; db < G::NDB; ++db) {
-        const int r = db * 32 + l32;
-        const u32x4 lo = *(const u32x4*)(vs + swz8_off<64>(r, 2 * g));
-        const u32x4 hi = *(const u32x4*)(vs + swz8_off<64>(r, 2 * g + 1));
-        const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[db], 0, 0, 0, sv, 0, 127);
-      }
+    for (int t = 0; t < G::NKS; ++t) {
+      const uint32_t off = (uint32_t)((qw0 + l32) * D + 64 * t + 32 * g);
+      const u32x4 lo = buf_load16(bq, off), hi = buf_load16(bq, off + 16);
+      qf[t] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
-    wait_all_memory();  // this thread's copies into the next stage have landed
+
+    f32x16 o[G::NDB];
+#pragma unroll
+    for (int i = 0; i < G::NDB; ++i) o[i] = f32x16{0};
+    float m_ref = kNegInf, ref = 0.f, l_run = 0.f;
+
+    auto gload = [&](int it, int stage) {
+      const int k0 = tiles.pos0(it);
+      char* ks = smem + stage * G::STAGE;
+      dma_tile8<D, 64>(bk, (uint32_t)k0 * D, ks, wave, lane);
+      dma_tile8<64, D>(bv, (uint32_t)(k0 / 64) * D * 64, ks + G::KBYTES, wave, lane);
+    };
+    if (ntiles > 0) gload(0, 0);
+    wait_all_memory();
     __syncthreads();
-  }
 
-  // epilogue: O' / l, then undo the rotation, O = O' H diag(s) / sqrt(d).
-  // Register r of block db holds head-dim column db*32 + (r/4)*8 + 4g + r%4:
-  // the Hadamard butterflies over bits 0, 1, 3, 4 (and 5, 6: db) of the column
-  // pair registers of one lane; bit 2 pairs lane l with lane l ^ 32.
-  const float lt = pair_sum(l_run);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    for (int it = 0; it < ntiles; ++it) {
+      const int cur = it & 1;
+      if (it + 1 < ntiles) gload(it + 1, cur ^ 1);
+      const int k0 = tiles.pos0(it);
+      const char* ks = smem + cur * G::STAGE;
+      const char* vs = ks + G::KBYTES;
+      if (k0 <= band.hi(qw_last) && k0 + G::KT - 1 >= band.lo(qw0)) {
+        const int sk = 127 + ke[k0 / 64];
+        const int sv = 127 + ve[k0 / 64];
+        // S^T = K Q^T, dequantised by the block scales inside the product
+        f32x16 s[2];
 #pragma unroll
-  for (int db = 0; db < G::NDB; ++db)
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{0};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] *= inv;
-#pragma unroll
-  for (int bit = 0; bit < 4; ++bit) {  // register bits r&1, r&2, r&4, r&8
-    const int h = 1 << bit;
-#pragma unroll
-    for (int db = 0; db < G::NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (!(r & h)) {
-          const float a = o[db][r], b = o[db][r + h];
-          o[db][r] = a + b;
-          o[db][r + h] = a - b;
+          for (int t = 0; t < G::NKS; ++t) {
+            const int r = kb * 32 + l32;
+            const u32x4 lo = *(const u32x4*)(ks + swz8_off<D>(r, 4 * t + 2 * g));
+            const u32x4 hi = *(const u32x4*)(ks + swz8_off<D>(r, 4 * t + 2 * g + 1));
+            const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[t], s[kb], 0, 0, 0, sk, 0, sq);
+          }
         }
-  }
+        // keys outside the row's band; key of register r of block kb is
+        // k0 + g*4 + C, C = kb*32 + (r/4)*8 + r%4
+        if (k0 + G::KT - 1 > band.hi(qw0)) {
+          const int ub = band.hi(qw0 + l32) - k0 - g * 4;
 #pragma unroll
-  for (int h = 1; h < G::NDB; h <<= 1)  // column bits 5, 6: between blocks
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db)
-      if (!(db & h))
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float a = o[db][r], b = o[db + h][r];
-          o[db][r] = a + b;
-          o[db + h][r] = a - b;
+            for (int r = 0; r < 16; ++r) {
+              const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
+              s[kb][r] = C > ub ? kNegInf : s[kb][r];
+            }
         }
+        if (k0 < band.lo(qw_last)) {
+          const int lb = band.lo(qw0 + l32) - k0 - g * 4;
 #pragma unroll
-  for (int db = 0; db < G::NDB; ++db)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {  // column bit 2: across the lane halves
-      const LanePair pr = lane_pair(o[db][r]);
-      o[db][r] = g == 0 ? pr.lo + pr.hi : pr.lo - pr.hi;
-    }
-  const int q = qw0 + l32;
-  if (q < N) {
-    T* orow = (T*)p.o + ((size_t)head * N + q) * D;
+            for (int r = 0; r < 16; ++r) {
+              const int C = kb * 32 + (r >> 2) * 8 + (r & 3);
+              s[kb][r] = C < lb ? kNegInf : s[kb][r];
+            }
+        }
+        // online softmax over the whole tile, then one P V product per
+        // 32-column block of O
+        const float mx = vmax(max16(s[0]), max16(s[1])) * p.c;
+        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kFp8Tau) != 0) {
+          FA_KEEP_BRANCH();
+          const float m_new = vmax(m_ref, pair_max(mx));
+          const float r_new = (m_new == kNegInf) ? 0.f : m_new;
+          const float alpha = fast_exp2(m_ref - r_new);  // 0 while m_ref = -inf
+          l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db)
+          for (int i = 0; i < G::NDB; ++i) o[i] *= alpha;
+          m_ref = m_new;
+          ref = r_new;
+        }
+        // P = 2^(S c - ref) <= 256, rounded to E4M3; byte i = 16 kb + r of the
+        // lane's operand is key kappa(g, i) of the tile
+        uint32_t pw[8];
+        float lp = 0.f;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int c = db * 32 + rr * 8 + g * 4;
-        float x[4];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = o[db][rr * 4 + e] * inv_sqrt_d<D>() * p.signs[c + e];
-        u32x2 w;
-        w[0] = pack2<T>(x[0], x[1]);
-        w[1] = pack2<T>(x[2], x[3]);
-        *(u32x2*)(orow + c) = w;
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * q;
+            const float e0 = fast_exp2(__builtin_fmaf(s[kb][r], p.c, -ref));
+            const float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], p.c, -ref));
+            const float e2 = fast_exp2(__builtin_fmaf(s[kb][r + 2], p.c, -ref));
+            const float e3 = fast_exp2(__builtin_fmaf(s[kb][r + 3], p.c, -ref));
+            lp += (e0 + e1) + (e2 + e3);  // row sum of the unrounded weights
+            pw[kb * 4 + q] = fp8x2<true>(e2, e3, fp8x2<false>(e0, e1, 0u));
+          }
+        l_run += lp;
+        const i32x8 pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+        // O'^T += V^T P^T: row db*32 + l32 of the V codes tile, bytes 32 g ..
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+          const int r = db * 32 + l32;
+          const u32x4 lo = *(const u32x4*)(vs + swz8_off<64>(r, 2 * g));
+          const u32x4 hi = *(const u32x4*)(vs + swz8_off<64>(r, 2 * g + 1));
+          const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[db], 0, 0, 0, sv, 0, 127);
+        }
       }
-    if (g == 0) p.lse[(size_t)head * N + q] = lt > 0.f ? (m_ref + fast_log2(lt)) * kLn2 : kNegInf;
+      wait_all_memory();  // this thread's copies into the next stage have landed
+      __syncthreads();
+    }
+
+    // epilogue: O' / l, then undo the rotation, O = O' H diag(s) / sqrt(d).
+    // Register r of block db holds head-dim column db*32 + (r/4)*8 + 4g + r%4:
+    // the Hadamard butterflies over bits 0, 1, 3, 4 (and 5, 6: db) of the column
+    // pair registers of one lane; bit 2 pairs lane l with lane l ^ 32.
+    const float lt = pair_sum(l_run);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= inv;
+#pragma unroll
+    for (int bit = 0; bit < 4; ++bit) {  // register bits r&1, r&2, r&4, r&8
+      const int h = 1 << bit;
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!(r & h)) {
+            const float a = o[db][r], b = o[db][r + h];
+            o[db][r] = a + b;
+            o[db][r + h] = a - b;
+          }
+    }
+#pragma unroll
+    for (int h = 1; h < G::NDB; h <<= 1)  // column bits 5, 6: between blocks
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db)
+        if (!(db & h))
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float a = o[db][r], b = o[db + h][r];
+            o[db][r] = a + b;
+            o[db + h][r] = a - b;
+          }
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {  // column bit 2: across the lane halves
+        const LanePair pr = lane_pair(o[db][r]);
+        o[db][r] = g == 0 ? pr.lo + pr.hi : pr.lo - pr.hi;
+      }
+    const int q = qw0 + l32;
+    if (q < N) {
+      T* orow = (T*)p.o + ((size_t)head * N + q) * D;
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int c = db * 32 + rr * 8 + g * 4;
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = o[db][rr * 4 + e] * inv_sqrt_d<D>() * p.signs[c + e];
+          u32x2 w;
+          w[0] = pack2<T>(x[0], x[1]);
+          w[1] = pack2<T>(x[2], x[3]);
+          *(u32x2*)(orow + c) = w;
+        }
+      if (g == 0) p.lse[(size_t)head * N + q] = lt > 0.f ? (m_ref + fast_log2(lt)) * kLn2 : kNegInf;
+    }
+  };
+
+  if constexpr (PERSIST) {
+    // causal work units: the tile pair (nqt - 1 - u, u) of a head, the longer
+    // rows first; every unit costs about the same
+    const int units = (p.nqt + 1) / 2, total = p.nheads * units;
+    for (int b = blockIdx.x; b < total; b += gridDim.x) {
+      const int logical = xcd_remap(b, total);
+      const int head = logical / units, u = logical % units;
+      const int nsub = 2 * u + 1 != p.nqt ? 2 : 1;
+      for (int e = 0; e < nsub; ++e) tile(head, e == 0 ? p.nqt - 1 - u : u);
+    }
+  } else {
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int head = logical / p.nqt, qt = logical % p.nqt;
+    tile(head, CAUSAL ? p.nqt - 1 - qt : qt);  // causal: the longer rows first
   }
 }
 
@@ -502,12 +520,15 @@ hipError_t quant_t(const Fp8QuantParams& qp, int wgs, hipStream_t s) {
 
 template <typename T, int D>
 hipError_t fwd8_t(const Fp8FwdParams& p, bool causal, hipStream_t s) {
-  dim3 grid(p.nheads * p.nqt), block(256);
   constexpr int WPE = D == 64 ? 4 : kFp8Wpe128;
-  if (causal)
-    hipLaunchKernelGGL((fp8_fwd_kernel<T, D, true, WPE>), grid, block, 0, s, p);
+  // causal work without a window: a persistent grid over tile pairs (as the
+  // 16-bit forward); the rest one workgroup per tile
+  if (causal && p.window == 0)
+    launch_units<fp8_fwd_kernel<T, D, true, WPE, true>>(p, p.nheads * ((p.nqt + 1) / 2), true, s);
+  else if (causal)
+    launch_units<fp8_fwd_kernel<T, D, true, WPE, false>>(p, p.nheads * p.nqt, false, s);
   else
-    hipLaunchKernelGGL((fp8_fwd_kernel<T, D, false, WPE>), grid, block, 0, s, p);
+    launch_units<fp8_fwd_kernel<T, D, false, WPE, false>>(p, p.nheads * p.nqt, false, s);
   return hipGetLastError();
 }
 
