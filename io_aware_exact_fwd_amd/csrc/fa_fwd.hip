@@ -291,7 +291,8 @@ void fwd_kernel(FwdParams p) {
           w[1] = pack2<T>(o[db][rr * 4 + 2] * inv, o[db][rr * 4 + 3] * inv);
           *(u32x2*)(orow + db * 32 + rr * 8 + g * 4) = w;
         }
-      if (g == 0) p.lse[(size_t)head * N + q] = lt > 0.f ? (m_ref + fast_log2(lt)) * kLn2 : kNegInf;
+      // -inf for a row without a visible key; a NaN row sum (a NaN score) stays NaN
+      if (g == 0) p.lse[(size_t)head * N + q] = !(lt <= 0.f) ? (m_ref + fast_log2(lt)) * kLn2 : kNegInf;
     }
   };
 
