@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from io_aware_exact_fwd_amd import fa_fwd
+from io_aware_exact_fwd_amd import fa_bwd, fa_fwd
 from io_aware_exact_fwd_amd.workloads import WORKLOADS, butterfly_block_mask, make_inputs
 
 from gpu_util import check_case, say
@@ -145,3 +145,26 @@ def test_dropout_keep_mask_bit_exact(causal, p, d):
         want = np.stack([keep[:, c::d].sum(axis=1) for c in range(d)], axis=1)
         kept = np.rint(got[0, h] * count[:, None] / mult)
         assert np.array_equal(kept, want), h
+
+
+# A window at least as wide as the sequence hides nothing.  Causal work with a
+# window runs one workgroup per tile; without one, the persistent grid over tile
+# pairs: the two schedules must give bitwise the same outputs (every tile is
+# computed the same way, only their assignment to workgroups differs).  The
+# dropout case has whole query tiles: in a ragged last tile the rows past N see a
+# band that does depend on the window, and as a wave moves the reference of all
+# its rows together, the rows before N can then differ in rounding (not beyond).
+@pytest.mark.parametrize("dtype,d,B,H,hkv,N,p", [("f16", 64, 8, 12, None, 1024, 0.0),
+                                              ("bf16", 128, 1, 8, 2, 2000, 0.0),
+                                              ("f16", 64, 2, 4, None, 768, 0.1)])
+def test_persistent_grid_equals_one_workgroup_per_tile(dtype, d, B, H, hkv, N, p):
+    say(f"[case] persistent vs per-tile grid: B={B} H={H} hkv={hkv} N={N} d={d} {dtype} p={p}")
+    q, k, v, do = (t.to("cuda") for t in make_inputs(B, H, N, d, dtype, hkv=hkv))
+    outs = []
+    for window in (0, N + 5):
+        kw = dict(causal=True, scale=1.0 / np.sqrt(d), window=window, dropout_p=p, seed=7)
+        o, lse = fa_fwd(q, k, v, **kw)
+        outs.append((o, lse) + tuple(fa_bwd(q, k, v, o, do, lse, **kw)))
+    torch.cuda.synchronize()
+    for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), *outs):
+        assert torch.equal(a, b), name
