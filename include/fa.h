@@ -118,7 +118,7 @@ typedef struct fa_problem {
   uint64_t seed;              /* dropout generator key                         */
   uint32_t offset;            /* dropout counter word: one value per call that
                                  must draw a fresh mask with the same seed     */
-  uint32_t flags;             /* 0, or FA_REUSE_LISTS (below)                  */
+  uint32_t flags;             /* 0, or FA_REUSE_LISTS | FA_BWD_ATOMIC_DQ       */
 } fa_problem;
 
 /* fa_problem.flags bits.
@@ -134,13 +134,27 @@ typedef struct fa_problem {
  *   block mask and for FA_F32 (which reads the mask itself). */
 #define FA_REUSE_LISTS 1u
 
+/* FA_BWD_ATOMIC_DQ: fa_bwd runs the single-pass backward of the pages'
+ *   backward loop ("Passo para tras: recalcular em vez de armazenar",
+ *   marketmaker.cc article): the key-outer kernel also forms dQ += dS K for its
+ *   keys and adds it into a float32 accumulator (B,H,N,d) in the workspace with
+ *   atomic adds, so S and dP are computed once per visible pair (10 d FLOPs)
+ *   instead of in two kernels (14 d).  dq then depends on the order of the
+ *   adds: repeated calls can differ in the last bits (dk and dv do not).
+ *   FA_F16 and FA_BF16 only (FA_F32: FA_ERR_UNSUPPORTED).  fa_bwd_dq and
+ *   fa_bwd_dkdv, the stages of the two-kernel backward, return FA_ERR_ARG with
+ *   this flag; the forward entry points ignore it. */
+#define FA_BWD_ATOMIC_DQ 2u
+
 /* Bytes of device workspace that fa_fwd (pass 0) or fa_bwd (pass 1) needs for
  * problem p; 0 if none.  Host-only arithmetic, no GPU call.  Returns 0 for an
  * invalid problem (the entry point itself then reports the error).  Layout:
  * with a block mask (FA_F16, FA_BF16) the compiled block lists come first in
  * both passes; the backward then holds D (float32, B*H*N) on the next
- * 256-byte boundary.  The backward's size is never smaller than the
- * forward's, so one buffer of the backward's size serves both. */
+ * 256-byte boundary and, with FA_BWD_ATOMIC_DQ (FA_F16, FA_BF16), the float32
+ * dQ accumulator (B*H*N*d) on the next.  The backward's size is never
+ * smaller than the forward's, so one buffer of the backward's size serves
+ * both. */
 size_t fa_workspace_size(const fa_problem* p, int pass);
 
 /* Forward.  Reads q, k, v; overwrites o (B,H,N,d, dtype) and lse (B,H,N,
@@ -155,7 +169,8 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
  * Overwrites (does not accumulate into) dq, dk, dv.  workspace: at least
  * fa_workspace_size(p, 1) bytes; it receives D_i = dO_i . O_i (float32, B*H*N)
  * and, with a block mask, the compiled block lists (unless FA_REUSE_LISTS
- * says they are there already). */
+ * says they are there already); with FA_BWD_ATOMIC_DQ also the float32 dQ
+ * accumulator. */
 int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
            size_t ws_bytes, hipStream_t stream);

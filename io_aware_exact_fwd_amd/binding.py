@@ -23,6 +23,7 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = 0, -1, -2, -3, -4
 FA_ERR_SCRATCH = -5
 FA_REUSE_LISTS = 1  # fa_problem.flags: the workspace already holds the compiled block lists
+FA_BWD_ATOMIC_DQ = 2  # fa_problem.flags: single-pass backward, dQ by float32 atomics
 NOALLOC_SCRATCH_BYTES = 64 << 20  # static scratch of fa_fwd_decode_noalloc, per GPU
 
 EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv",
@@ -407,10 +408,12 @@ def fa_fwd_fp8(q, k, v, signs, causal=False, scale=None, window=0, out=None, lse
 
 
 def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, block_mask=None, mask_block=128,
-           window=0, dropout_p=0.0, seed=0, offset=0, workspace=None, reuse_lists=False):
+           window=0, dropout_p=0.0, seed=0, offset=0, workspace=None, reuse_lists=False,
+           atomic_dq=False):
     """Backward of <O, dO>: returns (dQ, dK, dV); dQ like q, dK and dV like k.
     workspace / reuse_lists: as for ``fa_fwd`` (a forward given the same
-    buffer leaves the block lists there for the backward)."""
+    buffer leaves the block lists there for the backward).  atomic_dq: the
+    single-pass backward (FA_BWD_ATOMIC_DQ; dQ summed with float32 atomics)."""
     import torch
 
     _check_qkv(q, k, v)
@@ -419,7 +422,7 @@ def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, block_mask=None, mas
         raise ValueError("lse must be a contiguous float32 GPU tensor")
     bm = _mask_arg(block_mask, q, mask_block)
     p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset,
-                     FA_REUSE_LISTS if reuse_lists else 0)
+                     (FA_REUSE_LISTS if reuse_lists else 0) | (FA_BWD_ATOMIC_DQ if atomic_dq else 0))
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_n = fa_workspace_size(p, 1)
     ws = _workspace(workspace, ws_n, q.device)

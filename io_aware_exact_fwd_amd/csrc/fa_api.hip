@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 6 * 100 + 0;
 
 // Size of the static scratch of fa_fwd_decode_noalloc (include/fa.h).
 constexpr size_t kScratchBytes = (size_t)64 << 20;
@@ -37,7 +37,7 @@ int check_problem(const fa_problem* p) {
   if (p->window < 0) return FA_ERR_ARG;
   if (p->H_kv < 0 || (p->H_kv > 0 && p->H % p->H_kv != 0)) return FA_ERR_ARG;
   if (!(p->dropout_p >= 0.f && p->dropout_p < 1.f)) return FA_ERR_ARG;
-  if ((p->flags & ~FA_REUSE_LISTS) != 0) return FA_ERR_ARG;
+  if ((p->flags & ~(FA_REUSE_LISTS | FA_BWD_ATOMIC_DQ)) != 0) return FA_ERR_ARG;
   if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (p->d != 64 && p->d != 128) return FA_ERR_UNSUPPORTED;
   // one head must be addressable with 32-bit byte offsets
@@ -62,6 +62,13 @@ size_t lists_bytes(const fa_problem* p) {
 
 size_t dvec_bytes(const fa_problem* p) {
   return align_up((size_t)p->B * p->H * p->N * sizeof(float));
+}
+
+// single-pass backward: the float32 dQ accumulator after D
+bool single_pass(const fa_problem* p) { return (p->flags & FA_BWD_ATOMIC_DQ) != 0; }
+size_t dqacc_bytes(const fa_problem* p) {
+  if (!single_pass(p) || p->dtype == FA_F32) return 0;
+  return align_up((size_t)p->B * p->H * p->N * p->d * sizeof(float));
 }
 
 struct Lists {
@@ -122,7 +129,7 @@ extern "C" {
 size_t fa_workspace_size(const fa_problem* p, int pass) {
   if (check_problem(p) != FA_OK) return 0;
   if (pass == 0) return lists_bytes(p);
-  return lists_bytes(p) + dvec_bytes(p);
+  return lists_bytes(p) + dvec_bytes(p) + dqacc_bytes(p);
 }
 
 int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -477,6 +484,7 @@ int bwd_setup(const fa_problem* p, const void* q, const void* k, const void* v, 
   b->dk = const_cast<void*>(dk);
   b->dv = const_cast<void*>(dv);
   b->dvec = (float*)((char*)workspace + lists_bytes(p));
+  b->dqacc = dqacc_bytes(p) ? (float*)((char*)workspace + lists_bytes(p) + dvec_bytes(p)) : nullptr;
   b->N = p->N;
   b->nheads = p->B * p->H;
   b->window = p->window;
@@ -533,6 +541,23 @@ int run_dq(const fa_problem* p, fa::BwdParams b, hipStream_t s) {
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// FA_BWD_ATOMIC_DQ: block lists (if any), then D, dK/dV with dQ by atomics,
+// and the dQ conversion
+int run_single_pass(const fa_problem* p, fa::BwdParams b, hipStream_t s) {
+  if (p->dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  const bool masked = p->block_mask != nullptr;
+  if (masked && !(p->flags & FA_REUSE_LISTS) &&
+      fa::launch_mask_compile(p->block_mask, p->N / p->mask_block, (int32_t*)b.m.row_ptr,
+                              (int32_t*)b.m.col_idx, (int32_t*)b.m.col_ptr,
+                              (int32_t*)b.m.row_idx, s) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  b.nheads = p->B * kv_heads(p);
+  b.ntiles = (p->N + fa::kBwdKeys - 1) / fa::kBwdKeys;
+  return fa::launch_bwd_single_pass(b, p->dtype, p->d, p->causal != 0, masked, s) == hipSuccess
+             ? FA_OK
+             : FA_ERR_LAUNCH;
+}
+
 int run_dkdv(const fa_problem* p, fa::BwdParams b, hipStream_t s) {
   b.nheads = p->B * kv_heads(p);  // one workgroup column per K/V head
   if (p->dtype == FA_F32)
@@ -555,6 +580,7 @@ int fa_bwd(const fa_problem* p, const void* q, const void* k, const void* v, con
   fa::BwdParams b;
   int st = bwd_setup(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_bytes, true, true, &b);
   if (st != FA_OK) return st;
+  if (single_pass(p)) return run_single_pass(p, b, stream);
   st = run_dq(p, b, stream);
   if (st != FA_OK) return st;
   return run_dkdv(p, b, stream);
@@ -567,6 +593,7 @@ int fa_bwd_dq(const fa_problem* p, const void* q, const void* k, const void* v, 
   int st = bwd_setup(p, q, k, v, o, dout, lse, dq, nullptr, nullptr, workspace, ws_bytes, true,
                      false, &b);
   if (st != FA_OK) return st;
+  if (single_pass(p)) return FA_ERR_ARG;  // a stage of the two-kernel backward only
   return run_dq(p, b, stream);
 }
 
@@ -577,6 +604,7 @@ int fa_bwd_dkdv(const fa_problem* p, const void* q, const void* k, const void* v
   int st = bwd_setup(p, q, k, v, nullptr, dout, lse, nullptr, dk, dv, workspace, ws_bytes, false,
                      true, &b);
   if (st != FA_OK) return st;
+  if (single_pass(p)) return FA_ERR_ARG;  // a stage of the two-kernel backward only
   return run_dkdv(p, b, stream);
 }
 

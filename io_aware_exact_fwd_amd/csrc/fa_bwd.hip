@@ -23,6 +23,20 @@
 //                    start at -D (see the kernel).
 // The price is computing S and dP in both kernels: 14 d multiply-add FLOPs
 // per visible pair instead of 10 d.
+//
+// The single-pass alternative (FA_BWD_ATOMIC_DQ) does the pages' own loop
+// ("Passo para tras: recalcular em vez de armazenar", marketmaker.cc article):
+// the key-outer kernel also forms dQ += dS K for its keys and adds it into a
+// float32 accumulator in HBM with atomics, so S and dP are computed once
+// (10 d FLOPs per pair).  A pre-pass writes D and clears the accumulator, and a
+// last pass scales and converts it.  Each step the waves store their dS
+// (one key per lane) into a shared 128-key x 64-query LDS tile; after a
+// barrier each wave multiplies a 32-query x 32-column block of it by the
+// workgroup's K tile (kept in LDS for the whole key tile), so its result is
+// the workgroup's complete contribution, and adds it into HBM with one atomic
+// add per element once the step's copies have landed (the adds then overlap
+// the next step).  dQ depends on the order of the atomic adds (not bitwise
+// repeatable); dK and dV are bitwise those of the two-kernel backward.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -50,6 +64,8 @@ constexpr int kDqWpe128Drop = 2;
 constexpr int kDkdvWpe64 = 3;
 constexpr int kDkdvWpe64Drop = 2;     // dropout's generator registers: three waves would spill
 constexpr int kDkdvWpe128 = 1;
+constexpr int kDkdvWpe64Adq = 2;      // single pass: K^T fragments and the dQ products
+constexpr int kDkdvWpe128Adq = 1;
 constexpr int kDkdvQueries = 64;      // queries per dK/dV step (two 32-query blocks)
 constexpr int kDkdvAhead = 4;         // LDS operand reads issued ahead of the score products
 
@@ -301,15 +317,20 @@ struct DkvGeom {
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
   static constexpr int NQB = QT / 32;       // 32-query blocks per step
+  // single pass: the workgroup's K tile and the step's dS^T (kBwdKeys x QT,
+  // 16-bit), both swizzled tiles
+  static constexpr int KTBYTES = kBwdKeys * D * 2;
+  static constexpr int DSBYTES = kBwdKeys * QT * 2;
   // waves per SIMD the registers allow
-  static constexpr int wpe(bool drop) {
+  static constexpr int wpe(bool drop, bool adq) {
+    if (adq) return D == 64 ? kDkdvWpe64Adq : kDkdvWpe128Adq;
     return D == 64 ? (drop ? kDkdvWpe64Drop : kDkdvWpe64) : kDkdvWpe128;
   }
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP, bool PERSIST>
+template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP, bool PERSIST, bool ADQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(DkvGeom<D>::wpe(DROP), DkvGeom<D>::wpe(DROP))))
+                          amdgpu_waves_per_eu(DkvGeom<D>::wpe(DROP, ADQ), DkvGeom<D>::wpe(DROP, ADQ))))
 void bwd_dkdv_kernel(BwdParams p) {
   using G = DkvGeom<D>;
   using V8 = typename Vec8<T>::type;
@@ -319,12 +340,18 @@ void bwd_dkdv_kernel(BwdParams p) {
   // to |S c| 2^-11, which for large logits (|S c| ~ 100) breaks the
   // gradients' tolerance.
   constexpr bool kFoldD = D == 64 && !DROP;
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE + (DROP ? 4 * kDropLdsPerWave : 0)];
+  constexpr int kDropBytes = DROP ? 4 * kDropLdsPerWave : 0;
+  __shared__ __attribute__((aligned(16))) char
+      smem[2 * G::STAGE + kDropBytes + (ADQ ? G::KTBYTES + G::DSBYTES : 0)];
   debug_fill_lds_nan(smem, sizeof(smem));
 
   const int lane_ = threadIdx.x & 63;
   const int wave = wave_id();
   const int N = p.N;
+
+  // single pass: the K tile and the dS^T tile
+  char* const ktile = smem + 2 * G::STAGE + kDropBytes;
+  char* const dstile = ktile + G::KTBYTES;
 
   // one key tile of one K/V head
   auto tile = [&](const int kvh, const int kt) __attribute__((always_inline)) {
@@ -417,10 +444,20 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     const int ntiles = nqt * p.group;
     if (ntiles > 0) gload(0, smem);
+    // single pass: the workgroup's K tile, for the whole key tile
+    if constexpr (ADQ) dma_tile<D, kBwdKeys>(bk, k0, ktile, wave, lane);
     land_next(smem);
     __syncthreads();
 
     const TileOffsets<D> toff(lane);
+    // single pass: transpose-read offsets of the dS^T tile (64 columns), and
+    // zeros for the rows of a 32-query block that this wave skips
+    const TileOffsets<64> tds(lane);
+    auto ds_zero = [&](const int qb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int c = 0; c < 32; c += 8)
+        *(u32x2*)(dstile + swz_off<64>(wave * 32 + l32, qb * 32 + c + 4 * g)) = u32x2{0u, 0u};
+    };
     // one query step; its LDS stage (it mod 2) is a compile-time constant (two
     // steps per iteration of the loop below), so stage addresses join the
     // reads' immediate offsets
@@ -443,8 +480,12 @@ void bwd_dkdv_kernel(BwdParams p) {
       auto qblocks = [&](auto qb0_c, auto nq_c) __attribute__((always_inline)) {
         constexpr int QB0 = decltype(qb0_c)::value, NQ = decltype(nq_c)::value;
         const int qa = qs0 + QB0 * 32, qz = qa + NQ * 32 - 1;  // the blocks' queries
-        // blocks that see none of the wave's keys add nothing
-        if (NQ < G::NQB && (qa > band.qhi(kw_last) || qz < band.qlo(kw0))) return;
+        // blocks that see none of the wave's keys add nothing (single pass:
+        // their dS^T rows are zeros)
+        if (NQ < G::NQB && (qa > band.qhi(kw_last) || qz < band.qlo(kw0))) {
+          if constexpr (ADQ) ds_zero(QB0);
+          return;
+        }
         f32x16 s[NQ], dp[NQ];
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
@@ -539,13 +580,57 @@ void bwd_dkdv_kernel(BwdParams p) {
             const V8 bq_ = toff.template tr_operand<T>(qsm, (2 * QB0 + t) * 16, db);
             dka[db] = mfma32(ad, bq_, dka[db]);
           }
+          if constexpr (ADQ) {
+            // dS^T row of this lane's key: words 0-1 of ad hold the block's
+            // queries 16 (t % 2) + 4 g + 0..3, words 2-3 the same + 8
+            const u32x4 w = __builtin_bit_cast(u32x4, ad);
+            const int col = (QB0 + i) * 32 + 16 * (t & 1) + 4 * g;
+            *(u32x2*)(dstile + swz_off<64>(wave * 32 + l32, col)) = u32x2{w[0], w[1]};
+            *(u32x2*)(dstile + swz_off<64>(wave * 32 + l32, col + 8)) = u32x2{w[2], w[3]};
+          }
         }
       };
       if (active) {
         qblocks(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
         qblocks(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+      } else if constexpr (ADQ) {
+        ds_zero(0);
+        ds_zero(1);
       }
-      if (it + 1 < ntiles) land_next(smem + nxt * G::STAGE);
+      if constexpr (ADQ) {
+        // dQ of the step's queries: wave w takes query block w / 2 and column
+        // block(s) of w % 2; dS (k = the workgroup's 128 keys) times the K tile,
+        // both read by transposes (k index: rows 4 g + 0..3 and + 8 of each
+        // 16-row group, as TileOffsets lays out its transpose operands)
+        __syncthreads();  // every wave's dS^T is in the tile
+        const int qb = wave >> 1;
+        f32x16 dqa[G::NDB / 2];
+#pragma unroll
+        for (int j = 0; j < G::NDB / 2; ++j) {
+          const int db = (wave & 1) * (G::NDB / 2) + j;
+          dqa[j] = f32x16{0};
+#pragma unroll
+          for (int kk = 0; kk < kBwdKeys / 16; ++kk)
+            dqa[j] = mfma32(tds.template tr_operand<T>(dstile, kk * 16, qb),
+                            toff.template tr_operand<T>(ktile, kk * 16, db), dqa[j]);
+        }
+        if (it + 1 < ntiles) land_next(smem + nxt * G::STAGE);
+        // the atomic adds go out after this step's wait, so the next step's
+        // computation overlaps them; register r is query qb*32 + 8 (r/4) + 4 g + r%4
+        float* dst = p.dqacc + ((size_t)qh * N + qs0 + qb * 32) * D + l32;
+#pragma unroll
+        for (int j = 0; j < G::NDB / 2; ++j) {
+          const int db = (wave & 1) * (G::NDB / 2) + j;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = (r >> 2) * 8 + g * 4 + (r & 3);
+            if (dqa[j][r] != 0.f && qs0 + qb * 32 + row < N)
+              unsafeAtomicAdd(dst + row * D + db * 32, dqa[j][r]);
+          }
+        }
+      } else {
+        if (it + 1 < ntiles) land_next(smem + nxt * G::STAGE);
+      }
       __syncthreads();
     };
     for (int it = 0; it < ntiles; it += 2) {
@@ -625,7 +710,7 @@ static hipError_t launch_dq_t(const BwdParams& p, bool causal, bool masked, hipS
   return hipGetLastError();
 }
 
-template <typename T, int D, bool DROP>
+template <typename T, int D, bool DROP, bool ADQ = false>
 static hipError_t launch_dkdv_t(const BwdParams& p, bool causal, bool masked, hipStream_t s) {
   const int units = p.nheads * p.ntiles;
   // causal work without a window or block mask runs on a persistent grid over
@@ -633,18 +718,111 @@ static hipError_t launch_dkdv_t(const BwdParams& p, bool causal, bool masked, hi
   // tile measured faster); the rest one workgroup per tile
   if constexpr (D == 64)
     if (causal && !masked && p.window == 0) {
-      launch_units<bwd_dkdv_kernel<T, D, true, false, DROP, true>>(p, p.nheads * ((p.ntiles + 1) / 2), true, s);
+      launch_units<bwd_dkdv_kernel<T, D, true, false, DROP, true, ADQ>>(p, p.nheads * ((p.ntiles + 1) / 2), true, s);
       return hipGetLastError();
     }
   if (causal && masked)
-    launch_units<bwd_dkdv_kernel<T, D, true, true, DROP, false>>(p, units, false, s);
+    launch_units<bwd_dkdv_kernel<T, D, true, true, DROP, false, ADQ>>(p, units, false, s);
   else if (causal)
-    launch_units<bwd_dkdv_kernel<T, D, true, false, DROP, false>>(p, units, false, s);
+    launch_units<bwd_dkdv_kernel<T, D, true, false, DROP, false, ADQ>>(p, units, false, s);
   else if (masked)
-    launch_units<bwd_dkdv_kernel<T, D, false, true, DROP, false>>(p, units, false, s);
+    launch_units<bwd_dkdv_kernel<T, D, false, true, DROP, false, ADQ>>(p, units, false, s);
   else
-    launch_units<bwd_dkdv_kernel<T, D, false, false, DROP, false>>(p, units, false, s);
+    launch_units<bwd_dkdv_kernel<T, D, false, false, DROP, false, ADQ>>(p, units, false, s);
   return hipGetLastError();
+}
+
+// ============================================================================
+// Single-pass backward: pre-pass and conversion
+// ============================================================================
+// D_i = dO_i . O_i for every query row, and the row's float32 dQ accumulator
+// cleared.  D / 8 threads per row, 8 elements each; rows = query heads x N.
+// The sum runs in the dQ kernel's order (two chains of multiply-adds, over
+// elements 16 t + 8 h + i for h = 0 and h = 1, then their sum), so D, and
+// with it dK and dV, are bitwise those of the two-kernel backward.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, size_t rows) {
+  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  const int part = threadIdx.x % TPR;
+  const int base = (threadIdx.x & 63) - part;  // lane of part 0 of this row
+  for (size_t row0 = (size_t)blockIdx.x * RPB; row0 < rows; row0 += (size_t)gridDim.x * RPB) {
+    const size_t row = row0 + threadIdx.x / TPR;
+    float x[8], y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = y[i] = 0.f;
+    if (row < rows) {
+      const size_t e = row * D + part * 8;
+      const typename Vec8<T>::type ov = __builtin_bit_cast(typename Vec8<T>::type, *(const u32x4*)((const T*)p.o + e));
+      const typename Vec8<T>::type gv = __builtin_bit_cast(typename Vec8<T>::type, *(const u32x4*)((const T*)p.dout + e));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[i] = to_f32(gv[i]);
+        y[i] = to_f32(ov[i]);
+      }
+      *(f32x4*)(p.dqacc + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)(p.dqacc + e + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // chain h = part % 2 passes through parts h, h + 2, h + 4, ...
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < TPR / 2; ++t) {
+      float a = acc;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a += x[i] * y[i];
+      acc = __shfl(a, base + 2 * t + (part & 1), 64);
+    }
+    const float lo = __shfl(acc, base, 64), hi = __shfl(acc, base + 1, 64);
+    if (row < rows && part == 0) p.dvec[row] = lo + hi;
+  }
+}
+
+// dq = f * accumulator, rounded to T; n8 groups of 8 elements.
+template <typename T>
+__global__ __launch_bounds__(256) void dq_convert_kernel(const float* acc, T* dq, size_t n8, float f) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+    const f32x4 a = *(const f32x4*)(acc + 8 * i);
+    const f32x4 b = *(const f32x4*)(acc + 8 * i + 4);
+    u32x4 w;
+    w[0] = pack2<T>(a[0] * f, a[1] * f);
+    w[1] = pack2<T>(a[2] * f, a[3] * f);
+    w[2] = pack2<T>(b[0] * f, b[1] * f);
+    w[3] = pack2<T>(b[2] * f, b[3] * f);
+    *(u32x4*)(dq + 8 * i) = w;
+  }
+}
+
+template <typename T, int D, bool DROP>
+static hipError_t single_pass_t(const BwdParams& p, bool causal, bool masked, hipStream_t s) {
+  const size_t rows = (size_t)p.nheads * p.group * p.N;  // query rows
+  constexpr int RPB = 256 / (D / 8);
+  const unsigned pgrid = (unsigned)min((rows + RPB - 1) / RPB, (size_t)65536);
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(pgrid), dim3(256), 0, s, p, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_dkdv_t<T, D, DROP, true>(p, causal, masked, s);
+  if (e != hipSuccess) return e;
+  const size_t n8 = rows * D / 8;
+  const unsigned grid = (unsigned)min((n8 + 255) / 256, (size_t)65536);
+  hipLaunchKernelGGL((dq_convert_kernel<T>), dim3(grid), dim3(256), 0, s, p.dqacc, (T*)p.dq, n8,
+                     DROP ? p.scale * p.drop.mult : p.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_single_pass(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                                  hipStream_t s) {
+  const bool drop = p.drop.t8 != 0;
+  if (dtype == 1) {
+    if (d == 64)
+      return drop ? single_pass_t<_Float16, 64, true>(p, causal, masked, s)
+                  : single_pass_t<_Float16, 64, false>(p, causal, masked, s);
+    return drop ? single_pass_t<_Float16, 128, true>(p, causal, masked, s)
+                : single_pass_t<_Float16, 128, false>(p, causal, masked, s);
+  }
+  if (d == 64)
+    return drop ? single_pass_t<__bf16, 64, true>(p, causal, masked, s)
+                : single_pass_t<__bf16, 64, false>(p, causal, masked, s);
+  return drop ? single_pass_t<__bf16, 128, true>(p, causal, masked, s)
+              : single_pass_t<__bf16, 128, false>(p, causal, masked, s);
 }
 
 template <bool DROP>

@@ -62,6 +62,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* dvec;    // D_i = dO_i . O_i, float32 [B*H*N]
+  float* dqacc;   // single-pass backward: float32 dQ accumulator [B*H*N*d], else null
   int N;
   int nheads;     // dQ kernel: query heads B*H; dK/dV kernel: K/V heads B*H_kv
   int ntiles;     // query tiles (dQ kernel) or key tiles (dK/dV kernel) per head
@@ -219,6 +220,11 @@ hipError_t launch_fwd_drop(const FwdParams& p, int dtype, int d, bool causal, bo
                            hipStream_t s);
 hipError_t launch_bwd_dq_drop(const BwdParams& p, int dtype, int d, bool causal, bool masked,
                               hipStream_t s);
+// Single-pass backward (FA_BWD_ATOMIC_DQ): D and the cleared accumulator,
+// dK/dV with dQ added into p.dqacc by atomics, then dq = scale * accumulator.
+// p as for launch_bwd_dkdv (K/V heads, key tiles), with dq and dqacc set.
+hipError_t launch_bwd_single_pass(const BwdParams& p, int dtype, int d, bool causal, bool masked,
+                                  hipStream_t s);
 hipError_t launch_bwd_dkdv_drop(const BwdParams& p, int dtype, int d, bool causal, bool masked,
                                 hipStream_t s);
 hipError_t launch_decode(const DecParams& p, int dtype, int d, bool causal, hipStream_t s);

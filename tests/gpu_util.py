@@ -37,7 +37,8 @@ def rel_fro(x, ref):
     return num / den if den > 0 else num
 
 
-def run_gpu(q, k, v, do, causal, scale, block_mask, mask_block, backward=True, **ext):
+def run_gpu(q, k, v, do, causal, scale, block_mask, mask_block, backward=True, atomic_dq=False,
+            **ext):
     dev = torch.device("cuda:0")
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
     bm = None if block_mask is None else torch.as_tensor(block_mask, dtype=torch.uint8, device=dev)
@@ -46,7 +47,7 @@ def run_gpu(q, k, v, do, causal, scale, block_mask, mask_block, backward=True, *
     grads = None
     if backward:
         grads = fa_bwd(qd, kd, vd, o, dod, lse, causal=causal, scale=scale, block_mask=bm,
-                       mask_block=mask_block, **ext)
+                       mask_block=mask_block, atomic_dq=atomic_dq, **ext)
     torch.cuda.synchronize()
     return o, lse, grads
 
@@ -140,12 +141,13 @@ def _host32(t):
 
 def check_case(name, B, H, N, d, dtype, causal, scale=None, block_mask=None, mask_block=128,
                heads=None, backward=True, seed=None, window=0, hkv=None, dropout=None,
-               inputs=None):
+               inputs=None, atomic_dq=False):
     """Run one case on the GPU and compare the selected heads (default: every
     head, i.e. the whole tensors) with the oracle.
 
     hkv: K/V heads (grouped-query attention); dropout: (p, seed, offset);
-    inputs: (q, k, v, dO) CPU tensors to use instead of ``make_inputs``.
+    inputs: (q, k, v, dO) CPU tensors to use instead of ``make_inputs``;
+    atomic_dq: run the single-pass backward (FA_BWD_ATOMIC_DQ).
     Returns a dict of the observed errors."""
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     ext = {"window": window}
@@ -155,10 +157,12 @@ def check_case(name, B, H, N, d, dtype, causal, scale=None, block_mask=None, mas
         okw.update(dropout_p=dropout[0], seed=dropout[1], offset=dropout[2])
     say(f"[case] {name}: B={B} H={H} H_kv={hkv or H} N={N} d={d} {dtype} causal={causal} "
         f"mask={'none' if block_mask is None else 'blocks'} window={window} "
-        f"dropout={dropout} heads={'all' if heads is None else heads}")
+        f"dropout={dropout} heads={'all' if heads is None else heads}"
+        f"{' single-pass' if atomic_dq else ''}")
     q, k, v, do = make_inputs(B, H, N, d, dtype, seed, hkv=hkv) if inputs is None else inputs
     g = H // (hkv or H)
-    o, lse, grads = run_gpu(q, k, v, do, causal, scale, block_mask, mask_block, backward, **ext)
+    o, lse, grads = run_gpu(q, k, v, do, causal, scale, block_mask, mask_block, backward,
+                            atomic_dq, **ext)
     outs = (_host32(o), _host32(lse), None if grads is None else tuple(_host32(t) for t in grads))
     del o, lse, grads
     sel = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]

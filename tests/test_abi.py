@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.fa_version() == 10500
+    assert B.fa_version() == 10600
     assert B.fa_status_string(0) == "ok"
     assert "workspace" in B.fa_status_string(B.FA_ERR_WORKSPACE)
     assert B.fa_status_string(12345) == "unknown status"
@@ -111,11 +111,35 @@ def _fwd(p, ws=None, ws_n=0, ptrs=(FAKE,) * 5):
     ({"dropout_p": 1.0}, B.FA_ERR_ARG),
     ({"dropout_p": -0.1}, B.FA_ERR_ARG),
     ({"dropout_p": math.nan}, B.FA_ERR_ARG),
-    ({"flags": 2}, B.FA_ERR_ARG),          # an unknown flag bit
+    ({"flags": 4}, B.FA_ERR_ARG),          # an unknown flag bit
     ({"flags": 0x80000001}, B.FA_ERR_ARG),
 ])
 def test_invalid_problems_rejected(kw, status):
     assert _fwd(_problem(**kw)) == status
+
+
+def test_single_pass_workspace_and_stage_checks():
+    """FA_BWD_ATOMIC_DQ adds the float32 dQ accumulator (B*H*N*d) after D in the
+    backward workspace (16-bit dtypes only), leaves the forward's size alone,
+    and is refused by the two stages of the two-kernel backward and, for
+    float32, by fa_bwd -- all before any GPU call."""
+    L = B.lib()
+    flag = B.FA_BWD_ATOMIC_DQ
+    p, pa = _problem(), _problem(flags=flag)
+    acc = 2 * 3 * 256 * 64 * 4
+    assert B.fa_workspace_size(pa, 0) == B.fa_workspace_size(p, 0)
+    assert B.fa_workspace_size(pa, 1) == B.fa_workspace_size(p, 1) + acc
+    pm, pma = (_problem(N=512, block_mask=0x1000, mask_block=128, flags=f) for f in (0, flag))
+    assert B.fa_workspace_size(pma, 1) == B.fa_workspace_size(pm, 1) + acc * 2
+    pf = _problem(dtype=B.FA_F32, flags=flag)
+    assert B.fa_workspace_size(pf, 1) == B.fa_workspace_size(_problem(dtype=B.FA_F32), 1)
+    args = [FAKE] * 9
+    n = B.fa_workspace_size(pa, 1)
+    assert L.fa_bwd_dq(ctypes.byref(pa), *args[:7], FAKE, n, None) == B.FA_ERR_ARG
+    assert L.fa_bwd_dkdv(ctypes.byref(pa), *args[:7], FAKE, n, None) == B.FA_ERR_ARG
+    assert L.fa_bwd(ctypes.byref(pa), *args, FAKE, n - 256, None) == B.FA_ERR_WORKSPACE
+    assert L.fa_bwd(ctypes.byref(pf), *args, FAKE, B.fa_workspace_size(pf, 1),
+                    None) == B.FA_ERR_UNSUPPORTED
 
 
 def test_null_and_misaligned_pointers_rejected():
