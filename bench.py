@@ -2,7 +2,8 @@
 """Throughput of tiled exact attention, forward + backward, on one MI355X.
 
 One step = the whole path over one batch of the workload: fa_fwd, then the two
-backward stages fa_bwd_dq and fa_bwd_dkdv, all through the C ABI.  Default
+backward stages fa_bwd_dq and fa_bwd_dkdv, all through the C ABI (with
+--backward single-pass: fa_bwd with FA_BWD_ATOMIC_DQ instead).  Default
 workload: GPT-2-medium-shaped attention, B=64 H=16 N=1024 d=64, fp16, causal,
 scale 1/8 (the shape of the paper's headline measurement), synthetic seeded
 inputs already resident in HBM.
@@ -93,6 +94,9 @@ def kernel_work(w):
         "fwd": {"flops": 4.0 * w.d * pairs, "bytes": 2 * x + 2 * xkv + n4},       # Q K V -> O, LSE
         "dq": {"flops": 6.0 * w.d * pairs, "bytes": 4 * x + 2 * xkv + 2 * n4},    # Q K V O dO LSE -> dQ D
         "dkdv": {"flops": 8.0 * w.d * pairs, "bytes": 2 * x + 4 * xkv + 2 * n4},  # Q K V dO LSE D -> dK dV
+        # single-pass backward (pre-pass, dK/dV with atomic dQ, conversion): S, dP,
+        # dV, dK, dQ products = 10 d FLOP/pair; Q K V O dO LSE -> dQ dK dV
+        "bwd": {"flops": 10.0 * w.d * pairs, "bytes": 4 * x + 4 * xkv + n4},
     }
 
 
@@ -336,7 +340,8 @@ def cpu_baseline(w, inputs, seconds):
 
 
 def _short(name):
-    for key in ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "mask_compile", "f32_"):
+    for key in ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_prep_kernel", "dq_convert_kernel",
+                "mask_compile", "f32_"):
         if key in name:
             return key + name[name.find(key) + len(key):][:40]
     return name[:60]
@@ -431,6 +436,9 @@ def main():
                     help="untimed run of the step before the warm-up steps, in ms of wall "
                          "time (clock ramp-up; 0 to skip)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--backward", choices=("two-kernel", "single-pass"), default="two-kernel",
+                    help="backward design: the dQ and dK/dV kernels (default), or one key-outer "
+                         "pass with dQ summed by float32 atomics (FA_BWD_ATOMIC_DQ)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU budget of the oracle baseline (0 to skip)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -464,7 +472,7 @@ def main():
 
     import torch
 
-    from io_aware_exact_fwd_amd import bwd_workspace, fa_bwd_dkdv, fa_bwd_dq, fa_fwd
+    from io_aware_exact_fwd_amd import bwd_workspace, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_into, fa_fwd
     from io_aware_exact_fwd_amd.workloads import WORKLOADS, bwd_flops, fwd_flops, make_inputs
 
     if not torch.cuda.is_available():
@@ -500,8 +508,9 @@ def main():
         ext.update(dropout_p=w.dropout, seed=DROPOUT_SEED, offset=0)
     # one workspace for the whole step: the forward compiles the block lists
     # into it and the backward reuses them (FA_REUSE_LISTS)
+    single = args.backward == "single-pass"
     p, ws, ws_n, bmt = bwd_workspace(q, w.causal, w.scale, bmd, w.mask_block, k=k,
-                                     reuse_lists=bmd is not None, **ext)
+                                     reuse_lists=bmd is not None, atomic_dq=single, **ext)
 
     def step(ev=None):
         if ev is not None:
@@ -509,16 +518,20 @@ def main():
         fa_fwd(q, k, v, w.causal, w.scale, bmt, w.mask_block, out=o, lse=lse, workspace=ws, **ext)
         if ev is not None:
             ev[1].record()
-        fa_bwd_dq(p, q, k, v, o, do, lse, dq, ws, ws_n)
+        if single:
+            fa_bwd_into(p, q, k, v, o, do, lse, dq, dk, dv, ws, ws_n)
+        else:
+            fa_bwd_dq(p, q, k, v, o, do, lse, dq, ws, ws_n)
         if ev is not None:
             ev[2].record()
-        fa_bwd_dkdv(p, q, k, v, do, lse, dk, dv, ws, ws_n)
+        if not single:
+            fa_bwd_dkdv(p, q, k, v, do, lse, dk, dv, ws, ws_n)
         if ev is not None:
             ev[3].record()
 
     log(f"[bench] workload {w.name}: B={w.B} H={w.H} H_kv={w.H_kv} N={w.N} d={w.d} {w.dtype} "
         f"causal={w.causal} mask={w.mask} window={w.window} dropout={w.dropout}; "
-        f"warmup {args.warmup}, steps {args.steps}")
+        f"{args.backward} backward; warmup {args.warmup}, steps {args.steps}")
     settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
@@ -534,11 +547,14 @@ def main():
         wall = time.perf_counter() - t0
     sclk = clock.mean()
 
-    per = {"fwd": [], "dq": [], "dkdv": []}
+    per = {"fwd": [], "bwd": []} if single else {"fwd": [], "dq": [], "dkdv": []}
     for ev in events:
         per["fwd"].append(ev[0].elapsed_time(ev[1]))
-        per["dq"].append(ev[1].elapsed_time(ev[2]))
-        per["dkdv"].append(ev[2].elapsed_time(ev[3]))
+        if single:
+            per["bwd"].append(ev[1].elapsed_time(ev[3]))
+        else:
+            per["dq"].append(ev[1].elapsed_time(ev[2]))
+            per["dkdv"].append(ev[2].elapsed_time(ev[3]))
     ms = {kk: sum(vv) / args.steps for kk, vv in per.items()}
     med = {kk: sorted(vv)[len(vv) // 2] for kk, vv in per.items()}
 
@@ -579,7 +595,9 @@ def main():
         cpu = cpu_baseline(w, inputs, args.cpu_seconds)
 
     out = {
-        "metric": METRIC if w.name == DEFAULT_WORKLOAD else f"attention fwd+bwd TFLOP/s ({w.name}), % of MFMA peak",
+        "metric": (METRIC if w.name == DEFAULT_WORKLOAD and not single else
+                   f"attention fwd+bwd TFLOP/s ({w.name}{', single-pass backward' if single else ''}),"
+                   " % of MFMA peak"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -596,12 +614,13 @@ def main():
                    "block_mask": w.mask,
                    **({"H_kv": w.H_kv} if w.H_kv != w.H else {}),
                    **({"window": w.window} if w.window else {}),
-                   **({"dropout": w.dropout} if w.dropout else {})},
+                   **({"dropout": w.dropout} if w.dropout else {}),
+                   "backward": args.backward},
         "pct_of_mfma_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
         "sclk_mhz": sclk,
         "pct_of_mfma_peak_at_sclk": round(100 * value / peak_at_sclk, 2) if sclk else None,
         "fwd_tflops": round(f_fwd / (ms["fwd"] / 1e3) / 1e12, 2),
-        "bwd_tflops": round(f_bwd / ((ms["dq"] + ms["dkdv"]) / 1e3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / ((ms["bwd"] if single else ms["dq"] + ms["dkdv"]) / 1e3) / 1e12, 2),
         "kernel_ms": {kk: round(vv, 5) for kk, vv in ms.items()},
         "kernel_ms_median": {kk: round(vv, 5) for kk, vv in med.items()},
         "cold_step_ms": round(cold_ms, 4),

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     fa_decode_workspace_size,
     fa_bwd_dkdv,
     fa_bwd_dq,
+    fa_bwd_into,
     fa_fwd,
     fa_fwd_decode,
     fa_fwd_decode_noalloc,

@@ -435,18 +435,29 @@ def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, block_mask=None, mas
 
 
 def bwd_workspace(q, causal=False, scale=None, block_mask=None, mask_block=128, k=None,
-                  window=0, dropout_p=0.0, seed=0, offset=0, reuse_lists=False):
+                  window=0, dropout_p=0.0, seed=0, offset=0, reuse_lists=False, atomic_dq=False):
     """(problem, workspace tensor, workspace bytes, mask) for the two backward
-    stages; reuse_lists sets FA_REUSE_LISTS in the problem (for a workspace
+    stages (or, with atomic_dq, for ``fa_bwd_into`` running the single-pass
+    backward); reuse_lists sets FA_REUSE_LISTS in the problem (for a workspace
     that a forward on the same buffer has filled)."""
     import torch
 
     bm = _mask_arg(block_mask, q, mask_block)
     p = make_problem(q, causal, scale, bm, mask_block, k, window, dropout_p, seed, offset,
-                     FA_REUSE_LISTS if reuse_lists else 0)
+                     (FA_REUSE_LISTS if reuse_lists else 0) | (FA_BWD_ATOMIC_DQ if atomic_dq else 0))
     ws_n = fa_workspace_size(p, 1)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
     return p, ws, ws_n, bm
+
+
+def fa_bwd_into(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_n):
+    """The whole backward (fa_bwd) into given outputs, for a problem and
+    workspace from ``bwd_workspace``."""
+    st = lib().fa_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                      dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                      dv.data_ptr(), ws.data_ptr(), ws_n, _stream(q))
+    if st != FA_OK:
+        raise FaError("fa_bwd", st)
 
 
 def fa_bwd_dq(p, q, k, v, o, dout, lse, dq, ws, ws_n):

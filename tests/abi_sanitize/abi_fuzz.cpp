@@ -88,7 +88,7 @@ fa_problem valid_problem() {
   p.dropout_p = pick(drops);
   p.seed = next_u64();
   p.offset = (uint32_t)next_u64();
-  p.flags = next_u64() % 3 == 0 ? FA_REUSE_LISTS : 0;
+  p.flags = (next_u64() % 3 == 0 ? FA_REUSE_LISTS : 0) | (next_u64() % 3 == 0 ? FA_BWD_ATOMIC_DQ : 0);
   return p;
 }
 
@@ -104,7 +104,7 @@ fa_problem random_problem() {
   static const int32_t mbs[] = {128, 256, 384, 64, 0, -128, 1 << 20};
   static const int32_t wins[] = {0, 0, 1, 300, 1 << 30, -1};
   static const float drops[] = {0.f, 0.f, 0.1f, 0.999f, 1.f, -0.1f, NAN};
-  static const uint32_t flags[] = {0, 0, FA_REUSE_LISTS, 2, 3};
+  static const uint32_t flags[] = {0, 0, FA_REUSE_LISTS, FA_BWD_ATOMIC_DQ, 3, 4, 7, 0x80000000u};
   fa_problem p;
   p.B = pick(bh);
   p.H = pick(bh);
@@ -175,6 +175,28 @@ void one(const fa_problem& p0) {
   st = fa_bwd(&p, Q, K, V, O, DO, (float*)L, DQ, DK, DV, WS, w1, nullptr);
   if (st != FA_OK) {
     CHECK(fa::g_rec.launches == before, "fa_bwd returned %d after launching", st);
+  } else if (p.flags & FA_BWD_ATOMIC_DQ) {
+    // single pass: D, then the float32 dQ accumulator, inside the workspace
+    CHECK(p.dtype != FA_F32, "single-pass backward accepted float32");
+    const fa::BwdParams& s = fa::g_rec.single;
+    const size_t dbytes = (size_t)p.B * p.H * p.N * 4;
+    CHECK(inside(s.dvec, dbytes, WS, w1), "single pass: D outside the workspace");
+    CHECK(inside(s.dqacc, dbytes * (size_t)p.d, WS, w1),
+          "single pass: dQ accumulator outside the workspace (B=%d H=%d N=%d d=%d w1=%zu)", p.B, p.H,
+          p.N, p.d, w1);
+    CHECK((const char*)s.dqacc >= (const char*)s.dvec + dbytes, "accumulator overlaps D");
+    CHECK(s.dq == DQ && s.dk == DK && s.dv == DV, "single pass: output pointers");
+    if (lists) {
+      if (!(p.flags & FA_REUSE_LISTS)) check_lists(p, WS, w1, "fa_bwd single pass");
+      const size_t nb = (size_t)(p.N / p.mask_block);
+      CHECK((const char*)s.dvec >= (const char*)s.m.row_idx + nb * nb * 4, "D overlaps the block lists");
+      CHECK((const char*)s.m.row_ptr == WS, "lists do not start the workspace");
+    }
+    before = fa::g_rec.launches;
+    CHECK(fa_bwd(&p, Q, K, V, O, DO, (float*)L, DQ, DK, DV, WS, w1 - 4, nullptr) == FA_ERR_WORKSPACE, "short bwd ws");
+    CHECK(fa_bwd_dq(&p, Q, K, V, O, DO, (float*)L, DQ, WS, w1, nullptr) == FA_ERR_ARG, "dq stage took the flag");
+    CHECK(fa_bwd_dkdv(&p, Q, K, V, DO, (float*)L, DK, DV, WS, w1, nullptr) == FA_ERR_ARG, "dkdv stage took the flag");
+    CHECK(fa::g_rec.launches == before, "rejected bwd calls launched");
   } else {
     const size_t dbytes = (size_t)p.B * p.H * p.N * 4;
     const float* dvec = p.dtype == FA_F32 ? fa::g_rec.f32.dvec : fa::g_rec.dq.dvec;

@@ -38,6 +38,11 @@ hipError_t launch_bwd_dkdv_drop(const BwdParams& p, int, int, bool, bool, hipStr
   g_rec.dkdv = p;
   return hipSuccess;
 }
+hipError_t launch_bwd_single_pass(const BwdParams& p, int, int, bool, bool, hipStream_t) {
+  ++g_rec.launches;
+  g_rec.single = p;
+  return hipSuccess;
+}
 hipError_t launch_decode(const DecParams& p, int, int, bool, hipStream_t) {
   ++g_rec.launches;
   g_rec.dec = p;

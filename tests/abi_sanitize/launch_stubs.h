@@ -9,7 +9,7 @@ struct Recorded {
   long launches = 0;
   long mask_compiles = 0;
   FwdParams fwd;
-  BwdParams dq, dkdv;
+  BwdParams dq, dkdv, single;  // single: the single-pass backward's launch
   DecParams dec;
   Fp8QuantParams q8;
   int q8_wgs = 0;
