@@ -67,7 +67,14 @@ constexpr int kDkdvWpe128 = 1;
 constexpr int kDkdvWpe64Adq = 2;      // single pass: K^T fragments and the dQ products
 constexpr int kDkdvWpe128Adq = 1;
 constexpr int kDkdvQueries = 64;      // queries per dK/dV step (two 32-query blocks)
-constexpr int kDkdvAhead = 4;         // LDS operand reads issued ahead of the score products
+// LDS operand reads issued ahead of the score products (head dim 64: six of
+// the eight, 1-2 % faster than four; 128: four)
+constexpr int kDkdvAhead64 = 6;
+constexpr int kDkdvAhead128 = 4;
+// dQ: LDS operand reads issued ahead of the score and dP products; at head dim
+// 128 two ahead measured 2 % faster, at 64 no change (and 16 bytes of spill
+// either way)
+constexpr int kDqAhead128 = 2;
 
 // ============================================================================
 // dQ kernel
@@ -204,6 +211,7 @@ void bwd_dq_kernel(BwdParams p) {
             dp[i] = mfma32(b, dof[t], dp[i]);
           }
         }
+        sched_reads_ahead<2 * NKB * G::NKS, D == 128 ? kDqAhead128 : 0>();
         // hide keys outside the row's band (future, outside the window, past
         // the end): key of register r is k0 + g*4 + C(kb, r) with
         // C = kb*32 + (r/4)*8 + r%4; hidden iff C < lb or C > ub
@@ -509,7 +517,7 @@ void bwd_dkdv_kernel(BwdParams p) {
             dp[i] = mfma32(b, vf[t], dp[i]);
           }
         }
-        sched_reads_ahead<2 * NQ * G::NKS, kDkdvAhead>();
+        sched_reads_ahead<2 * NQ * G::NKS, D == 64 ? kDkdvAhead64 : kDkdvAhead128>();
         // hide queries outside this lane's key band (before the key under
         // causal, outside the window, past the end).  Query of register r in
         // block qb is qs0 + g*4 + C(qb, r), C = qb*32 + (r/4)*8 + r%4; hidden

@@ -172,6 +172,9 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int t = 0; t < G::NKS; ++t) s[j] = mfma32(toff.template row_operand<T>(ks, j * 32, t), qf[t], s[j]);
         }
+        // head dim 128: the K operand reads issued four products ahead
+        // (measured 3 % faster; no change at 64)
+        sched_reads_ahead<NKB * G::NKS, D == 128 ? 4 : 0>();
         // 2. mask keys outside the row's band (future keys, keys outside the
         // window, keys past the end).  Key of register r is k0 + g*4 + C(j, r),
         // C = j*32 + (r/4)*8 + r%4; it is hidden iff C < lb or C > ub.
