@@ -200,8 +200,9 @@ int fa_fwd(const fa_problem* p, const void* q, const void* k, const void* v, voi
 namespace {
 
 // Decode geometry: rows per K/V head, row blocks, key tiles (of kDecKeys) and splits.  The
-// split count aims at >= 2048 workgroups (8 per CU) and depends only on the
-// problem, so the workspace size is known before any launch.
+// split count aims at >= 1024 workgroups (4 per CU, two rounds of the two that
+// fit in LDS; 512 and 2048 measured 2 % slower on decode_gqa) and depends only
+// on the problem, so the workspace size is known before any launch.
 struct DecodeShape {
   int rows, nrb, nkv, tile0, ntiles, tps, nsplit;
 };
@@ -217,7 +218,7 @@ DecodeShape decode_shape(const fa_problem* p, int n_q) {
   g.tile0 = lo / fa::kDecKeys;
   g.ntiles = (p->N - 1) / fa::kDecKeys - g.tile0 + 1;
   const int64_t wgs = (int64_t)g.nkv * g.nrb;
-  int want = (int)((2048 + wgs - 1) / wgs);
+  int want = (int)((1024 + wgs - 1) / wgs);
   if (want < 1) want = 1;
   if (want > g.ntiles) want = g.ntiles;
   g.tps = (g.ntiles + want - 1) / want;

@@ -257,6 +257,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p, int tota
     for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
     lse = m + fast_log2(sum) * kLn2;
     const float* po = p.part_o + (size_t)row * ns * D + lane;
+    // eight splits' loads in flight at a time (5 % of the call on decode_gqa)
+#pragma unroll 8
     for (int s = 0; s < ns; ++s) {
       const float w = fast_exp2((pl[s] - lse) * kLog2e);  // 0 for LSE_s = -inf
 #pragma unroll

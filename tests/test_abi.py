@@ -206,14 +206,14 @@ def test_mask_compile_argument_checks():
 
 
 def _decode_splits(B_, Hkv, N, n_q, group, window=0):
-    """The split rule the library documents: >= 2048 workgroups of (K/V head,
+    """The split rule the library documents: >= 1024 workgroups of (K/V head,
     128-row block, key split), never more splits than 32-key tiles."""
     rows = group * n_q
     nrb = (rows + 127) // 128
     lo = max(0, N - n_q - window + 1) if window else 0
     ntiles = (N - 1) // 32 - lo // 32 + 1
     wgs = B_ * Hkv * nrb
-    want = min(max(1, -(-2048 // wgs)), ntiles)
+    want = min(max(1, -(-1024 // wgs)), ntiles)
     tps = -(-ntiles // want)
     return -(-ntiles // tps)
 
@@ -348,7 +348,7 @@ def test_decode_noalloc_checks_before_any_gpu_call():
                                    None) == B.FA_ERR_ARG
     assert L.fa_fwd_decode_noalloc(ctypes.byref(p), 1, FAKE, FAKE, FAKE, FAKE + 4, FAKE,
                                    None) == B.FA_ERR_ARG
-    # 128 rows of one K/V head, 2048 splits of 32 keys, d = 128: 134 MB of partials
+    # 128 rows of one K/V head, 1024 splits of 64 keys, d = 128: 67.6 MB of partials
     big = _problem(B=1, H=8, H_kv=1, N=65536, d=128, causal=1, dtype=B.FA_BF16)
     assert B.fa_decode_workspace_size(big, 16) > B.NOALLOC_SCRATCH_BYTES
     assert L.fa_fwd_decode_noalloc(ctypes.byref(big), 16, FAKE, FAKE, FAKE, FAKE, FAKE,
