@@ -340,8 +340,8 @@ def cpu_baseline(w, inputs, seconds):
 
 
 def _short(name):
-    for key in ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_prep_kernel", "dq_convert_kernel",
-                "mask_compile", "f32_"):
+    for key in ("f32_", "fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_prep_kernel",
+                "dq_convert_kernel", "mask_compile"):
         if key in name:
             return key + name[name.find(key) + len(key):][:40]
     return name[:60]
