@@ -150,8 +150,7 @@ def test_dropout_keep_mask_bit_exact(causal, p, d):
 # A window at least as wide as the sequence hides nothing.  Causal work with a
 # window runs one workgroup per tile; without one, the persistent grid over tile
 # pairs: the two schedules must give bitwise the same outputs (every tile is
-# computed the same way, only their assignment to workgroups differs; the shapes
-# keep both grids on the same side of the split-key threshold).  The
+# computed the same way, only their assignment to workgroups differs).  The
 # dropout case has whole query tiles: in a ragged last tile the rows past N see a
 # band that does depend on the window, and as a wave moves the reference of all
 # its rows together, the rows before N can then differ in rounding (not beyond).
