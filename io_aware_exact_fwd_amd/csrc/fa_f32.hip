@@ -92,59 +92,64 @@ template <int D>
 __global__ __launch_bounds__(kF32Threads) void f32_fwd_kernel(F32Params p) {
   __shared__ float ks[kF32Tile][D + kF32Pad];
   __shared__ float vs[kF32Tile][D + kF32Pad];
+  debug_fill_lds_nan((char*)ks, sizeof(ks));
+  debug_fill_lds_nan((char*)vs, sizeof(vs));
   const int head = blockIdx.x;
   const int sub = threadIdx.x % kF32Split;
-  const int q = blockIdx.y * kF32Rows + threadIdx.x / kF32Split;
-  const size_t hoff = (size_t)head * p.N * D;
-  const size_t kvoff = (size_t)(head / p.group) * p.N * D;
-  float qv[D], o[D];
+  const int nrb = (p.N + kF32Rows - 1) / kF32Rows;
+  for (int rb = blockIdx.y; rb < nrb; rb += gridDim.y) {
+    const int q = rb * kF32Rows + threadIdx.x / kF32Split;
+    const size_t hoff = (size_t)head * p.N * D;
+    const size_t kvoff = (size_t)(head / p.group) * p.N * D;
+    float qv[D], o[D];
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    qv[c] = q < p.N ? p.q[hoff + (size_t)q * D + c] : 0.f;
-    o[c] = 0.f;
-  }
-  // this lane's share of the row: running maximum and sum (base 2)
-  float m = -INFINITY, l = 0.f;
-  for (int j0 = 0; j0 < p.N; j0 += kF32Tile) {
-    __syncthreads();
-    f32_stage<D>(ks, vs, p.k + kvoff, p.v + kvoff, j0, p.N);
-    __syncthreads();
-#pragma unroll 1
-    for (int jj = sub; jj < kF32Tile; jj += kF32Split) {
-      if (!f32_visible(p, q, j0 + jj)) continue;
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < D; ++c) acc = fmaf(qv[c], ks[jj][c], acc);
-      const float sc = acc * p.c;
-      if (sc > m) {
-        const float alpha = exp2f(m - sc);
-        l *= alpha;
-#pragma unroll
-        for (int c = 0; c < D; ++c) o[c] *= alpha;
-        m = sc;
-      }
-      const float e = exp2f(sc - m);
-      l += e;  // the row sum normalises P itself; dropout acts on the weights only
-      const float ez = e * f32_drop(p, head, q, j0 + jj);
-#pragma unroll
-      for (int c = 0; c < D; ++c) o[c] = fmaf(ez, vs[jj][c], o[c]);
+    for (int c = 0; c < D; ++c) {
+      qv[c] = q < p.N ? p.q[hoff + (size_t)q * D + c] : 0.f;
+      o[c] = 0.f;
     }
-  }
-  // merge the group's states at the row's maximum (a lane that saw no
-  // key, m = -inf, contributes nothing)
-  const float mt = f32_group_max(m);
-  const float a = m == -INFINITY ? 0.f : exp2f(m - mt);
-  const float lt = f32_group_sum(l * a);
+    // this lane's share of the row: running maximum and sum (base 2)
+    float m = -INFINITY, l = 0.f;
+    for (int j0 = 0; j0 < p.N; j0 += kF32Tile) {
+      __syncthreads();
+      f32_stage<D>(ks, vs, p.k + kvoff, p.v + kvoff, j0, p.N);
+      __syncthreads();
+#pragma unroll 1
+      for (int jj = sub; jj < kF32Tile; jj += kF32Split) {
+        if (!f32_visible(p, q, j0 + jj)) continue;
+        float acc = 0.f;
 #pragma unroll
-  for (int c = 0; c < D; ++c) o[c] = f32_group_sum(o[c] * a);
-  if (q < p.N) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    // lane s of the group stores columns s, s + 32, ...
+        for (int c = 0; c < D; ++c) acc = fmaf(qv[c], ks[jj][c], acc);
+        const float sc = acc * p.c;
+        if (sc > m) {
+          const float alpha = exp2f(m - sc);
+          l *= alpha;
 #pragma unroll
-    for (int c = 0; c < D; ++c)
-      if (c % kF32Split == sub) p.out_o[hoff + (size_t)q * D + c] = o[c] * inv;
-    // -inf for a row without a visible key; a NaN row sum stays NaN
-    if (sub == 0) p.lse[(size_t)head * p.N + q] = !(lt <= 0.f) ? (mt + log2f(lt)) * kLn2 : -INFINITY;
+          for (int c = 0; c < D; ++c) o[c] *= alpha;
+          m = sc;
+        }
+        const float e = exp2f(sc - m);
+        l += e;  // the row sum normalises P itself; dropout acts on the weights only
+        const float ez = e * f32_drop(p, head, q, j0 + jj);
+#pragma unroll
+        for (int c = 0; c < D; ++c) o[c] = fmaf(ez, vs[jj][c], o[c]);
+      }
+    }
+    // merge the group's states at the row's maximum (a lane that saw no
+    // key, m = -inf, contributes nothing)
+    const float mt = f32_group_max(m);
+    const float a = m == -INFINITY ? 0.f : exp2f(m - mt);
+    const float lt = f32_group_sum(l * a);
+#pragma unroll
+    for (int c = 0; c < D; ++c) o[c] = f32_group_sum(o[c] * a);
+    if (q < p.N) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      // lane s of the group stores columns s, s + 32, ...
+#pragma unroll
+      for (int c = 0; c < D; ++c)
+        if (c % kF32Split == sub) p.out_o[hoff + (size_t)q * D + c] = o[c] * inv;
+      // -inf for a row without a visible key; a NaN row sum stays NaN
+      if (sub == 0) p.lse[(size_t)head * p.N + q] = !(lt <= 0.f) ? (mt + log2f(lt)) * kLn2 : -INFINITY;
+    }
   }
 }
 
@@ -152,52 +157,57 @@ template <int D>
 __global__ __launch_bounds__(kF32Threads) void f32_dq_kernel(F32Params p) {
   __shared__ float ks[kF32Tile][D + kF32Pad];
   __shared__ float vs[kF32Tile][D + kF32Pad];
+  debug_fill_lds_nan((char*)ks, sizeof(ks));
+  debug_fill_lds_nan((char*)vs, sizeof(vs));
   const int head = blockIdx.x;
   const int sub = threadIdx.x % kF32Split;
-  const int q = blockIdx.y * kF32Rows + threadIdx.x / kF32Split;
-  const size_t hoff = (size_t)head * p.N * D;
-  const size_t kvoff = (size_t)(head / p.group) * p.N * D;
-  float qv[D], dov[D], dq[D];
-  float dd = 0.f;
+  const int nrb = (p.N + kF32Rows - 1) / kF32Rows;
+  for (int rb = blockIdx.y; rb < nrb; rb += gridDim.y) {
+    const int q = rb * kF32Rows + threadIdx.x / kF32Split;
+    const size_t hoff = (size_t)head * p.N * D;
+    const size_t kvoff = (size_t)(head / p.group) * p.N * D;
+    float qv[D], dov[D], dq[D];
+    float dd = 0.f;
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    const bool in = q < p.N;
-    qv[c] = in ? p.q[hoff + (size_t)q * D + c] : 0.f;
-    dov[c] = in ? p.dout[hoff + (size_t)q * D + c] : 0.f;
-    dd = fmaf(dov[c], in ? p.o[hoff + (size_t)q * D + c] : 0.f, dd);
-    dq[c] = 0.f;
-  }
-  float lse2 = INFINITY;
-  if (q < p.N) {
-    const float l = p.lse[(size_t)head * p.N + q];
-    if (l != -INFINITY) lse2 = l * kLog2e;
-    if (sub == 0) p.dvec[(size_t)head * p.N + q] = dd;
-  }
-  for (int j0 = 0; j0 < p.N; j0 += kF32Tile) {
-    __syncthreads();
-    f32_stage<D>(ks, vs, p.k + kvoff, p.v + kvoff, j0, p.N);
-    __syncthreads();
-#pragma unroll 1
-    for (int jj = sub; jj < kF32Tile; jj += kF32Split) {
-      if (!f32_visible(p, q, j0 + jj)) continue;
-      float s = 0.f, dp = 0.f;
-#pragma unroll
-      for (int c = 0; c < D; ++c) {
-        s = fmaf(qv[c], ks[jj][c], s);
-        dp = fmaf(dov[c], vs[jj][c], dp);
-      }
-      const float pr = exp2f(s * p.c - lse2);
-      const float ds = pr * (dp * f32_drop(p, head, q, j0 + jj) - dd) * p.scale;
-#pragma unroll
-      for (int c = 0; c < D; ++c) dq[c] = fmaf(ds, ks[jj][c], dq[c]);
+    for (int c = 0; c < D; ++c) {
+      const bool in = q < p.N;
+      qv[c] = in ? p.q[hoff + (size_t)q * D + c] : 0.f;
+      dov[c] = in ? p.dout[hoff + (size_t)q * D + c] : 0.f;
+      dd = fmaf(dov[c], in ? p.o[hoff + (size_t)q * D + c] : 0.f, dd);
+      dq[c] = 0.f;
     }
-  }
+    float lse2 = INFINITY;
+    if (q < p.N) {
+      const float l = p.lse[(size_t)head * p.N + q];
+      if (l != -INFINITY) lse2 = l * kLog2e;
+      if (sub == 0) p.dvec[(size_t)head * p.N + q] = dd;
+    }
+    for (int j0 = 0; j0 < p.N; j0 += kF32Tile) {
+      __syncthreads();
+      f32_stage<D>(ks, vs, p.k + kvoff, p.v + kvoff, j0, p.N);
+      __syncthreads();
+#pragma unroll 1
+      for (int jj = sub; jj < kF32Tile; jj += kF32Split) {
+        if (!f32_visible(p, q, j0 + jj)) continue;
+        float s = 0.f, dp = 0.f;
 #pragma unroll
-  for (int c = 0; c < D; ++c) dq[c] = f32_group_sum(dq[c]);
-  if (q < p.N) {
+        for (int c = 0; c < D; ++c) {
+          s = fmaf(qv[c], ks[jj][c], s);
+          dp = fmaf(dov[c], vs[jj][c], dp);
+        }
+        const float pr = exp2f(s * p.c - lse2);
+        const float ds = pr * (dp * f32_drop(p, head, q, j0 + jj) - dd) * p.scale;
 #pragma unroll
-    for (int c = 0; c < D; ++c)
-      if (c % kF32Split == sub) p.dq[hoff + (size_t)q * D + c] = dq[c];
+        for (int c = 0; c < D; ++c) dq[c] = fmaf(ds, ks[jj][c], dq[c]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < D; ++c) dq[c] = f32_group_sum(dq[c]);
+    if (q < p.N) {
+#pragma unroll
+      for (int c = 0; c < D; ++c)
+        if (c % kF32Split == sub) p.dq[hoff + (size_t)q * D + c] = dq[c];
+    }
   }
 }
 
@@ -207,89 +217,105 @@ __global__ __launch_bounds__(kF32Threads) void f32_dkdv_kernel(F32Params p) {
   __shared__ float dos[kF32Tile][D + kF32Pad];
   __shared__ float l2s[kF32Tile];
   __shared__ float dds[kF32Tile];
+  debug_fill_lds_nan((char*)qs, sizeof(qs));
+  debug_fill_lds_nan((char*)dos, sizeof(dos));
+  debug_fill_lds_nan((char*)l2s, sizeof(l2s));
+  debug_fill_lds_nan((char*)dds, sizeof(dds));
   const int kvh = blockIdx.x;  // K/V head; its query heads are kvh * group + r
   const int sub = threadIdx.x % kF32Split;
-  const int kj = blockIdx.y * kF32Rows + threadIdx.x / kF32Split;
-  const size_t kvoff = (size_t)kvh * p.N * D;
-  float kv[D], vv[D], dk[D], dv[D];
+  const int nrb = (p.N + kF32Rows - 1) / kF32Rows;
+  for (int rb = blockIdx.y; rb < nrb; rb += gridDim.y) {
+    const int kj = rb * kF32Rows + threadIdx.x / kF32Split;
+    const size_t kvoff = (size_t)kvh * p.N * D;
+    float kv[D], vv[D], dk[D], dv[D];
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    const bool in = kj < p.N;
-    kv[c] = in ? p.k[kvoff + (size_t)kj * D + c] : 0.f;
-    vv[c] = in ? p.v[kvoff + (size_t)kj * D + c] : 0.f;
-    dk[c] = 0.f;
-    dv[c] = 0.f;
-  }
-  for (int r = 0; r < p.group; ++r) {
-    const int head = kvh * p.group + r;
-    const size_t hoff = (size_t)head * p.N * D;
-    for (int i0 = 0; i0 < p.N; i0 += kF32Tile) {
-      __syncthreads();
-      f32_stage<D>(qs, dos, p.q + hoff, p.dout + hoff, i0, p.N);
-      if (threadIdx.x < kF32Tile) {
-        const int qi = i0 + threadIdx.x;
-        float l2 = INFINITY, dd = 0.f;
-        if (qi < p.N) {
-          const float l = p.lse[(size_t)head * p.N + qi];
-          if (l != -INFINITY) l2 = l * kLog2e;
-          dd = p.dvec[(size_t)head * p.N + qi];
+    for (int c = 0; c < D; ++c) {
+      const bool in = kj < p.N;
+      kv[c] = in ? p.k[kvoff + (size_t)kj * D + c] : 0.f;
+      vv[c] = in ? p.v[kvoff + (size_t)kj * D + c] : 0.f;
+      dk[c] = 0.f;
+      dv[c] = 0.f;
+    }
+    for (int r = 0; r < p.group; ++r) {
+      const int head = kvh * p.group + r;
+      const size_t hoff = (size_t)head * p.N * D;
+      for (int i0 = 0; i0 < p.N; i0 += kF32Tile) {
+        __syncthreads();
+        f32_stage<D>(qs, dos, p.q + hoff, p.dout + hoff, i0, p.N);
+        if (threadIdx.x < kF32Tile) {
+          const int qi = i0 + threadIdx.x;
+          float l2 = INFINITY, dd = 0.f;
+          if (qi < p.N) {
+            const float l = p.lse[(size_t)head * p.N + qi];
+            if (l != -INFINITY) l2 = l * kLog2e;
+            dd = p.dvec[(size_t)head * p.N + qi];
+          }
+          l2s[threadIdx.x] = l2;
+          dds[threadIdx.x] = dd;
         }
-        l2s[threadIdx.x] = l2;
-        dds[threadIdx.x] = dd;
-      }
-      __syncthreads();
+        __syncthreads();
 #pragma unroll 1
-      for (int ii = sub; ii < kF32Tile; ii += kF32Split) {
-        if (!f32_visible(p, i0 + ii, kj)) continue;
-        float s = 0.f, dp = 0.f;
+        for (int ii = sub; ii < kF32Tile; ii += kF32Split) {
+          if (!f32_visible(p, i0 + ii, kj)) continue;
+          float s = 0.f, dp = 0.f;
 #pragma unroll
-        for (int c = 0; c < D; ++c) {
-          s = fmaf(qs[ii][c], kv[c], s);
-          dp = fmaf(dos[ii][c], vv[c], dp);
-        }
-        const float pr = exp2f(s * p.c - l2s[ii]);
-        const float z = f32_drop(p, head, i0 + ii, kj);
-        const float ds = pr * (dp * z - dds[ii]) * p.scale;
-        const float pz = pr * z;
+          for (int c = 0; c < D; ++c) {
+            s = fmaf(qs[ii][c], kv[c], s);
+            dp = fmaf(dos[ii][c], vv[c], dp);
+          }
+          const float pr = exp2f(s * p.c - l2s[ii]);
+          const float z = f32_drop(p, head, i0 + ii, kj);
+          const float ds = pr * (dp * z - dds[ii]) * p.scale;
+          const float pz = pr * z;
 #pragma unroll
-        for (int c = 0; c < D; ++c) {
-          dv[c] = fmaf(pz, dos[ii][c], dv[c]);
-          dk[c] = fmaf(ds, qs[ii][c], dk[c]);
+          for (int c = 0; c < D; ++c) {
+            dv[c] = fmaf(pz, dos[ii][c], dv[c]);
+            dk[c] = fmaf(ds, qs[ii][c], dk[c]);
+          }
         }
       }
     }
-  }
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    dk[c] = f32_group_sum(dk[c]);
-    dv[c] = f32_group_sum(dv[c]);
-  }
-  if (kj < p.N) {
+    for (int c = 0; c < D; ++c) {
+      dk[c] = f32_group_sum(dk[c]);
+      dv[c] = f32_group_sum(dv[c]);
+    }
+    if (kj < p.N) {
 #pragma unroll
-    for (int c = 0; c < D; ++c)
-      if (c % kF32Split == sub) {
-        p.dk[kvoff + (size_t)kj * D + c] = dk[c];
-        p.dv[kvoff + (size_t)kj * D + c] = dv[c];
-      }
+      for (int c = 0; c < D; ++c)
+        if (c % kF32Split == sub) {
+          p.dk[kvoff + (size_t)kj * D + c] = dk[c];
+          p.dv[kvoff + (size_t)kj * D + c] = dv[c];
+        }
+    }
   }
 }
 
+// (heads, row blocks): the kernels loop over row blocks with a stride of
+// gridDim.y, kept below 2^16 (the runtime's limit for that dimension); the
+// debug build keeps it at 3, so that its tests run that loop many rounds
+static dim3 f32_grid(const F32Params& p) {
+  const int nrb = (p.N + kF32Rows - 1) / kF32Rows;
+  const int cap = kDebugBuild ? 3 : 65535;
+  return dim3(p.nheads, nrb < cap ? nrb : cap);
+}
+
 hipError_t launch_f32_fwd(const F32Params& p, hipStream_t s) {
-  dim3 grid(p.nheads, (p.N + kF32Rows - 1) / kF32Rows), block(kF32Threads);
+  const dim3 grid = f32_grid(p), block(kF32Threads);
   if (p.d == 64) hipLaunchKernelGGL(f32_fwd_kernel<64>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(f32_fwd_kernel<128>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_f32_dq(const F32Params& p, hipStream_t s) {
-  dim3 grid(p.nheads, (p.N + kF32Rows - 1) / kF32Rows), block(kF32Threads);
+  const dim3 grid = f32_grid(p), block(kF32Threads);
   if (p.d == 64) hipLaunchKernelGGL(f32_dq_kernel<64>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(f32_dq_kernel<128>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_f32_dkdv(const F32Params& p, hipStream_t s) {
-  dim3 grid(p.nheads, (p.N + kF32Rows - 1) / kF32Rows), block(kF32Threads);
+  const dim3 grid = f32_grid(p), block(kF32Threads);
   if (p.d == 64) hipLaunchKernelGGL(f32_dkdv_kernel<64>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(f32_dkdv_kernel<128>, grid, block, 0, s, p);
   return hipGetLastError();

@@ -3,8 +3,11 @@
 1. NaN-filled LDS: every tiled kernel of the debug build fills its LDS with NaN
    before first use.  Its outputs must equal the production library's bit for
    bit (and be finite), on ragged shapes, masks, windows, grouped heads,
-   dropout, the decode shape and the FP8 path: no kernel reads LDS it has not
-   written.
+   dropout, the decode shape, the FP8 path and the float32 path: no kernel
+   reads LDS it has not written.  The float32 kernels of the debug build also
+   run on a grid of at most 3 row blocks per head, each workgroup looping over
+   many, so the same equality covers that loop (which the production library
+   reaches only past N = 524,280).
 2. Tile visits: the forward, dQ and dK/dV kernels of the debug build count the
    tiles they load.  A tile must be loaded exactly when some row of the
    workgroup sees some key of it under the visibility definition (the
@@ -63,7 +66,14 @@ def _run(case, lib_path=None, visits=None):
     return (o, lse, *g), bm
 
 
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+F32_CASES = [
+    ("f32-d64-ragged-causal", 1, 2, 2, 1000, 64, "f32", True, 0, None, 0.0),
+    ("f32-d128-window-gqa", 1, 4, 2, 700, 128, "f32", False, 150, None, 0.0),
+    ("f32-d64-blocks-dropout", 1, 2, 1, 1024, 64, "f32", True, 0, "holes", 0.25),
+]
+
+
+@pytest.mark.parametrize("case", CASES + F32_CASES, ids=[c[0] for c in CASES + F32_CASES])
 def test_nan_filled_lds_changes_nothing(case):
     say(f"[case] NaN LDS {case[0]}")
     prod, _ = _run(case)
