@@ -1,7 +1,8 @@
 """Seeded random combinations of the problem's features against the fp64
 oracle (MI355X only): sequence lengths with ragged ends, both head dims and
 16-bit dtypes, causal or not, sliding windows, grouped K/V heads, random
-block masks (with empty rows and columns), dropout, and either backward.
+block masks (with empty rows and columns), dropout, and either backward; and
+a second draw of the same features through the float32 path.
 Each case compares the whole tensors with the stated tolerances, like the
 hand-picked cases; the draw is fixed, so a failure names a reproducible
 configuration.  bfloat16 O is gated as for large logits: |O - O_ref| <= 1e-2 +
@@ -47,7 +48,7 @@ def _draw(i):
                 block_mask=bm, dropout=dropout, atomic_dq=atomic_dq, seed=seed)
 
 
-CASES = list(range(120))
+CASES = list(range(400))
 
 
 @pytest.mark.parametrize("i", CASES)
@@ -61,3 +62,35 @@ def test_random_combination(i):
                hkv=c["hkv"] if c["hkv"] != c["H"] else None, dropout=c["dropout"],
                seed=c["seed"], atomic_dq=c["atomic_dq"],
                o_rel=2.0 ** -8 if c["dtype"] == "bf16" else 0.0)
+
+
+def _draw_f32(i):
+    """The float32 path: the same features except the single-pass backward
+    (16-bit only), shorter sequences."""
+    rng = np.random.default_rng(50000 + i)
+    d = int(rng.choice([64, 128]))
+    H_kv = int(rng.choice([1, 2]))
+    H = H_kv * int(rng.choice([1, 2, 3]))
+    masked = rng.random() < 0.3
+    N = 128 * int(rng.integers(1, 6)) if masked else int(rng.integers(1, 700))
+    causal = bool(rng.random() < 0.6)
+    window = int(rng.choice([0, 0, int(rng.integers(1, 400))]))
+    bm = None
+    if masked:
+        nb = N // 128
+        bm = (rng.random((nb, nb)) < 0.5).astype(np.uint8)
+    dropout = None
+    if rng.random() < 0.25:
+        dropout = (float(rng.choice([0.1, 0.3])), int(rng.integers(0, 2**31)), int(rng.integers(0, 1000)))
+    return dict(H=H, hkv=H_kv, N=N, d=d, causal=causal, window=window, block_mask=bm,
+                dropout=dropout, seed=int(rng.integers(0, 2**31)))
+
+
+@pytest.mark.parametrize("i", list(range(40)))
+def test_random_combination_f32(i):
+    c = _draw_f32(i)
+    name = (f"random-f32-{i}-d{c['d']}-H{c['H']}kv{c['hkv']}-N{c['N']}-c{int(c['causal'])}"
+            f"-w{c['window']}-mask{int(c['block_mask'] is not None)}-drop{c['dropout'] is not None}")
+    check_case(name, 1, c["H"], c["N"], c["d"], "f32", c["causal"], block_mask=c["block_mask"],
+               mask_block=128, window=c["window"], hkv=c["hkv"] if c["hkv"] != c["H"] else None,
+               dropout=c["dropout"], seed=c["seed"])
