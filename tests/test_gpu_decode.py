@@ -4,8 +4,9 @@ The last n_q positions of a sequence against its N keys: fp64 oracle with the
 query offset N - n_q on the same seeded inputs, covering one and several
 queries, grouped heads (rows of several query heads per workgroup, more than
 one 128-row block), causal and windowed visibility, ragged key counts, a
-single key, the split path and the direct (one split) path, and the decode
-workload at full size.  Q = 0 makes LSE an exact count of the visible keys."""
+single key, the split path and the direct (one split) path, the decode
+workload at full size, and 60 seeded random problems over the same features.
+Q = 0 makes LSE an exact count of the visible keys."""
 
 import numpy as np
 import pytest
@@ -110,3 +111,26 @@ def test_decode_repeatable():
     o2, l2 = fa_fwd_decode(qd, kd, vd, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _draw_decode(i):
+    """Seeded random decode problems: either dtype and head dim, grouped heads,
+    ragged key counts (a single key included), one or several queries,
+    causal or not, with or without a window."""
+    rng = np.random.default_rng(70000 + i)
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    hkv = int(rng.choice([1, 2, 4]))
+    H = hkv * int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.choice([1, 2]))
+    N = int(rng.integers(1, 6000))
+    nq = int(min(N, rng.choice([1, 1, 2, 3, int(rng.integers(1, 65))])))
+    causal = bool(rng.random() < 0.7)
+    window = int(rng.choice([0, 0, int(rng.integers(1, 1500))]))
+    return dtype, d, B, H, hkv, N, nq, causal, window
+
+
+@pytest.mark.parametrize("i", list(range(60)))
+def test_decode_random(i):
+    dtype, d, B, H, hkv, N, nq, causal, window = _draw_decode(i)
+    _decode_case(f"decode-random{i}", B, H, hkv, N, nq, d, dtype, causal, window)

@@ -188,6 +188,26 @@ def test_fp8_matches_oracle(kind, dtype, d, B, H, hkv, N, causal, window, qmul):
                      H // hkv, N, heads)
 
 
+def _draw_fp8(i):
+    """Seeded random FP8 problems: input kind, dtype, head dim, grouped heads,
+    ragged lengths, causal or not, windows, peaked rows."""
+    rng = np.random.default_rng(80000 + i)
+    kind = str(rng.choice(["normal", "outlier", "rising"]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2]))
+    H = hkv * int(rng.choice([1, 2, 3]))
+    N = int(rng.integers(1, 1600))
+    causal = bool(rng.random() < 0.6)
+    window = int(rng.choice([0, 0, int(rng.integers(1, 500))]))
+    qmul = float(rng.choice([1.0, 1.0, 4.0]))
+    return kind, dtype, d, 1, H, hkv, N, causal, window, qmul
+
+
+@pytest.mark.parametrize("i", list(range(30)))
+def test_fp8_random(i):
+    test_fp8_matches_oracle(*_draw_fp8(i))
+
 def test_fp8_repeatable():
     """Two calls on the same inputs give the same bits."""
     q, k, v = _inputs("normal", 1, 4, 2, 777, 128, "bf16")
