@@ -32,21 +32,23 @@ __device__ int block_sum(int v, int* lds) {
   return t;
 }
 
-// Exclusive prefix sum over the workgroup's threads in thread order.
+// Exclusive prefix sum over the workgroup's threads in thread order: an
+// inclusive scan inside each wave (log2 64 lane shifts), then each wave adds
+// the totals of the waves before it (lds: kMaskThreads / 64 words).
 __device__ int block_exclusive_scan(int v, int* lds) {
-  __syncthreads();
-  lds[threadIdx.x] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < kMaskThreads; ++i) {
-      const int x = lds[i];
-      lds[i] = run;
-      run += x;
-    }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
+  __syncthreads();  // earlier readers of lds are done
+  if (lane == 63) lds[wave] = x;
   __syncthreads();
-  return lds[threadIdx.x];
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += lds[w];
+  return base + x - v;
 }
 
 __global__ __launch_bounds__(kMaskThreads) void mask_count_kernel(const uint8_t* mask, int nb,
@@ -81,7 +83,7 @@ __device__ void offsets_in_place(int32_t* a, int nb, int* lds) {
 
 __global__ __launch_bounds__(kMaskThreads) void mask_scan_kernel(int nb, int32_t* row_ptr,
                                                                  int32_t* col_ptr) {
-  __shared__ int lds[kMaskThreads];
+  __shared__ int lds[kMaskThreads / 64];
   offsets_in_place(row_ptr, nb, lds);
   offsets_in_place(col_ptr, nb, lds);
 }
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(kMaskThreads) void mask_fill_kernel(const uint8_t* 
                                                                  int32_t* col_idx,
                                                                  const int32_t* col_ptr,
                                                                  int32_t* row_idx) {
-  __shared__ int lds[kMaskThreads];
+  __shared__ int lds[kMaskThreads / 64];
   const int g = blockIdx.x;
   const int per = (nb + kMaskThreads - 1) / kMaskThreads;
   const int lo = min(nb, (int)threadIdx.x * per), hi = min(nb, lo + per);
