@@ -306,9 +306,17 @@ void bwd_dq_kernel(BwdParams p) {
       for (int e = 0; e < nsub; ++e) tile(head, e == 0 ? p.ntiles - 1 - u : u);
     }
   } else {
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int head = logical / p.ntiles, qt = logical % p.ntiles;
-    tile(head, CAUSAL ? p.ntiles - 1 - qt : qt);  // causal: the longer rows first
+    // causal: the longer rows first (one call of the tile body, so that it is
+    // inlined once)
+    int head, qt;
+    if (CAUSAL && p.spread > 0) {
+      spread_tile(blockIdx.x, p.nheads, p.ntiles, p.spread, head, qt);
+    } else {
+      const int logical = xcd_remap(blockIdx.x, gridDim.x);
+      head = logical / p.ntiles;
+      qt = logical % p.ntiles;
+    }
+    tile(head, CAUSAL ? p.ntiles - 1 - qt : qt);
   }
 }
 
@@ -690,23 +698,41 @@ void bwd_dkdv_kernel(BwdParams p) {
       for (int e = 0; e < nsub; ++e) tile(kvh, e == 0 ? u : p.ntiles - 1 - u);
     }
   } else {
-    // in order: under causal masking the longer columns first
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    tile(logical / p.ntiles, logical % p.ntiles);
+    // in order: under causal masking the longer columns first (key tile 0
+    // sees every query); one call of the tile body, so that it is inlined once
+    int kvh, kt;
+    if (CAUSAL && p.spread > 0) {
+      spread_tile(blockIdx.x, p.nheads, p.ntiles, p.spread, kvh, kt);
+    } else {
+      const int logical = xcd_remap(blockIdx.x, gridDim.x);
+      kvh = logical / p.ntiles;
+      kt = logical % p.ntiles;
+    }
+    tile(kvh, kt);
   }
 }
 
 template <typename T, int D, bool DROP>
-static hipError_t launch_dq_t(const BwdParams& p, bool causal, bool masked, hipStream_t s) {
+static hipError_t launch_dq_t(const BwdParams& p_in, bool causal, bool masked, hipStream_t s) {
+  BwdParams p = p_in;
+  p.spread = 0;
   const int units = p.nheads * p.ntiles;
-  // causal work without a window or block mask runs on a persistent grid over
-  // tile pairs (not under dropout at head dim 64: the unit loop's registers
-  // would spill); the rest one workgroup per tile
-  if constexpr (!(DROP && D == 64))
-    if (causal && !masked && p.window == 0) {
+  // causal work without a window or block mask: one workgroup per tile in the
+  // spread order when all tiles fit on the GPU at once, else a persistent grid
+  // over tile pairs (not under dropout at head dim 64: the unit loop's
+  // registers would spill); the rest one workgroup per tile
+  if (causal && !masked && p.window == 0) {
+    constexpr auto kTile = bwd_dq_kernel<T, D, true, false, DROP, false>;
+    p.spread = spread_for<kTile>(p.nheads, p.ntiles);
+    if (p.spread > 0) {
+      launch_units<kTile>(p, units, false, s);
+      return hipGetLastError();
+    }
+    if constexpr (!(DROP && D == 64)) {
       launch_units<bwd_dq_kernel<T, D, true, false, DROP, true>>(p, p.nheads * ((p.ntiles + 1) / 2), true, s);
       return hipGetLastError();
     }
+  }
   if (causal && masked)
     launch_units<bwd_dq_kernel<T, D, true, true, DROP, false>>(p, units, false, s);
   else if (causal)
@@ -719,16 +745,26 @@ static hipError_t launch_dq_t(const BwdParams& p, bool causal, bool masked, hipS
 }
 
 template <typename T, int D, bool DROP, bool ADQ = false>
-static hipError_t launch_dkdv_t(const BwdParams& p, bool causal, bool masked, hipStream_t s) {
+static hipError_t launch_dkdv_t(const BwdParams& p_in, bool causal, bool masked, hipStream_t s) {
+  BwdParams p = p_in;
+  p.spread = 0;
   const int units = p.nheads * p.ntiles;
-  // causal work without a window or block mask runs on a persistent grid over
-  // tile pairs at head dim 64 (at 128, one wave per SIMD, one workgroup per
-  // tile measured faster); the rest one workgroup per tile
-  if constexpr (D == 64)
-    if (causal && !masked && p.window == 0) {
+  // causal work without a window or block mask: one workgroup per tile in the
+  // spread order when all tiles fit on the GPU at once, else a persistent grid
+  // over tile pairs at head dim 64 (at 128, one wave per SIMD, one workgroup
+  // per tile measured faster); the rest one workgroup per tile
+  if (causal && !masked && p.window == 0) {
+    constexpr auto kTile = bwd_dkdv_kernel<T, D, true, false, DROP, false, ADQ>;
+    p.spread = spread_for<kTile>(p.nheads, p.ntiles);
+    if (p.spread > 0) {
+      launch_units<kTile>(p, units, false, s);
+      return hipGetLastError();
+    }
+    if constexpr (D == 64) {
       launch_units<bwd_dkdv_kernel<T, D, true, false, DROP, true, ADQ>>(p, p.nheads * ((p.ntiles + 1) / 2), true, s);
       return hipGetLastError();
     }
+  }
   if (causal && masked)
     launch_units<bwd_dkdv_kernel<T, D, true, true, DROP, false, ADQ>>(p, units, false, s);
   else if (causal)

@@ -275,6 +275,27 @@ __device__ __forceinline__ int xcd_remap(int linear, int total) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// Causal work on a small grid (every tile of the launch resident at once, one
+// workgroup per tile): the time is the most loaded CU's, so spread the cost
+// evenly over CUs.  Workgroup b goes to XCD b mod 8 and, within the XCD, the
+// dispatcher fills its CUs in order; XCD x takes the tiles of heads
+// [x hx, (x+1) hx) (hx = nheads / 8), sorted by cost (level 0 the costliest),
+// and deals them to its cpx CUs in rounds that alternate direction, so that
+// each CU's tiles add up to about the same number of key-tile steps.
+// A bijection from [0, nheads * ntiles) onto (head, level) whenever
+// nheads % 8 == 0.
+__device__ __forceinline__ void spread_tile(int b, int nheads, int ntiles, int cpx, int& head,
+                                            int& level) {
+  const int hx = nheads >> 3, n = hx * ntiles;
+  const int x = b & 7, j = b >> 3;
+  const int r = j / cpx, k = j % cpx;
+  // a last round that fills fewer than cpx CUs runs forward, so that i < n
+  const bool reverse = (r & 1) && (r + 1) * cpx <= n;
+  const int i = r * cpx + (reverse ? cpx - 1 - k : k);
+  head = x * hx + i % hx;
+  level = i / hx;
+}
+
 // IEEE maximum (NaN-propagating): v_maximum3_f32 on gfx950, no input
 // canonicalisation as fmaxf needs.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }

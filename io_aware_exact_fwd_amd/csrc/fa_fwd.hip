@@ -310,9 +310,17 @@ void fwd_kernel(FwdParams p) {
       for (int e = 0; e < nsub; ++e) tile(head, e == 0 ? p.nqt - 1 - u : u);
     }
   } else {
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int head = logical / p.nqt, qt = logical % p.nqt;
-    tile(head, CAUSAL ? p.nqt - 1 - qt : qt);  // causal: the longer rows first
+    // causal: the longer rows first (one call of the tile body, so that it is
+    // inlined once)
+    int head, qt;
+    if (CAUSAL && p.spread > 0) {
+      spread_tile(blockIdx.x, p.nheads, p.nqt, p.spread, head, qt);
+    } else {
+      const int logical = xcd_remap(blockIdx.x, gridDim.x);
+      head = logical / p.nqt;
+      qt = logical % p.nqt;
+    }
+    tile(head, CAUSAL ? p.nqt - 1 - qt : qt);
   }
 }
 
@@ -322,12 +330,19 @@ static hipError_t launch_fwd_t(FwdParams p, bool causal, hipStream_t s) {
   constexpr int WPE = D == 64 ? kFwdWpe64 : (DROP ? kFwdWpe128Drop : kFwdWpe128);
   constexpr int BR = kFwdWaves * 32;
   p.nqt = (p.N + BR - 1) / BR;
+  p.spread = 0;
   static_assert(kFwdWaves * 64 == kThreads, "one workgroup size for all launches");
-  // causal work without a window or block mask runs on a persistent grid
-  // over tile pairs; the rest one workgroup per tile
+  // causal work without a window or block mask: one workgroup per tile in the
+  // spread order when all tiles fit on the GPU at once, else a persistent
+  // grid over tile pairs; the rest one workgroup per tile
   if constexpr (!MASKED)
     if (causal && p.window == 0) {
-      launch_units<fwd_kernel<T, D, true, false, DROP, WPE, KT, true>>(p, p.nheads * ((p.nqt + 1) / 2), true, s);
+      constexpr auto kTile = fwd_kernel<T, D, true, false, DROP, WPE, KT, false>;
+      p.spread = spread_for<kTile>(p.nheads, p.nqt);
+      if (p.spread > 0)
+        launch_units<kTile>(p, p.nheads * p.nqt, false, s);
+      else
+        launch_units<fwd_kernel<T, D, true, false, DROP, WPE, KT, true>>(p, p.nheads * ((p.nqt + 1) / 2), true, s);
       return hipGetLastError();
     }
   if (causal)

@@ -49,6 +49,7 @@ struct FwdParams {
   MaskLists m;
   DropParams drop;
   int32_t* visits;  // debug build: tile-visit counters (see fa_debug_set_tile_visits), else null
+  int spread;       // set by the launcher: CUs per XCD for spread_tile, or 0
 };
 
 struct BwdParams {
@@ -73,6 +74,7 @@ struct BwdParams {
   MaskLists m;
   DropParams drop;
   int32_t* visits;  // debug build: tile-visit counters, else null
+  int spread;       // set by the launcher: CUs per XCD for spread_tile, or 0
 };
 
 // Decode-shaped forward (fa_decode.hip): n_q queries per head at positions
@@ -186,17 +188,33 @@ inline int cu_count() {
   if (dev >= 0 && dev < kDevices) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
-// Grid of a persistent launch: min(units, CUs x workgroups of Kernel per CU);
-// the occupancy is queried once per kernel.
+// Workgroups of Kernel resident on the GPU at once: CUs x workgroups per CU,
+// the occupancy queried once per kernel.
 template <auto Kernel>
-inline int persistent_grid(int units) {
+inline long long resident_workgroups() {
   static const int per_cu = [] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel, kThreads, 0) != hipSuccess || n < 1) n = 1;
     return n;
   }();
-  const long long g = (long long)cu_count() * per_cu;
+  return (long long)cu_count() * per_cu;
+}
+// Grid of a persistent launch: min(units, resident workgroups).
+template <auto Kernel>
+inline int persistent_grid(int units) {
+  const long long g = resident_workgroups<Kernel>();
   return (int)(units < g ? units : g);
+}
+// Causal tiles of nheads heads, ntiles each, launched one workgroup per tile
+// with Kernel: the CUs per XCD that spread_tile deals them over when they are
+// all resident at once and the heads split evenly over the 8 XCDs (measured
+// on GPT-2-small's forward: 32.4 -> 25.6 us against tile pairs, whose 384
+// units load half the CUs twice), else 0.
+template <auto Kernel>
+inline int spread_for(int nheads, int ntiles) {
+  const int cus = cu_count();
+  if (nheads % 8 != 0 || cus % 8 != 0) return 0;
+  return (long long)nheads * ntiles <= resident_workgroups<Kernel>() ? cus / 8 : 0;
 }
 // Launch Kernel over `units` work units: a persistent grid, or one workgroup
 // per unit.  The kernels take persistent grids for causal work without a
