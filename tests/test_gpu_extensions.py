@@ -148,15 +148,21 @@ def test_dropout_keep_mask_bit_exact(causal, p, d):
 
 
 # A window at least as wide as the sequence hides nothing.  Causal work with a
-# window runs one workgroup per tile; without one, the persistent grid over tile
-# pairs: the two schedules must give bitwise the same outputs (every tile is
-# computed the same way, only their assignment to workgroups differs).  The
-# dropout case has whole query tiles: in a ragged last tile the rows past N see a
-# band that does depend on the window, and as a wave moves the reference of all
-# its rows together, the rows before N can then differ in rounding (not beyond).
+# window runs one workgroup per tile in head order; without one, the persistent
+# grid over tile pairs or, when every tile fits on the GPU at once and the heads
+# split evenly over the 8 XCDs, one workgroup per tile in the spread order: the
+# schedules must give bitwise the same outputs (every tile is computed the same
+# way, only their assignment to workgroups differs).  B=8 H=32 takes the tile
+# pairs; the other shapes take the spread order wherever their heads split
+# evenly over the XCDs, the 8 x 65 tiles of N = 8300 in all three kernels, with
+# rounds in both directions and a partial last round.  The dropout case has
+# whole query tiles: in a ragged last tile the rows past N see a band that does
+# depend on the window, and as a wave moves the reference of all its rows
+# together, the rows before N can then differ in rounding (not beyond).
 @pytest.mark.parametrize("dtype,d,B,H,hkv,N,p", [("f16", 64, 8, 32, None, 1024, 0.0),
                                               ("bf16", 128, 1, 8, 2, 2000, 0.0),
-                                              ("f16", 64, 2, 4, None, 768, 0.1)])
+                                              ("f16", 64, 2, 4, None, 768, 0.1),
+                                              ("f16", 64, 1, 8, None, 8300, 0.0)])
 def test_persistent_grid_equals_one_workgroup_per_tile(dtype, d, B, H, hkv, N, p):
     say(f"[case] persistent vs per-tile grid: B={B} H={H} hkv={hkv} N={N} d={d} {dtype} p={p}")
     q, k, v, do = (t.to("cuda") for t in make_inputs(B, H, N, d, dtype, hkv=hkv))
