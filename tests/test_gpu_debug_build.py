@@ -42,6 +42,8 @@ def _holes(nb):
 CASES = [
     # name, B, H, hkv, N, d, dtype, causal, window, mask, dropout
     ("dense-f16-d64-ragged-causal", 2, 2, 2, 1000, 64, "f16", True, 0, None, 0.0),
+    # 8 heads, every tile resident: the three kernels in the spread order
+    ("spread-bf16-d64-causal", 2, 4, 4, 1500, 64, "bf16", True, 0, None, 0.0),
     ("dense-bf16-d128-ragged", 1, 3, 3, 777, 128, "bf16", False, 0, None, 0.0),
     ("window-f16-d64", 1, 2, 2, 1500, 64, "f16", True, 300, None, 0.0),
     ("window-bf16-d128-twosided", 1, 2, 2, 1300, 128, "bf16", False, 200, None, 0.0),
